@@ -1,0 +1,255 @@
+"""Plain CPU oracle for block-sparse causal prefill attention (fp64, NumPy).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The library never calls it, and it
+shares no code, table or helper with the HIP path.
+
+What it computes, step by step, in the order the pages give:
+
+1. Block approximation (FlashPrefill, gist.science technical summary,
+   section 2.A "Approximation par Blocs"): keys are replaced by their per-block
+   mean k_bar; queries are pooled the same way (q_bar), and V is pooled for
+   the correction term (step 5).
+2. Pooled block logits s[h, I, J] = sigma * q_bar[h, I] . k_bar[h // g, J] for
+   J <= I (causal blocks only).
+3. Block scores Score[h, I, J] = softmax over J <= I of s[h, I, :].
+4. Max-based dynamic threshold (same page, section 2.B, the threshold
+   equation): thresh_I = alpha * max_{J <= I} Score[I, J]; block J is kept iff
+   Score[I, J] >= thresh_I.  The result is one ascending list of kept KV
+   blocks per (query head, query block) (section 2.C, index-based skipping).
+5. Attention over the kept blocks with the mean-correction term
+   (FlashPrefill V2 abstract, which names the term but prints no formula):
+   row i of query block I attends to every token j <= i of the kept blocks,
+   and, when the correction is on, to one pooled entry per skipped block
+   J < I with logit sigma * q_i . k_bar_J + ln n_J and value v_bar_J (the
+   skipped block stands in as n_J copies of its mean key and mean value).
+   Output o_i = sum w v / sum w, lse_i = max z + ln sum exp(z - max z).
+
+Readings taken where the pages are silent (listed with reasons in the design
+notes): Score is softmax-normalised (3); sigma = 1/sqrt(d) (2); the compare
+is inclusive (4); selection is per query head with KV head h // g (2, 4);
+partial last blocks average their valid tokens; the correction form (5); a
+skipped diagonal block gets no correction entry (its mean mixes future
+tokens).  fp8 inputs are judged on their dequantized values.
+
+Pins (tests/test_oracle.py): alpha = 0 reduces to dense causal attention
+computed by an independent routine; masks equal brute-force per-block scoring
+on tiny inputs; every probability row sums to 1; the correction equals dense
+attention in closed form when K and V are constant within blocks; constant V
+gives constant output; the argmax block is always kept and masks nest in
+alpha; GQA equals MHA with repeated K/V; a varlen batch equals its requests.
+The correction's definition itself is a reading, not a formula from the pages;
+only its implementation under that reading is pinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BAND_REL = 1e-3   # blocks whose score lies within this relative distance of the threshold
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def num_blocks(seqlen: int, block: int) -> int:
+    return (seqlen + block - 1) // block
+
+
+def block_lengths(seqlen: int, block: int) -> np.ndarray:
+    """n_J: tokens in block J (block, except for a partial last block)."""
+    nB = num_blocks(seqlen, block)
+    return np.array([min(block, seqlen - J * block) for J in range(nB)], dtype=np.int64)
+
+
+def block_means(x, block: int) -> np.ndarray:
+    """Per-block mean over the valid tokens.  x [S, H, d] -> [H, nB, d] (fp64)."""
+    S, H, d = x.shape
+    nB = num_blocks(S, block)
+    out = np.empty((H, nB, d), dtype=np.float64)
+    for J in range(nB):
+        seg = _f64(x[J * block:min(S, (J + 1) * block)])      # [n_J, H, d]
+        out[:, J, :] = seg.mean(axis=0)
+    return out
+
+
+def block_logits(q_bar: np.ndarray, k_bar: np.ndarray, sigma: float) -> np.ndarray:
+    """s[h, I, J] = sigma * q_bar[h, I] . k_bar[h // g, J] for J <= I; -inf above."""
+    Hq, nB, _ = q_bar.shape
+    Hkv = k_bar.shape[0]
+    g = Hq // Hkv
+    causal = np.tril(np.ones((nB, nB), dtype=bool))
+    s = np.full((Hq, nB, nB), -np.inf)
+    for h in range(Hq):
+        full = sigma * (q_bar[h] @ k_bar[h // g].T)
+        s[h] = np.where(causal, full, -np.inf)
+    return s
+
+
+def block_scores(s: np.ndarray) -> np.ndarray:
+    """Score[h, I, J] = softmax over the causal blocks J <= I of s[h, I, :]."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)                      # exp(-inf) = 0 above the diagonal
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def threshold(score: np.ndarray, alpha: float) -> Tuple[np.ndarray, np.ndarray]:
+    """keep = Score >= alpha * max_{J<=I} Score over causal blocks.
+
+    Also returns the band flags: causal blocks whose score lies within
+    BAND_REL relative of the threshold (only meaningful for alpha > 0).
+    """
+    nB = score.shape[-1]
+    causal = np.tril(np.ones((nB, nB), dtype=bool))[None]
+    thresh = alpha * score.max(axis=-1, keepdims=True)
+    keep = causal & (score >= thresh)
+    if alpha > 0:
+        band = causal & (np.abs(score - thresh) <= BAND_REL * thresh)
+    else:
+        band = np.zeros_like(keep)
+    return keep, band
+
+
+class Selection:
+    """Everything the selection step produces for one sequence."""
+
+    def __init__(self, q_bar, k_bar, v_bar, s, score, keep, band, block):
+        self.q_bar, self.k_bar, self.v_bar = q_bar, k_bar, v_bar
+        self.s, self.score, self.keep, self.band = s, score, keep, band
+        self.block = block
+
+    def lists(self) -> List[List[np.ndarray]]:
+        """Kept KV blocks per (query head, query block), ascending."""
+        Hq, nB, _ = self.keep.shape
+        return [[np.flatnonzero(self.keep[h, I, :I + 1]) for I in range(nB)]
+                for h in range(Hq)]
+
+
+def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
+                  pool_v: bool = True) -> Selection:
+    """Pooling, block scores and thresholding for one sequence.
+
+    q [S, Hq, d], k and v [S, Hkv, d] (any float dtype; upcast to fp64).
+    """
+    d = q.shape[-1]
+    if sigma is None:
+        sigma = 1.0 / math.sqrt(d)
+    q_bar = block_means(q, block)
+    k_bar = block_means(k, block)
+    v_bar = block_means(v, block) if pool_v else None
+    s = block_logits(q_bar, k_bar, sigma)
+    score = block_scores(s)
+    keep, band = threshold(score, alpha)
+    return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block)
+
+
+def block_entries(q, k, v, keep_row: np.ndarray, h: int, I: int, block: int, sigma: float,
+                  g: int, correction: bool, k_bar=None, v_bar=None):
+    """Logits z [n_I, n_entries] and values [n_entries, d] for query block I of head h.
+
+    Entries: the tokens of every kept block J <= I (token j masked to -inf for
+    rows i < j), then, with the correction, one pooled entry per skipped J < I.
+    """
+    S = q.shape[0]
+    hk = h // g
+    r0, r1 = I * block, min(S, (I + 1) * block)
+    rows = np.arange(r0, r1)
+    q_i = _f64(q[r0:r1, h])                                    # [n_I, d]
+    kept = [J for J in range(I + 1) if keep_row[J]]
+    if kept:
+        tok = np.concatenate([np.arange(J * block, min(S, (J + 1) * block)) for J in kept])
+    else:
+        tok = np.zeros(0, dtype=np.int64)
+    z = sigma * (q_i @ _f64(k[tok, hk]).T)                      # [n_I, n_tok]
+    z[tok[None, :] > rows[:, None]] = -np.inf                  # causal inside block I
+    vals = _f64(v[tok, hk])
+    if correction:
+        skipped = [J for J in range(I) if not keep_row[J]]
+        if skipped:
+            n = block_lengths(S, block)[skipped].astype(np.float64)
+            zc = sigma * (q_i @ k_bar[hk, skipped].T) + np.log(n)[None, :]
+            z = np.concatenate([z, zc], axis=1)
+            vals = np.concatenate([vals, v_bar[hk, skipped]], axis=0)
+    return z, vals
+
+
+def softmax_rows(z: np.ndarray):
+    """Row softmax pieces: (max M, weights exp(z - M), row sums l)."""
+    M = z.max(axis=1, keepdims=True)
+    w = np.exp(z - M)
+    return M[:, 0], w, w.sum(axis=1)
+
+
+def sparse_attention(q, k, v, sel: Selection, correction: bool, sigma: Optional[float] = None,
+                     pairs: Optional[Iterable[Tuple[int, int]]] = None,
+                     keep: Optional[np.ndarray] = None):
+    """Attention over the kept blocks (plus the correction entries).
+
+    Returns o [S, Hq, d] and lse [Hq, S] (fp64); rows of (head, query block)
+    pairs not listed in ``pairs`` stay NaN.  ``keep`` overrides the selection's
+    mask (used to evaluate under a mask produced elsewhere).
+    """
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    block = sel.block
+    if sigma is None:
+        sigma = 1.0 / math.sqrt(d)
+    keep = sel.keep if keep is None else keep
+    nB = num_blocks(S, block)
+    if pairs is None:
+        pairs = [(h, I) for h in range(Hq) for I in range(nB)]
+    o = np.full((S, Hq, d), np.nan)
+    lse = np.full((Hq, S), np.nan)
+    for h, I in pairs:
+        z, vals = block_entries(q, k, v, keep[h, I], h, I, block, sigma, g, correction,
+                                sel.k_bar, sel.v_bar)
+        M, w, l = softmax_rows(z)
+        r0, r1 = I * block, min(S, (I + 1) * block)
+        o[r0:r1, h] = (w @ vals) / l[:, None]
+        lse[h, r0:r1] = M + np.log(l)
+    return o, lse
+
+
+def attention_probabilities(q, k, v, sel: Selection, correction: bool, h: int, I: int,
+                            sigma: Optional[float] = None) -> np.ndarray:
+    """Normalised weights of every entry for the rows of query block I of head h."""
+    d = q.shape[-1]
+    g = q.shape[1] // k.shape[1]
+    if sigma is None:
+        sigma = 1.0 / math.sqrt(d)
+    z, _ = block_entries(q, k, v, sel.keep[h, I], h, I, sel.block, sigma, g, correction,
+                         sel.k_bar, sel.v_bar)
+    _, w, l = softmax_rows(z)
+    return w / l[:, None]
+
+
+def dequantize_blockwise(codes_value, scales, block: int) -> np.ndarray:
+    """x = x8 * scale[h, t // block] for fp8 values decoded to float ([S, H, d])."""
+    x8 = _f64(codes_value)
+    S = x8.shape[0]
+    sc = _f64(scales)                                           # [H, nB]
+    idx = np.arange(S) // block
+    return x8 * sc[:, idx].T[:, :, None]
+
+
+def flops_executed(sel: Selection, seqlen: int, head_dim: int, correction: bool,
+                   keep: Optional[np.ndarray] = None) -> Tuple[float, float]:
+    """Algorithmic work: (F_kept, F_corr).
+
+    F_kept = 4 d sum over kept (h, I, J) of n_I n_J (diagonal tile counted in
+    full); F_corr = 4 d sum over (h, I) of n_I * |skipped J < I|.
+    """
+    keep = sel.keep if keep is None else keep
+    n = block_lengths(seqlen, sel.block).astype(np.float64)
+    f_kept = 4.0 * head_dim * float(np.einsum("hij,i,j->", keep.astype(np.float64), n, n))
+    f_corr = 0.0
+    if correction:
+        nB = len(n)
+        strict = np.tril(np.ones((nB, nB), dtype=bool), -1)[None]
+        skipped = (strict & ~keep).sum(axis=2).astype(np.float64)   # [Hq, nB]
+        f_corr = 4.0 * head_dim * float((skipped * n[None, :]).sum())
+    return f_kept, f_corr

@@ -1,0 +1,328 @@
+"""Pins for the CPU oracle: each check comes from something other than the
+oracle itself (a textbook routine, brute force, a closed form, an invariant
+the threshold equation implies), so that a dropped term, a wrong sign, index
+or operand fails at least one of them."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_long_pooling_amd import synth
+
+
+def _rand_qkv(S, Hq, Hkv, d, seed, scale=1.0):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((S, Hq, d)) * scale
+    k = r.standard_normal((S, Hkv, d)) * scale
+    v = r.standard_normal((S, Hkv, d))
+    return q, k, v
+
+
+def _dense_causal_torch(q, k, v):
+    """Full causal softmax attention by torch's own routine (fp64, CPU)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+    Q = torch.from_numpy(q).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+    V = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _dense_causal_matrix(q, k, v):
+    """Textbook dense causal attention with the full S x S matrix; also lse."""
+    S, Hq, d = q.shape
+    g = Hq // k.shape[1]
+    o = np.empty_like(q)
+    lse = np.empty((Hq, S))
+    mask = np.triu(np.ones((S, S), dtype=bool), 1)
+    for h in range(Hq):
+        a = q[:, h] @ k[:, h // g].T / math.sqrt(d)
+        a[mask] = -np.inf
+        m = a.max(axis=1, keepdims=True)
+        e = np.exp(a - m)
+        o[:, h] = (e @ v[:, h // g]) / e.sum(1, keepdims=True)
+        lse[h] = m[:, 0] + np.log(e.sum(1))
+    return o, lse
+
+
+# ---------------------------------------------------------------- alpha = 0
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,d", [(200, 64, 4, 2, 16), (128, 32, 2, 2, 8), (64, 64, 3, 1, 8),
+                                          (33, 16, 1, 1, 4)])
+@pytest.mark.parametrize("corr", [False, True])
+def test_alpha0_is_dense_causal(S, B, Hq, Hkv, d, corr):
+    q, k, v = _rand_qkv(S, Hq, Hkv, d, seed=S + d)
+    sel = O.select_blocks(q, k, v, B, alpha=0.0)
+    assert sel.keep.sum() == Hq * O.num_blocks(S, B) * (O.num_blocks(S, B) + 1) // 2
+    o, lse = O.sparse_attention(q, k, v, sel, correction=corr)
+    o_t = _dense_causal_torch(q, k, v)
+    o_m, lse_m = _dense_causal_matrix(q, k, v)
+    np.testing.assert_allclose(o, o_t, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(o, o_m, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_m, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------- brute-force mask
+
+def _brute_force_keep(q, k, B, alpha):
+    """Per-block scoring written with Python loops and math.fsum."""
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    nB = (S + B - 1) // B
+    sig = 1.0 / math.sqrt(d)
+
+    def mean(x, J, h):
+        toks = range(J * B, min(S, (J + 1) * B))
+        return [math.fsum(float(x[t, h, c]) for t in toks) / len(toks) for c in range(d)]
+
+    keep = np.zeros((Hq, nB, nB), dtype=bool)
+    band = np.zeros((Hq, nB, nB), dtype=bool)
+    for h in range(Hq):
+        kb = [mean(k, J, h // g) for J in range(nB)]
+        for I in range(nB):
+            qb = mean(q, I, h)
+            s = [sig * math.fsum(a * b for a, b in zip(qb, kb[J])) for J in range(I + 1)]
+            m = max(s)
+            den = math.fsum(math.exp(x - m) for x in s)
+            score = [math.exp(x - m) / den for x in s]
+            thr = alpha * max(score)
+            for J in range(I + 1):
+                keep[h, I, J] = score[J] >= thr
+                band[h, I, J] = alpha > 0 and abs(score[J] - thr) <= 1e-3 * thr
+    return keep, band
+
+
+@pytest.mark.parametrize("alpha", [0.05, 0.1, 0.3, 0.5, 0.9, 1.0])
+def test_mask_matches_brute_force(alpha):
+    q, k, v = synth.make_sequence(320, 4, 2, 16, seed=7, verticals=False)
+    q, k = q.float().numpy(), k.float().numpy()
+    sel = O.select_blocks(q, k, None, 32, alpha, pool_v=False)
+    keep_bf, band_bf = _brute_force_keep(q, k, 32, alpha)
+    outside = ~(sel.band | band_bf)
+    assert np.array_equal(sel.keep[outside], keep_bf[outside])
+    # A non-trivial mask: something is skipped for alpha >= 0.3 on this input.
+    if alpha >= 0.3:
+        causal = np.tril(np.ones(sel.keep.shape[1:], bool))
+        assert sel.keep.sum() < sel.keep.shape[0] * causal.sum()
+
+
+def test_mask_brute_force_partial_block_and_gqa():
+    q, k, _ = _rand_qkv(77, 6, 2, 8, seed=3, scale=2.0)
+    for alpha in (0.2, 0.6):
+        sel = O.select_blocks(q, k, None, 16, alpha, pool_v=False)
+        keep_bf, band_bf = _brute_force_keep(q, k, 16, alpha)
+        outside = ~(sel.band | band_bf)
+        assert np.array_equal(sel.keep[outside], keep_bf[outside])
+
+
+def test_block_means_brute_force():
+    x = np.random.default_rng(1).standard_normal((45, 3, 5))
+    m = O.block_means(x, 16)
+    for h in range(3):
+        for J in range(3):
+            toks = range(16 * J, min(45, 16 * J + 16))
+            for c in range(5):
+                ref = math.fsum(x[t, h, c] for t in toks) / len(toks)
+                assert abs(m[h, J, c] - ref) < 1e-15
+    assert list(O.block_lengths(45, 16)) == [16, 16, 13]
+
+
+# ----------------------------------------------------------- normalisation
+
+@pytest.mark.parametrize("corr", [False, True])
+def test_probability_rows_sum_to_one(corr):
+    q, k, v = synth.make_sequence(256, 2, 1, 16, seed=5, verticals=False)
+    q, k, v = (t.float().numpy() for t in (q, k, v))
+    sel = O.select_blocks(q, k, v, 32, alpha=0.5)
+    for h in range(2):
+        for I in range(8):
+            p = O.attention_probabilities(q, k, v, sel, corr, h, I)
+            np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12, rtol=0)
+            assert (p >= 0).all()
+
+
+# ----------------------------------------------------- correction (closed form)
+
+def _block_constant_inputs(S, B, Hq, Hkv, d, seed):
+    """K and V constant inside every block; queries near their block's key
+    direction, so the diagonal block is the strict argmax of every row."""
+    r = np.random.default_rng(seed)
+    nB = (S + B - 1) // B
+    g = Hq // Hkv
+    c = r.standard_normal((Hkv, nB, d))
+    c *= (2.5 + r.random((Hkv, nB, 1))) / np.linalg.norm(c, axis=-1, keepdims=True) * math.sqrt(math.sqrt(d))
+    vb = r.standard_normal((Hkv, nB, d))
+    blk = np.arange(S) // B
+    k = c[:, blk].transpose(1, 0, 2).copy()
+    v = vb[:, blk].transpose(1, 0, 2).copy()
+    q = np.repeat(c, g, axis=0)[:, blk].transpose(1, 0, 2) + 0.3 * r.standard_normal((S, Hq, d))
+    return q, k, v
+
+
+@pytest.mark.parametrize("alpha", [0.01, 0.1, 0.3, 0.7, 1.0])
+def test_correction_closed_form_equals_dense(alpha):
+    S, B = 256, 16
+    q, k, v = _block_constant_inputs(S, B, 4, 2, 16, seed=11)
+    sel = O.select_blocks(q, k, v, B, alpha)
+    nB = S // B
+    # precondition of the closed form: the diagonal is always kept
+    assert all(sel.keep[h, I, I] for h in range(4) for I in range(nB))
+    o, lse = O.sparse_attention(q, k, v, sel, correction=True)
+    o_d, lse_d = _dense_causal_matrix(q, k, v)
+    np.testing.assert_allclose(o, o_d, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_d, atol=1e-12, rtol=0)
+    if alpha >= 0.3:
+        # something really was skipped, and without the correction the result differs
+        assert (~sel.keep & np.tril(np.ones((nB, nB), bool), -1)[None]).any()
+        o_nc, _ = O.sparse_attention(q, k, v, sel, correction=False)
+        assert np.abs(o_nc - o_d).max() > 1e-3
+
+
+def test_hand_worked_example():
+    """S=4, B=2, d=4 (sigma = 1/2), one head, worked by hand.
+
+    Keys: k0 = k1 = 0, k2 = k3 = (2,0,0,0).  Queries q2 = q3 = (3,0,0,0).
+    Pooled logits of query block 1: s10 = 0, s11 = 3, so block 0 scores
+    e^-3 = 0.0498 of the row max: skipped at alpha = 0.1, kept at 0.04.
+    Values v0..v3 = unit vectors e0..e3, so v_bar0 = (1/2, 1/2, 0, 0).
+    Row 2: token 2 with logit 3, correction entry ln 2 + 0 with value v_bar0:
+      o2 = (1, 1, e^3, 0) / (e^3 + 2),  lse2 = ln(e^3 + 2).
+    Row 3: tokens 2, 3 (logit 3 each) and the same correction entry:
+      o3 = (1, 1, e^3, e^3) / (2 e^3 + 2),  lse3 = ln(2 e^3 + 2).
+    Rows 0, 1 see only block 0 with zero keys: o0 = e0, o1 = (e0 + e1) / 2.
+    Without the correction rows 2, 3 see block 1 only: o2 = e2, o3 = (e2+e3)/2.
+    """
+    q = np.zeros((4, 1, 4)); k = np.zeros((4, 1, 4)); v = np.zeros((4, 1, 4))
+    q[0, 0] = [1, 2, 3, 4]
+    q[2, 0, 0] = q[3, 0, 0] = 3.0
+    k[2, 0, 0] = k[3, 0, 0] = 2.0
+    for t in range(4):
+        v[t, 0, t] = 1.0
+    e3 = math.exp(3.0)
+    sel = O.select_blocks(q, k, v, 2, alpha=0.1)
+    assert sel.keep[0].tolist() == [[True, False], [False, True]]
+    o, lse = O.sparse_attention(q, k, v, sel, correction=True)
+    np.testing.assert_allclose(o[0, 0], [1, 0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(o[1, 0], [0.5, 0.5, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(o[2, 0], np.array([1, 1, e3, 0]) / (e3 + 2), atol=1e-15)
+    np.testing.assert_allclose(o[3, 0], np.array([1, 1, e3, e3]) / (2 * e3 + 2), atol=1e-15)
+    np.testing.assert_allclose(lse[0], [0, math.log(2), math.log(e3 + 2), math.log(2 * e3 + 2)],
+                               atol=1e-14)
+    o_nc, _ = O.sparse_attention(q, k, v, sel, correction=False)
+    np.testing.assert_allclose(o_nc[2, 0], [0, 0, 1, 0], atol=1e-15)
+    np.testing.assert_allclose(o_nc[3, 0], [0, 0, 0.5, 0.5], atol=1e-15)
+    sel2 = O.select_blocks(q, k, v, 2, alpha=0.04)
+    assert sel2.keep[0].tolist() == [[True, False], [True, True]]
+
+
+def test_skipped_diagonal_gets_no_correction():
+    """A strong sink in block 0 makes the diagonal of later rows fall below
+    the threshold; the rows then see the kept past blocks and the correction
+    entries of skipped strictly-past blocks only."""
+    S, B, d = 96, 16, 8
+    r = np.random.default_rng(4)
+    q = 0.1 * r.standard_normal((S, 1, d))
+    k = 0.1 * r.standard_normal((S, 1, d))
+    v = r.standard_normal((S, 1, d))
+    q[:, 0, 0] += 3.0
+    k[:16, 0, 0] += 6.0
+    sel = O.select_blocks(q, k, v, B, alpha=0.5)
+    assert not sel.keep[0, 5, 5] and sel.keep[0, 5, 0]
+    p = O.attention_probabilities(q, k, v, sel, True, 0, 5)
+    kept = int(sel.keep[0, 5, :6].sum())
+    skipped_past = 5 - int(sel.keep[0, 5, :5].sum())
+    assert p.shape[1] == kept * B + skipped_past
+
+
+# --------------------------------------------------------------- invariants
+
+def test_constant_v_gives_constant_output():
+    q, k, _ = _rand_qkv(150, 4, 2, 8, seed=9, scale=1.5)
+    v = np.broadcast_to(np.array([0.25, -1, 2, 0, 3, 1, -2, 0.5]), (150, 2, 8)).copy()
+    for alpha in (0.0, 0.2, 0.9):
+        for corr in (False, True):
+            sel = O.select_blocks(q, k, v, 32, alpha)
+            o, _ = O.sparse_attention(q, k, v, sel, corr)
+            np.testing.assert_allclose(o, np.broadcast_to(v[0, 0], o.shape), atol=1e-13)
+
+
+def test_threshold_invariants():
+    q, k, _ = synth.make_sequence(1024, 4, 1, 64, seed=1, verticals=False)
+    q, k = q.float().numpy(), k.float().numpy()
+    nB = 16
+    causal = np.tril(np.ones((nB, nB), bool))
+    prev = None
+    for alpha in (0.0, 0.05, 0.1, 0.3, 0.5, 0.9, 1.0):
+        sel = O.select_blocks(q, k, None, 64, alpha, pool_v=False)
+        am = sel.s.argmax(axis=2)
+        for h in range(4):
+            for I in range(nB):
+                assert sel.keep[h, I, am[h, I]]                 # argmax always kept
+        assert not (sel.keep & ~causal).any()                   # never a future block
+        if prev is not None:
+            assert not (sel.keep & ~prev).any()                 # masks nest as alpha grows
+        prev = sel.keep
+    # alpha = 1: only blocks tied with the max survive
+    sel = O.select_blocks(q, k, None, 64, 1.0, pool_v=False)
+    assert np.array_equal(sel.keep.sum(axis=2), np.ones((4, nB), int))
+
+
+def test_single_block_is_dense_for_every_alpha():
+    q, k, v = _rand_qkv(40, 2, 1, 8, seed=2)
+    o_d, _ = _dense_causal_matrix(q, k, v)
+    for alpha in (0.0, 0.5, 1.0):
+        sel = O.select_blocks(q, k, v, 64, alpha)
+        o, _ = O.sparse_attention(q, k, v, sel, True)
+        np.testing.assert_allclose(o, o_d, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    q, k, v = _rand_qkv(128, 8, 2, 16, seed=21, scale=1.3)
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    for alpha in (0.2, 0.7):
+        a = O.select_blocks(q, k, v, 16, alpha)
+        b = O.select_blocks(q, kr, vr, 16, alpha)
+        assert np.array_equal(a.keep, b.keep)
+        oa, la = O.sparse_attention(q, k, v, a, True)
+        ob, lb = O.sparse_attention(q, kr, vr, b, True)
+        np.testing.assert_allclose(oa, ob, atol=1e-13)
+        np.testing.assert_allclose(la, lb, atol=1e-13)
+
+
+def test_pairs_subset_matches_full():
+    q, k, v = _rand_qkv(100, 4, 2, 8, seed=8)
+    sel = O.select_blocks(q, k, v, 16, 0.4)
+    o, lse = O.sparse_attention(q, k, v, sel, True)
+    pairs = [(0, 0), (3, 6), (1, 4)]
+    o2, lse2 = O.sparse_attention(q, k, v, sel, True, pairs=pairs)
+    for h, I in pairs:
+        r0, r1 = 16 * I, min(100, 16 * I + 16)
+        np.testing.assert_array_equal(o2[r0:r1, h], o[r0:r1, h])
+        np.testing.assert_array_equal(lse2[h, r0:r1], lse[h, r0:r1])
+    assert np.isnan(o2[16:32, 0]).all()
+
+
+def test_flop_count_dense_closed_form():
+    S, B, d, Hq = 256, 64, 16, 2
+    q, k, v = _rand_qkv(S, Hq, 1, d, seed=1)
+    sel = O.select_blocks(q, k, v, B, 0.0)
+    fk, fc = O.flops_executed(sel, S, d, True)
+    nB = S // B
+    assert fk == 4 * d * Hq * B * B * nB * (nB + 1) // 2
+    assert fc == 0.0
+
+
+# ------------------------------------------------------------------- fp8
+
+def test_dequantize_blockwise_elementwise():
+    r = np.random.default_rng(0)
+    x8 = r.standard_normal((70, 3, 4))
+    sc = r.random((3, 3)) + 0.5
+    x = O.dequantize_blockwise(x8, sc, 32)
+    for t in range(70):
+        for h in range(3):
+            assert np.allclose(x[t, h], x8[t, h] * sc[h, t // 32], rtol=0, atol=0)
