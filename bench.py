@@ -1,0 +1,271 @@
+"""Benchmark of the block-sparse prefill hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input: block-mean
+pooling + block scores + threshold + lists (fp_select_blocks), then attention
+over the kept blocks with the mean correction (fp_sparse_prefill_fwd).  The
+default workload is one Llama-3-8B-shaped layer at 131072 tokens (32 query
+heads, 8 KV heads, d 128, block 128), threshold ratio 0.1; the ratios 0.05 and
+0.2 are timed beside it.
+
+Prints one JSON line.  value = effective TFLOP/s of the whole step, counting
+only the algorithmic work of the executed blocks: F_kept = 4 d sum over kept
+(h, I, J) of n_I n_J and F_corr = 4 d sum over (h, I) of n_I * |skipped J < I|.
+The roofline entry is for the attention kernel (MFMA-bound), timed with HIP
+events on the launch stream.  The CPU baseline is the fp64 oracle on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill attn latency + effective TFLOP/s (% MFMA peak) at 128K, GQA 32/8 d128"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBPS = 8000.0
+# Averages of the attention kernel's rocprofv3 counters on this workload
+# (KiB per dispatch); None until measured on the current kernel.
+TRAFFIC_KIB = None
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_s128k")
+    ap.add_argument("--alpha", type=float, default=0.1)
+    ap.add_argument("--no-correction", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline alpha only: no sweep, no dense references, no CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def work_counts(fp, sel, S, Hq, d, B, correction):
+    """F_kept, F_corr and kept-block count from the device lists."""
+    import torch
+    nB = (S + B - 1) // B
+    cnt = sel.kv_cnt.to(torch.int64)                                    # [Hq, nB]
+    I = torch.arange(nB, device=cnt.device)
+    base = (torch.arange(Hq, device=cnt.device)[:, None] * (nB * (nB + 1) // 2)
+            + (I * (I + 1) // 2)[None, :])
+    last = sel.kv_idx.to(torch.int64)[base + cnt - 1]                  # largest kept J per row
+    diag_kept = (last == I[None, :]).to(torch.int64)
+    n = torch.full((nB,), B, dtype=torch.int64, device=cnt.device)
+    n[-1] = S - (nB - 1) * B
+    # only row nB-1 can hold the partial block, and only as its diagonal
+    n_j_sum = cnt * B
+    n_j_sum[:, -1] -= diag_kept[:, -1] * (B - int(n[-1]))
+    f_kept = 4.0 * d * float((n[None, :] * n_j_sum).sum())
+    f_corr = 0.0
+    if correction:
+        skipped = I[None, :] - (cnt - diag_kept)
+        f_corr = 4.0 * d * float((n[None, :] * skipped).sum())
+    return f_kept, f_corr, int(cnt.sum())
+
+
+def selection_bytes(S, Hq, Hkv, d, B, kept, correction):
+    nB = (S + B - 1) // B
+    nv = 1 if correction else 0
+    read = S * (Hq + Hkv * (1 + nv)) * d * 2
+    write = (Hq + Hkv * (1 + nv)) * nB * d * 4 + 4 * kept + 4 * Hq * nB
+    return read + write
+
+
+def time_steps(fn_sel, fn_attn, steps, stream):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        fn_sel()
+        e1.record(stream)
+        fn_attn()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
+    attn_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+    return wall * 1e3 / steps, sel_ms, attn_ms
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the path is built and "
+              "timed on a single MI355X; see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_long_pooling_amd as fp
+    from block_sparse_long_pooling_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.paged or w.dtype != "bf16":
+        raise SystemExit("bench.py times the single-sequence bf16 workloads")
+    S, Hq, Hkv, d, B = w.seqlens[0], w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    corr = not args.no_correction
+    log(f"bench: workload {w.name} S={S} Hq={Hq} Hkv={Hkv} d={d} B={B} alpha={args.alpha} corr={corr}")
+    t = time.perf_counter()
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, w.seed, w.verticals)
+    log(f"bench: inputs generated in {time.perf_counter() - t:.1f}s")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+
+    def measure(alpha, steps, warmup):
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr)
+        sel = fp.alloc_selection(p, S, dev)
+        fs = lambda: fp.fp_select_blocks(p, qd, kd, vd, sel=sel)
+        fa = lambda: fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, out=out)
+        for _ in range(warmup):
+            fs(); fa()
+        step_ms, sel_ms, attn_ms = time_steps(fs, fa, steps, stream)
+        f_kept, f_corr, kept = work_counts(fp, sel, S, Hq, d, B, corr)
+        causal = Hq * ((S + B - 1) // B) * ((S + B - 1) // B + 1) // 2
+        return dict(alpha=alpha, ms_per_step=step_ms, select_ms=sel_ms, attn_ms=attn_ms,
+                    f_kept=f_kept, f_corr=f_corr, kept_blocks=kept, density=kept / causal,
+                    sel=sel, p=p)
+
+    head = measure(args.alpha, args.steps, args.warmup)
+    f_alg = head["f_kept"] + head["f_corr"]
+    attn_tflops = f_alg / (head["attn_ms"] * 1e-3) / 1e12
+    step_tflops = f_alg / (head["ms_per_step"] * 1e-3) / 1e12
+    sel_bytes = selection_bytes(S, Hq, Hkv, d, B, head["kept_blocks"], corr)
+    sel_gbps = sel_bytes / (head["select_ms"] * 1e-3) / 1e9
+    log(f"bench: alpha={args.alpha} step {head['ms_per_step']:.3f} ms (select {head['select_ms']:.3f}, "
+        f"attn {head['attn_ms']:.3f}); density {head['density']:.4f}; attn {attn_tflops:.1f} TFLOP/s; "
+        f"select {sel_gbps:.0f} GB/s")
+
+    extra = {}
+    if not args.quick:
+        sweep = []
+        for a in w.alphas:
+            if a == args.alpha:
+                continue
+            r = measure(a, max(3, args.steps // 2), 1)
+            fa_ = r["f_kept"] + r["f_corr"]
+            sweep.append(dict(alpha=a, ms_per_step=round(r["ms_per_step"], 4),
+                              select_ms=round(r["select_ms"], 4), attn_ms=round(r["attn_ms"], 4),
+                              density=round(r["density"], 5),
+                              attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2)))
+            log(f"bench: sweep {sweep[-1]}")
+            del r
+        extra["alpha_sweep"] = sweep
+        # dense references on the same GPU
+        dense = measure(0.0, 2, 1)
+        f_dense = 4.0 * d * Hq * (S * (S + 1) / 2)
+        extra["dense_ref"] = {
+            "ours_alpha0_attn_ms": round(dense["attn_ms"], 3),
+            "ours_alpha0_tflops": round(f_dense / (dense["attn_ms"] * 1e-3) / 1e12, 1),
+        }
+        del dense
+        torch.cuda.empty_cache()
+        try:
+            Qt = qd.permute(1, 0, 2)[None]
+            Kt = kd.permute(1, 0, 2)[None]
+            Vt = vd.permute(1, 0, 2)[None]
+            f = lambda: torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, is_causal=True,
+                                                                         enable_gqa=True)
+            f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(2):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sdpa_ms = e0.elapsed_time(e1) / 2
+            extra["dense_ref"]["torch_sdpa_ms"] = round(sdpa_ms, 3)
+            extra["dense_ref"]["torch_sdpa_tflops"] = round(f_dense / (sdpa_ms * 1e-3) / 1e12, 1)
+            extra["dense_ref"]["speedup_vs_torch_sdpa"] = round(sdpa_ms / head["ms_per_step"], 2)
+        except Exception as ex:          # black-box reference; report, do not fail the bench
+            extra["dense_ref"]["torch_sdpa_error"] = str(ex)[:200]
+        log(f"bench: dense {extra['dense_ref']}")
+
+    cpu = None
+    if not args.quick:
+        cpu = cpu_baseline(q, k, v, B, args.alpha, corr, head, args.cpu_seconds)
+        log(f"bench: cpu {cpu}")
+
+    roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "kernel": "k_attn_bf16<128,128>", "traffic": TRAFFIC_KIB}
+    rec = {
+        "metric": METRIC, "value": round(step_tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "block": B, "alpha": args.alpha, "mean_correction": corr},
+        "select_ms": round(head["select_ms"], 4), "attn_ms": round(head["attn_ms"], 4),
+        "density": round(head["density"], 5), "attn_tflops": round(attn_tflops, 2),
+        "select_gbps": round(sel_gbps, 1), "select_hbm_frac": round(sel_gbps / PEAK_HBM_GBPS, 4),
+        "flops": {"kept": head["f_kept"], "corr": head["f_corr"]},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(q, k, v, B, alpha, corr, head, seconds):
+    """The fp64 oracle on the host: full selection, then attention for a
+    sample of (head, query block) pairs under the GPU's mask until about
+    `seconds` have passed; the rate is scaled to the whole workload."""
+    import numpy as np
+    import oracle as O
+    import block_sparse_long_pooling_amd as fp
+    S, Hq, d = q.shape
+    nB = (S + B - 1) // B
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    t0 = time.perf_counter()
+    sel = O.select_blocks(qn, kn, vn, B, alpha)
+    t_sel = time.perf_counter() - t0
+    mask = fp.lists_to_mask(head["sel"].kv_idx, head["sel"].kv_cnt, Hq, nB)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(Hq * nB)
+    t1 = time.perf_counter()
+    f_s = 0.0
+    done = 0
+    n_full = np.full(nB, B)
+    n_full[-1] = S - (nB - 1) * B
+    for idx in order:
+        h, I = divmod(int(idx), nB)
+        O.sparse_attention(qn, kn, vn, sel, corr, pairs=[(h, I)], keep=mask)
+        kept = mask[h, I, :I + 1]
+        f_s += 4.0 * d * n_full[I] * float(n_full[:I + 1][kept].sum())
+        if corr:
+            f_s += 4.0 * d * n_full[I] * float((~kept[:I]).sum())
+        done += 1
+        if time.perf_counter() - t1 > seconds:
+            break
+    t_att = time.perf_counter() - t1
+    f_total = head["f_kept"] + head["f_corr"]
+    est_total_s = t_sel + t_att * f_total / max(f_s, 1.0)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": round(f_total / est_total_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"full fp64 selection ({t_sel:.1f}s) + attention for {done} of {Hq * nB} random "
+                      f"(head, query block) pairs ({t_att:.1f}s), scaled by FLOP to the whole workload",
+            "est_seconds_full": round(est_total_s, 1)}
+
+
+if __name__ == "__main__":
+    main()

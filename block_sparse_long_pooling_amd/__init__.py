@@ -1,0 +1,232 @@
+"""Block-sparse causal prefill attention for MI355X (gfx950).
+
+Thin ctypes binding over libflashprefill.so: argument marshalling only.
+Every step of the method (pooling, scoring, thresholding, attention, mean
+correction) runs in the library's HIP kernels; torch provides device memory
+and the current stream.  Function names follow the C entry points
+(include/flashprefill.h).  If the library is missing the functions raise;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashprefill.so")
+
+FP_OK, FP_INVALID_ARGUMENT, FP_UNSUPPORTED, FP_WORKSPACE_TOO_SMALL, FP_DEVICE_ERROR = range(5)
+FP_DTYPE_BF16, FP_DTYPE_FP8_E4M3FN = 0, 1
+FP_MAX_BATCH = 128
+
+
+class fp_params(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("mean_correction", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class FlashPrefillError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"flashprefill status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+EXPORTS = {
+    "fp_select_blocks": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, ctypes.c_int32,
+                                        _P, _P, _P, _P, _P, _P]),
+    "fp_sparse_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
+    "fp_sparse_prefill_varlen_paged": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
+                                                      ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                      _I32P, ctypes.c_int32, _P, _P, _P,
+                                                      ctypes.c_size_t, _P, _P, _P]),
+    "fp_index_capacity": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
+    "fp_count_entries": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
+    "fp_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
+    "fp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflashprefill.so (built by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int):
+    if status != FP_OK:
+        raise FlashPrefillError(status, lib().fp_last_error().decode())
+
+
+def make_params(num_q_heads, num_kv_heads, head_dim, block_size, alpha, mean_correction=True,
+                softmax_scale=0.0, dtype=FP_DTYPE_BF16) -> fp_params:
+    return fp_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+                     float(alpha), float(softmax_scale), int(bool(mean_correction)), int(dtype))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _cu_host(cu_seqlens) -> ctypes.Array:
+    vals = [int(x) for x in (cu_seqlens.tolist() if torch.is_tensor(cu_seqlens) else cu_seqlens)]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def fp_index_capacity(params: fp_params, cu_seqlens: Sequence[int]) -> int:
+    cu = _cu_host(cu_seqlens)
+    return int(lib().fp_index_capacity(ctypes.byref(params), cu, len(cu) - 1))
+
+
+def fp_count_entries(params: fp_params, cu_seqlens: Sequence[int]) -> int:
+    cu = _cu_host(cu_seqlens)
+    return int(lib().fp_count_entries(ctypes.byref(params), cu, len(cu) - 1))
+
+
+def fp_varlen_workspace_bytes(params: fp_params, cu_seqlens: Sequence[int]) -> int:
+    cu = _cu_host(cu_seqlens)
+    return int(lib().fp_varlen_workspace_bytes(ctypes.byref(params), cu, len(cu) - 1))
+
+
+@dataclass
+class Selection:
+    """Outputs of fp_select_blocks (device tensors)."""
+    pooled_q: torch.Tensor      # fp32 [Hq, nB, d]
+    pooled_k: torch.Tensor      # fp32 [Hkv, nB, d]
+    pooled_v: Optional[torch.Tensor]
+    kv_idx: torch.Tensor        # int32, triangular-packed lists
+    kv_cnt: torch.Tensor        # int32 [Hq, nB]
+    block_size: int
+
+
+def alloc_selection(params: fp_params, seqlen: int, device, pool_v: Optional[bool] = None) -> Selection:
+    """Output buffers for fp_select_blocks on one sequence."""
+    B, d, Hq = params.block_size, params.head_dim, params.num_q_heads
+    nB = (seqlen + B - 1) // B
+    if pool_v is None:
+        pool_v = bool(params.mean_correction)
+    pq = torch.empty((Hq, nB, d), dtype=torch.float32, device=device)
+    pk = torch.empty((params.num_kv_heads, nB, d), dtype=torch.float32, device=device)
+    pv = torch.empty_like(pk) if pool_v else None
+    cap = fp_index_capacity(params, [0, seqlen])
+    kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    kv_cnt = torch.empty((Hq, nB), dtype=torch.int32, device=device)
+    return Selection(pq, pk, pv, kv_idx, kv_cnt, B)
+
+
+def fp_select_blocks(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
+                     pool_v: Optional[bool] = None, sel: Optional[Selection] = None) -> Selection:
+    """Pooling + block scores + threshold + lists for one sequence (bf16 q/k/v).
+
+    ``sel`` supplies preallocated output buffers (see alloc_selection)."""
+    S = q.shape[0]
+    dev = q.device
+    if sel is None:
+        sel = alloc_selection(params, S, dev, pool_v)
+    pool_v = sel.pooled_v is not None
+    pq, pk, pv, kv_idx, kv_cnt = sel.pooled_q, sel.pooled_k, sel.pooled_v, sel.kv_idx, sel.kv_cnt
+    _check(lib().fp_select_blocks(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v) if pool_v else None,
+                                  S, _ptr(pq), _ptr(pk), _ptr(pv), _ptr(kv_idx), _ptr(kv_cnt),
+                                  _stream(dev)))
+    return sel
+
+
+def fp_sparse_prefill_fwd(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          sel: Selection, q_scale=None, k_scale=None, v_scale=None,
+                          out: Optional[torch.Tensor] = None, return_lse: bool = False,
+                          lse: Optional[torch.Tensor] = None):
+    """Attention over the kept blocks (+ mean correction) for one sequence.
+
+    q/k/v are bf16, or uint8 e4m3fn codes with fp32 scales [H, nB] when
+    params.dtype is FP_DTYPE_FP8_E4M3FN.  Returns out (bf16 [S, Hq, d]) and,
+    with return_lse, lse (fp32 [Hq, S]).
+    """
+    S, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
+    _check(lib().fp_sparse_prefill_fwd(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), S,
+                                       _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _ptr(sel.pooled_k),
+                                       _ptr(sel.pooled_v), _ptr(out), _ptr(lse), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+@dataclass
+class VarlenResult:
+    out: torch.Tensor
+    lse: Optional[torch.Tensor]
+    kv_idx: torch.Tensor
+    kv_cnt: torch.Tensor
+    workspace: torch.Tensor
+
+
+def fp_sparse_prefill_varlen_paged(params: fp_params, q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_table: torch.Tensor, cu_seqlens,
+                                   return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None) -> VarlenResult:
+    """Continuous batch over a paged KV cache (bf16): selection + attention."""
+    T, Hq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    dev = q.device
+    cu = _cu_host(cu_seqlens)
+    batch = len(cu) - 1
+    cap = fp_index_capacity(params, list(cu))
+    ncnt = fp_count_entries(params, list(cu))
+    wsb = fp_varlen_workspace_bytes(params, list(cu))
+    kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty(max(ncnt, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().fp_sparse_prefill_varlen_paged(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
+        _ptr(block_table), block_table.shape[1], cu, batch, _ptr(kv_idx), _ptr(kv_cnt),
+        _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
+
+
+def lists_to_mask(kv_idx: torch.Tensor, kv_cnt: torch.Tensor, num_heads: int, nB: int,
+                  offset: int = 0, cnt_offset: int = 0) -> "numpy.ndarray":
+    """Host helper: triangular-packed lists -> boolean mask [Hq, nB, nB] (numpy)."""
+    import numpy as np
+    idx = kv_idx.cpu().numpy()
+    cnt = kv_cnt.reshape(-1).cpu().numpy()
+    mask = np.zeros((num_heads, nB, nB), dtype=bool)
+    tri = nB * (nB + 1) // 2
+    for h in range(num_heads):
+        for I in range(nB):
+            c = int(cnt[cnt_offset + h * nB + I])
+            base = offset + h * tri + I * (I + 1) // 2
+            mask[h, I, idx[base:base + c]] = True
+    return mask

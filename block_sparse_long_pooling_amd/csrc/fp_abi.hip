@@ -1,0 +1,349 @@
+// C-ABI entry points of libflashprefill: host-side validation, size queries,
+// request tables and kernel launches.  Nothing here allocates, frees or
+// synchronises; every call enqueues on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "flashprefill.h"
+#include "fp_launch.h"
+
+#define FP_EXPORT extern "C" __attribute__((visibility("default")))
+
+static_assert(FP_MAX_BATCH <= FP_TABLE_MAX, "request table too small");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return FP_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t tri(int64_t n) { return n * (n + 1) / 2; }
+
+int check_params(const fp_params* p) {
+    if (!p) return fail(FP_INVALID_ARGUMENT, "params is NULL");
+    if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+        return fail(FP_INVALID_ARGUMENT, "num_q_heads (%d) and num_kv_heads (%d) must be >= 1", p->num_q_heads,
+                    p->num_kv_heads);
+    if (p->num_q_heads % p->num_kv_heads != 0)
+        return fail(FP_INVALID_ARGUMENT, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                    p->num_q_heads, p->num_kv_heads);
+    if (p->num_q_heads / p->num_kv_heads > 32)
+        return fail(FP_UNSUPPORTED, "more than 32 query heads per KV head (%d)", p->num_q_heads / p->num_kv_heads);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(FP_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->head_dim);
+    if (p->block_size != 64 && p->block_size != 128)
+        return fail(FP_UNSUPPORTED, "block_size %d (supported: 64, 128)", p->block_size);
+    if (!(p->alpha >= 0.f && p->alpha <= 1.f))
+        return fail(FP_INVALID_ARGUMENT, "alpha must lie in [0, 1] (got %g)", (double)p->alpha);
+    if (!std::isfinite(p->softmax_scale))
+        return fail(FP_INVALID_ARGUMENT, "softmax_scale must be finite");
+    if (p->mean_correction != 0 && p->mean_correction != 1)
+        return fail(FP_INVALID_ARGUMENT, "mean_correction must be 0 or 1");
+    if (p->dtype != FP_DTYPE_BF16 && p->dtype != FP_DTYPE_FP8_E4M3FN)
+        return fail(FP_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
+    return FP_OK;
+}
+
+float sigma_of(const fp_params& p) {
+    return p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.head_dim));
+}
+
+// Validate cu_seqlens_host and fill the request table.  items_per_tile = 1
+// counts query blocks; TI counts tiles of TI query blocks (selection).
+int build_table(const fp_params& p, const int32_t* cu, int32_t batch, int items_per_tile, SeqTable& t) {
+    if (!cu) return fail(FP_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
+    if (batch < 1) return fail(FP_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
+    if (batch > FP_MAX_BATCH) return fail(FP_UNSUPPORTED, "batch %d exceeds %d", batch, FP_MAX_BATCH);
+    if (cu[0] != 0) return fail(FP_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+    const int B = p.block_size;
+    std::memset(&t, 0, sizeof t);
+    t.batch = batch;
+    int64_t blocks = 0, idx = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (cu[b + 1] < cu[b]) return fail(FP_INVALID_ARGUMENT, "cu_seqlens not non-decreasing at %d", b + 1);
+        const int64_t len = (int64_t)cu[b + 1] - cu[b];
+        const int64_t nb = (len + B - 1) / B;
+        if (nb > FP_MAX_BLOCKS / 2)
+            return fail(FP_UNSUPPORTED, "request %d has %lld blocks (max %d)", b, (long long)nb, FP_MAX_BLOCKS / 2);
+        t.tok_off[b] = cu[b];
+        t.blk_off[b] = (int32_t)blocks;
+        t.idx_off[b] = idx;
+        blocks += nb;
+        idx += (int64_t)p.num_q_heads * tri(nb);
+    }
+    t.tok_off[batch] = cu[batch];
+    t.blk_off[batch] = (int32_t)blocks;
+    t.idx_off[batch] = idx;
+    t.total_tokens = cu[batch];
+    t.total_blocks = (int32_t)blocks;
+    std::vector<int> ord(batch);
+    for (int b = 0; b < batch; ++b) ord[b] = b;
+    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) {
+        return (cu[x + 1] - cu[x]) > (cu[y + 1] - cu[y]);
+    });
+    int64_t items = 0;
+    for (int s = 0; s < batch; ++s) {
+        const int b = ord[s];
+        const int nb = t.blk_off[b + 1] - t.blk_off[b];
+        t.order[s] = b;
+        t.item_off[s] = (int32_t)items;
+        items += (nb + items_per_tile - 1) / items_per_tile;
+    }
+    t.item_off[batch] = (int32_t)items;
+    t.total_items = (int32_t)items;
+    if ((int64_t)items * p.num_q_heads > 0x7fffffff)
+        return fail(FP_UNSUPPORTED, "too many work items");
+    return FP_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return FP_OK;
+    return fail(FP_DEVICE_ERROR, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+int select_tile(const fp_params& p) { return 32 / (p.num_q_heads / p.num_kv_heads); }
+
+int run_select(const fp_params& p, const int32_t* cu, int32_t batch, const void* q, const void* k, const void* v,
+               const KVLayout& kv, bool paged, float* pq, float* pk, float* pv, int32_t* kv_idx,
+               int32_t* kv_cnt, hipStream_t st) {
+    SeqTable t;
+    int rc = build_table(p, cu, batch, 1, t);
+    if (rc) return rc;
+    PoolArgs pa;
+    pa.q = static_cast<const uint16_t*>(q);
+    pa.k = static_cast<const uint16_t*>(k);
+    pa.v = pv ? static_cast<const uint16_t*>(v) : nullptr;
+    pa.pq = pq;
+    pa.pk = pk;
+    pa.pv = pv;
+    pa.kv = kv;
+    pa.Hq = p.num_q_heads;
+    pa.Hkv = p.num_kv_heads;
+    pa.D = p.head_dim;
+    pa.B = p.block_size;
+    pa.q_chunks = p.num_q_heads * p.head_dim / 8;
+    pa.k_chunks = p.num_kv_heads * p.head_dim / 8;
+    pa.total_chunks = pa.q_chunks + pa.k_chunks * (pv ? 2 : 1);
+    rc = device_status(launch_pool(pa, t, paged, st), "pool");
+    if (rc) return rc;
+
+    SeqTable ts;
+    const int TI = select_tile(p);
+    rc = build_table(p, cu, batch, TI, ts);
+    if (rc) return rc;
+    SelArgs sa;
+    sa.pq = pq;
+    sa.pk = pk;
+    sa.kv_idx = kv_idx;
+    sa.kv_cnt = kv_cnt;
+    sa.Hq = p.num_q_heads;
+    sa.Hkv = p.num_kv_heads;
+    sa.g = p.num_q_heads / p.num_kv_heads;
+    sa.D = p.head_dim;
+    sa.TI = TI;
+    sa.scale = sigma_of(p);
+    sa.ln_alpha = p.alpha > 0.f ? (float)std::log((double)p.alpha) : -INFINITY;
+    return device_status(launch_select(sa, ts, st), "select");
+}
+
+}  // namespace
+
+FP_EXPORT const char* fp_status_string(int status) {
+    switch (status) {
+        case FP_OK: return "ok";
+        case FP_INVALID_ARGUMENT: return "invalid argument";
+        case FP_UNSUPPORTED: return "unsupported";
+        case FP_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case FP_DEVICE_ERROR: return "device error";
+        default: return "unknown status";
+    }
+}
+
+FP_EXPORT const char* fp_last_error(void) { return g_last_error.c_str(); }
+
+FP_EXPORT int64_t fp_index_capacity(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
+    SeqTable t;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return -1;
+    return t.idx_off[batch];
+}
+
+FP_EXPORT int64_t fp_count_entries(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
+    SeqTable t;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return -1;
+    return (int64_t)params->num_q_heads * t.total_blocks;
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+struct WsLayout {
+    size_t q, k, v, total;
+};
+WsLayout ws_layout(const fp_params& p, int64_t total_blocks) {
+    WsLayout w;
+    const size_t per = (size_t)total_blocks * p.head_dim * sizeof(float);
+    w.q = 0;
+    w.k = align256(per * p.num_q_heads);
+    w.v = w.k + align256(per * p.num_kv_heads);
+    w.total = w.v + (p.mean_correction ? align256(per * p.num_kv_heads) : 0);
+    return w;
+}
+}  // namespace
+
+FP_EXPORT size_t fp_varlen_workspace_bytes(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
+    SeqTable t;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return 0;
+    return ws_layout(*params, t.total_blocks).total;
+}
+
+FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const void* k, const void* v, int32_t seqlen,
+                               float* pooled_q, float* pooled_k, float* pooled_v, int32_t* kv_idx, int32_t* kv_cnt,
+                               void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (seqlen < 0) return fail(FP_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", seqlen);
+    if (seqlen == 0) return ok();
+    if (!aligned(q, 16) || !aligned(k, 16)) return fail(FP_INVALID_ARGUMENT, "q and k must be non-NULL and 16-byte aligned");
+    if (!aligned(pooled_q, 16) || !aligned(pooled_k, 16))
+        return fail(FP_INVALID_ARGUMENT, "pooled_q and pooled_k must be non-NULL and 16-byte aligned");
+    if (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+        return fail(FP_INVALID_ARGUMENT, "kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
+    if (pooled_v && (!aligned(pooled_v, 16) || !aligned(v, 16)))
+        return fail(FP_INVALID_ARGUMENT, "pooled_v needs a non-NULL, 16-byte aligned v (and itself aligned)");
+    const int32_t cu[2] = {0, seqlen};
+    KVLayout kv = {nullptr, 1, 0, 0};
+    (void)hipGetLastError();
+    rc = run_select(*params, cu, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v, kv_idx, kv_cnt,
+                    static_cast<hipStream_t>(stream));
+    return rc ? rc : ok();
+}
+
+FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, const void* k, const void* v,
+                                    const float* q_scale, const float* k_scale, const float* v_scale, int32_t seqlen,
+                                    const int32_t* kv_idx, const int32_t* kv_cnt, const float* pooled_k,
+                                    const float* pooled_v, void* out, float* lse, void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    const fp_params& p = *params;
+    if (seqlen < 0) return fail(FP_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", seqlen);
+    if (seqlen == 0) return ok();
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(FP_INVALID_ARGUMENT, "q, k, v and out must be non-NULL and 16-byte aligned");
+    if (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+        return fail(FP_INVALID_ARGUMENT, "kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
+    if (p.mean_correction && (!aligned(pooled_k, 16) || !aligned(pooled_v, 16)))
+        return fail(FP_INVALID_ARGUMENT, "mean_correction needs 16-byte aligned pooled_k and pooled_v");
+    if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    const bool fp8 = p.dtype == FP_DTYPE_FP8_E4M3FN;
+    if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+        return fail(FP_INVALID_ARGUMENT, "fp8 inputs need q_scale, k_scale and v_scale");
+    const int32_t cu[2] = {0, seqlen};
+    SeqTable t;
+    rc = build_table(p, cu, 1, 1, t);
+    if (rc) return rc;
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.kv_idx = kv_idx;
+    a.kv_cnt = kv_cnt;
+    a.pk = pooled_k;
+    a.pv = pooled_v;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.kv = KVLayout{nullptr, 1, 0, 0};
+    a.Hq = p.num_q_heads;
+    a.Hkv = p.num_kv_heads;
+    a.g = p.num_q_heads / p.num_kv_heads;
+    a.scale_log2 = (float)(sigma_of(p) * 1.4426950408889634);
+    a.correction = p.mean_correction;
+    (void)hipGetLastError();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = fp8 ? device_status(launch_attn_fp8(a, t, p.head_dim, p.block_size, st), "attention (fp8)")
+             : device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, false, st), "attention");
+    return rc ? rc : ok();
+}
+
+FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q, const void* k_cache,
+                                             const void* v_cache, int32_t page_size, int32_t num_pages,
+                                             const int32_t* block_table, int32_t max_pages_per_seq,
+                                             const int32_t* cu_seqlens_host, int32_t batch,
+                                             int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    const fp_params& p = *params;
+    if (p.dtype != FP_DTYPE_BF16) return fail(FP_UNSUPPORTED, "the paged entry reads bf16 only");
+    SeqTable t;
+    rc = build_table(p, cu_seqlens_host, batch, 1, t);
+    if (rc) return rc;
+    if (page_size < 1 || p.block_size % page_size != 0)
+        return fail(FP_INVALID_ARGUMENT, "page_size (%d) must divide block_size (%d)", page_size, p.block_size);
+    if (num_pages < 1) return fail(FP_INVALID_ARGUMENT, "num_pages must be >= 1");
+    for (int b = 0; b < batch; ++b) {
+        const int64_t need = ((int64_t)cu_seqlens_host[b + 1] - cu_seqlens_host[b] + page_size - 1) / page_size;
+        if (need > max_pages_per_seq)
+            return fail(FP_INVALID_ARGUMENT, "request %d needs %lld pages > max_pages_per_seq %d", b,
+                        (long long)need, max_pages_per_seq);
+    }
+    if (t.total_tokens == 0) return ok();
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(FP_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be non-NULL and 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+        return fail(FP_INVALID_ARGUMENT, "block_table, kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    const WsLayout ws = ws_layout(p, t.total_blocks);
+    if (!aligned(workspace, 256)) return fail(FP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < ws.total)
+        return fail(FP_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", workspace_bytes, ws.total);
+    char* wsb = static_cast<char*>(workspace);
+    float* pq = reinterpret_cast<float*>(wsb + ws.q);
+    float* pk = reinterpret_cast<float*>(wsb + ws.k);
+    float* pv = p.mean_correction ? reinterpret_cast<float*>(wsb + ws.v) : nullptr;
+    KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    rc = run_select(p, cu_seqlens_host, batch, q, k_cache, v_cache, kv, true, pq, pk, pv, kv_idx, kv_cnt, st);
+    if (rc) return rc;
+    AttnArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.q_scale = a.k_scale = a.v_scale = nullptr;
+    a.kv_idx = kv_idx;
+    a.kv_cnt = kv_cnt;
+    a.pk = pk;
+    a.pv = pv;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.kv = kv;
+    a.Hq = p.num_q_heads;
+    a.Hkv = p.num_kv_heads;
+    a.g = p.num_q_heads / p.num_kv_heads;
+    a.scale_log2 = (float)(sigma_of(p) * 1.4426950408889634);
+    a.correction = p.mean_correction;
+    rc = device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, true, st), "attention (paged)");
+    return rc ? rc : ok();
+}

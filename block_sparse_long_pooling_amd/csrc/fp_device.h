@@ -1,0 +1,89 @@
+// Device-side definitions shared by the flashprefill kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define FP_TABLE_MAX 128   // requests per call (kernel-argument tables)
+#define FP_MAX_BLOCKS 8192 // query blocks per request (kept-block bitmap in LDS)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// Requests of one launch and the order in which workgroups visit them.
+// Work items of request b are counted by the launch (query blocks, query
+// block tiles, ...); sorted position s holds request order[s], longest first,
+// and its items start at rank item_off[s].  A single sequence is batch = 1.
+struct SeqTable {
+    int64_t idx_off[FP_TABLE_MAX + 1];   // start of request b's kv_idx region
+    int32_t tok_off[FP_TABLE_MAX + 1];   // cu_seqlens
+    int32_t blk_off[FP_TABLE_MAX + 1];   // cumulative query blocks
+    int32_t order[FP_TABLE_MAX];
+    int32_t item_off[FP_TABLE_MAX + 1];
+    int32_t batch;
+    int32_t total_tokens;
+    int32_t total_blocks;
+    int32_t total_items;
+};
+
+__device__ __forceinline__ int seq_len(const SeqTable& t, int b) { return t.tok_off[b + 1] - t.tok_off[b]; }
+__device__ __forceinline__ int seq_blocks(const SeqTable& t, int b) { return t.blk_off[b + 1] - t.blk_off[b]; }
+
+// Rank (in visiting order) -> (request, item index counted from the request's
+// last item, so that long rows go first).
+__device__ __forceinline__ void item_of(const SeqTable& t, int rank, int& b, int& local) {
+    int lo = 0, hi = t.batch - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (t.item_off[mid] <= rank) lo = mid; else hi = mid - 1;
+    }
+    b = t.order[lo];
+    local = rank - t.item_off[lo];
+}
+
+// Global query block -> request.
+__device__ __forceinline__ int request_of_block(const SeqTable& t, int gb) {
+    int lo = 0, hi = t.batch - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (t.blk_off[mid] <= gb) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Where the KV rows of a request live: contiguous [T, Hkv, d] or a page pool
+// [num_pages * page_size, Hkv, d] addressed through a block table.
+struct KVLayout {
+    const int32_t* block_table;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages;
+};
+
+// Row of token tr (0-based inside request b whose packed rows start at tok0);
+// -1 when the page id is out of range.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_row(const KVLayout& L, int b, int tok0, int tr) {
+    if (!PAGED) return (int64_t)tok0 + tr;
+    int page = L.block_table[(int64_t)b * L.max_pages + tr / L.page_size];
+    if ((unsigned)page >= (unsigned)L.num_pages) return -1;
+    return (int64_t)page * L.page_size + tr % L.page_size;
+}
+
+// Head permutation that puts the query heads of one KV head on one XCD when
+// workgroups are dispatched round-robin over 8 XCDs (slot = blockIdx % 8).
+__device__ __forceinline__ int xcd_head(int slot, int Hq) {
+    if (Hq % 8 != 0) return slot;
+    return (slot % 8) * (Hq / 8) + slot / 8;
+}

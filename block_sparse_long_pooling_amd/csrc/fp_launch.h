@@ -1,0 +1,54 @@
+// Host-side launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp_device.h"
+
+struct PoolArgs {
+    const uint16_t* q;   // bf16 [T, Hq, d]
+    const uint16_t* k;   // bf16 rows (contiguous or paged)
+    const uint16_t* v;   // may be null (then not pooled)
+    float* pq;           // [Hq, total_blocks, d]
+    float* pk;           // [Hkv, total_blocks, d]
+    float* pv;           // [Hkv, total_blocks, d] or null
+    KVLayout kv;
+    int32_t Hq, Hkv, D, B;
+    int32_t q_chunks;    // Hq * d / 8
+    int32_t k_chunks;    // Hkv * d / 8
+    int32_t total_chunks;
+};
+
+struct SelArgs {
+    const float* pq;
+    const float* pk;
+    int32_t* kv_idx;
+    int32_t* kv_cnt;
+    int32_t Hq, Hkv, g, D, TI;   // TI query blocks x g heads per workgroup (TI * g <= 32)
+    float scale;                 // sigma
+    float ln_alpha;              // threshold on s - max s (-inf keeps every causal block)
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* q_scale;        // fp8: [Hq, total_blocks]
+    const float* k_scale;        // fp8: [Hkv, total_blocks]
+    const float* v_scale;
+    const int32_t* kv_idx;
+    const int32_t* kv_cnt;
+    const float* pk;             // pooled [Hkv, total_blocks, d] (correction)
+    const float* pv;
+    uint16_t* out;               // bf16 [T, Hq, d]
+    float* lse;                  // [Hq, T] or null
+    KVLayout kv;
+    int32_t Hq, Hkv, g;
+    float scale_log2;            // sigma * log2(e)
+    int32_t correction;
+};
+
+hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s);
+hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, hipStream_t s);

@@ -1,0 +1,349 @@
+// Sparse flash attention over the kept KV blocks, with the mean-correction
+// term (FlashPrefill, gist.science technical summary, section 2.C: the kernel
+// walks per-query-block index lists, so skipped blocks cost no work; FlashPrefill
+// V2 abstract: mean correction, PackGQA-style memory access, FP8, paged KV).
+//
+// A workgroup owns one (query head h, query block I) of one request; each of
+// its BLK/32 waves owns 32 query rows.  Per kept block J the K tile and the V
+// tile go to LDS, then every wave computes
+//     S^T = K Q^T        (v_mfma_f32_32x32x16_bf16; lane = query, 16 keys per
+//                         32-key subtile in registers)
+//     online softmax     (exp2 domain, row statistics are per-lane scalars
+//                         combined with the partner lane l ^ 32)
+//     O^T += V^T P^T     (P straight from registers; V^T from LDS)
+// Transposed products keep the query index on the MFMA column (= lane), so
+// neither P nor the softmax statistics ever cross lanes through LDS.  V^T is
+// written to LDS through registers (8x8 transposes), with keys permuted inside
+// each 16-key group so that the 32x32 output layout of S^T is directly the
+// B operand layout of the PV product.
+//
+// Mean correction: after the kept blocks, the pooled K_bar / V_bar of the
+// skipped blocks J < I go through the same pipeline as one more "tile" per
+// BLK pooled blocks, with logit sigma*q.k_bar_J + ln n_J and every kept or
+// non-past block masked out.  Query heads of one KV head are placed on one
+// XCD so their K/V tiles meet in that XCD's L2.
+#include "fp_launch.h"
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Swap bits 2 and 3 of a key position inside its 16-key group.
+__device__ __forceinline__ int key_perm(int p) { return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// 8 rows x 8 bf16 (x[u] = row u) -> 8 columns (y[j] = column j of all rows).
+__device__ __forceinline__ void transpose8(const uint4* x, uint4* y) {
+    const uint32_t* xs = reinterpret_cast<const uint32_t*>(x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t a = xs[(2 * m) * 4 + j / 2];
+            const uint32_t c = xs[(2 * m + 1) * 4 + j / 2];
+            w[m] = (j & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+        }
+        y[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+__device__ __forceinline__ uint4 f32x8_to_bf16(const float4& a, const float4& b) {
+    return make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+}
+
+template <int D, int BLK>
+struct Tile {
+    static constexpr int NW = BLK / 32;     // waves per workgroup
+    static constexpr int NT = 64 * NW;      // threads
+    static constexpr int KCH = D / 8;       // 16-byte chunks per K row
+    static constexpr int VCH = BLK / 8;     // 16-byte chunks per V^T row
+    static constexpr int NSUB = BLK / 32;   // 32-key subtiles of S^T
+    static constexpr int NDS = D / 32;      // 32-row d subtiles of O^T
+};
+
+// K tile [BLK keys][D] and V^T tile [D][BLK keys (permuted)] of KV block J.
+template <int D, int BLK, bool PAGED>
+__device__ __forceinline__ void load_kv_tile(const uint16_t* kb, const uint16_t* vb, const KVLayout& L, int b,
+                                             int tok0, int len, int J, int Hkv, int hk, uint4* lk, uint4* lv,
+                                             int tid) {
+    using T = Tile<D, BLK>;
+    const int64_t rs = (int64_t)Hkv * D;
+    for (int i = tid; i < BLK * T::KCH; i += T::NT) {
+        const int row = i / T::KCH, ch = i % T::KCH;
+        const int tr = J * BLK + row;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (tr < len) {
+            const int64_t r = kv_row<PAGED>(L, b, tok0, tr);
+            if (r >= 0) val = *reinterpret_cast<const uint4*>(kb + r * rs + (int64_t)hk * D + ch * 8);
+        }
+        lk[row * T::KCH + (ch ^ (row % T::KCH))] = val;
+    }
+    for (int i = tid; i < T::VCH * T::KCH; i += T::NT) {
+        const int kg = i / T::KCH, dc = i % T::KCH;
+        uint4 x[8], y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tr = J * BLK + key_perm(8 * kg + u);
+            x[u] = make_uint4(0, 0, 0, 0);
+            if (tr < len) {
+                const int64_t r = kv_row<PAGED>(L, b, tok0, tr);
+                if (r >= 0) x[u] = *reinterpret_cast<const uint4*>(vb + r * rs + (int64_t)hk * D + dc * 8);
+            }
+        }
+        transpose8(x, y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int drow = 8 * dc + j;
+            lv[drow * T::VCH + (kg ^ (drow % T::VCH))] = y[j];
+        }
+    }
+}
+
+// Pooled K_bar / V_bar of blocks c0 .. c0+BLK-1 (zero for blocks >= I), as bf16.
+template <int D, int BLK>
+__device__ __forceinline__ void load_pooled_tile(const float* pk, const float* pv, int64_t prow0, int c0, int I,
+                                                 uint4* lk, uint4* lv, int tid) {
+    using T = Tile<D, BLK>;
+    for (int i = tid; i < BLK * T::KCH; i += T::NT) {
+        const int row = i / T::KCH, ch = i % T::KCH;
+        const int J = c0 + row;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (J < I) {
+            const float4* s = reinterpret_cast<const float4*>(pk + (prow0 + J) * D + ch * 8);
+            val = f32x8_to_bf16(s[0], s[1]);
+        }
+        lk[row * T::KCH + (ch ^ (row % T::KCH))] = val;
+    }
+    for (int i = tid; i < T::VCH * T::KCH; i += T::NT) {
+        const int kg = i / T::KCH, dc = i % T::KCH;
+        uint4 x[8], y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int J = c0 + key_perm(8 * kg + u);
+            x[u] = make_uint4(0, 0, 0, 0);
+            if (J < I) {
+                const float4* s = reinterpret_cast<const float4*>(pv + (prow0 + J) * D + dc * 8);
+                x[u] = f32x8_to_bf16(s[0], s[1]);
+            }
+        }
+        transpose8(x, y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int drow = 8 * dc + j;
+            lv[drow * T::VCH + (kg ^ (drow % T::VCH))] = y[j];
+        }
+    }
+}
+
+// S^T[sub] = K[32 sub + .., :] Q^T for this wave's 32 queries.
+template <int D, int BLK>
+__device__ __forceinline__ void qk_tile(const uint4* lk, const bf16x8* qf, int col, int half, f32x16* s) {
+    using T = Tile<D, BLK>;
+#pragma unroll
+    for (int sub = 0; sub < T::NSUB; ++sub) {
+        f32x16 acc = {};
+        const int row = 32 * sub + col;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const uint4 a = lk[row * T::KCH + ((half + 2 * kk) ^ (row % T::KCH))];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], acc, 0, 0, 0);
+        }
+        s[sub] = acc;
+    }
+}
+
+// O^T[dsub] += V^T[32 dsub + .., :] P^T.
+template <int D, int BLK>
+__device__ __forceinline__ void pv_tile(const uint4* lv, const uint32_t (*pk)[8], int col, int half, f32x16* o) {
+    using T = Tile<D, BLK>;
+#pragma unroll
+    for (int ds = 0; ds < T::NDS; ++ds) {
+        const int row = 32 * ds + col;
+#pragma unroll
+        for (int st = 0; st < BLK / 16; ++st) {
+            const uint4 a = lv[row * T::VCH + ((half + 2 * st) ^ (row % T::VCH))];
+            const uint32_t* p = &pk[st >> 1][4 * (st & 1)];
+            const uint4 bp = make_uint4(p[0], p[1], p[2], p[3]);
+            o[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, bp), o[ds], 0, 0, 0);
+        }
+    }
+}
+
+// Online-softmax update with logits x (log2 units, -inf = masked) already in s.
+// Packs P to bf16 pairs pk[sub][0..7] (registers 2i, 2i+1 of subtile sub).
+template <int NSUB, int NDS>
+__device__ __forceinline__ void softmax_update(f32x16* s, float& m, float& l, f32x16* o, uint32_t (*pk)[8]) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ds][r] *= alpha;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(s[sub][2 * i] - m_use);
+            const float p1 = __builtin_amdgcn_exp2f(s[sub][2 * i + 1] - m_use);
+            l += p0 + p1;
+            pk[sub][i] = pack_bf16(p0, p1);
+        }
+    }
+}
+
+template <int D, int BLK, bool PAGED>
+__global__ __launch_bounds__(2 * BLK) void k_attn_bf16(AttnArgs a, SeqTable t) {
+    using T = Tile<D, BLK>;
+    __shared__ uint4 lk[BLK * T::KCH];
+    __shared__ uint4 lv[D * T::VCH];
+    __shared__ uint32_t kept_bits[FP_MAX_BLOCKS / 32];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int rank = blockIdx.x / a.Hq;
+    const int h = xcd_head(blockIdx.x % a.Hq, a.Hq);
+    int b, local;
+    item_of(t, rank, b, local);
+    const int nb = seq_blocks(t, b);
+    const int I = nb - 1 - local;
+    const int tok0 = t.tok_off[b];
+    const int len = t.tok_off[b + 1] - tok0;
+    const int q0 = tok0 + I * BLK;
+    const int nI = min(BLK, len - I * BLK);
+    const int hk = h / a.g;
+    const int32_t* list = a.kv_idx + t.idx_off[b] + (int64_t)h * ((int64_t)nb * (nb + 1) / 2) +
+                          (int64_t)I * (I + 1) / 2;
+    const int cnt = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)h * nb + I];
+    const int qr = 32 * w + col;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vb = static_cast<const uint16_t*>(a.v);
+
+    bf16x8 qf[D / 16];
+    {
+        const uint16_t* qp = qb + ((int64_t)(q0 + qr) * a.Hq + h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (qr < nI) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+            qf[kk] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+    const float c = a.scale_log2;
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[T::NDS];
+#pragma unroll
+    for (int ds = 0; ds < T::NDS; ++ds) o[ds] = f32x16{};
+    f32x16 s[T::NSUB];
+    uint32_t pk[T::NSUB][8];
+
+    for (int it = 0; it < cnt; ++it) {
+        const int J = list[it];
+        __syncthreads();
+        load_kv_tile<D, BLK, PAGED>(kb, vb, a.kv, b, tok0, len, J, a.Hkv, hk, lk, lv, tid);
+        __syncthreads();
+        qk_tile<D, BLK>(lk, qf, col, half, s);
+        const bool diag = (J == I);
+#pragma unroll
+        for (int sub = 0; sub < T::NSUB; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
+                s[sub][r] = (diag && key > qr) ? -INFINITY : s[sub][r] * c;
+            }
+        softmax_update<T::NSUB, T::NDS>(s, m, l, o, pk);
+        pv_tile<D, BLK>(lv, pk, col, half, o);
+    }
+
+    if (a.correction && I > 0) {
+        const int nwords = (I + 31) >> 5;
+        for (int i = tid; i < nwords; i += T::NT) kept_bits[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += T::NT) {
+            const int J = list[i];
+            if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
+        }
+        __syncthreads();
+        const int64_t prow0 = (int64_t)hk * t.total_blocks + t.blk_off[b];
+        // Every block J < I of a request is full, so ln n_J = ln BLK (log2 units here).
+        const float log2_blk = __log2f((float)BLK);
+        for (int c0 = 0; c0 < I; c0 += BLK) {
+            const int c1 = min(I, c0 + BLK);
+            int kept = 0;
+            for (int wd = c0 >> 5; wd < (c1 + 31) >> 5; ++wd) {
+                uint32_t bits = kept_bits[wd];
+                const int lo = max(c0, wd * 32) - wd * 32, hi = min(c1, wd * 32 + 32) - wd * 32;
+                const uint32_t mask = (hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+                kept += __popc(bits & mask);
+            }
+            if (kept == c1 - c0) continue;                 // nothing skipped in this range
+            __syncthreads();
+            load_pooled_tile<D, BLK>(a.pk, a.pv, prow0, c0, I, lk, lv, tid);
+            __syncthreads();
+            qk_tile<D, BLK>(lk, qf, col, half, s);
+#pragma unroll
+            for (int sub = 0; sub < T::NSUB; ++sub)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int J = c0 + 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
+                    const bool skipped = J < I && !((kept_bits[min(J, I - 1) >> 5] >> (J & 31)) & 1u);
+                    s[sub][r] = skipped ? fmaf(s[sub][r], c, log2_blk) : -INFINITY;
+                }
+            softmax_update<T::NSUB, T::NDS>(s, m, l, o, pk);
+            pv_tile<D, BLK>(lv, pk, col, half, o);
+        }
+    }
+
+    // Epilogue: normalise, stage the bf16 tile in LDS, store full rows.
+    const float l_tot = l + __shfl_xor(l, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int ds = 0; ds < T::NDS; ++ds)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int chunk = 4 * ds + g4;        // d0 = 32 ds + 8 g4 + 4 half
+            uint2 v2 = make_uint2(pack_bf16(o[ds][4 * g4] * inv, o[ds][4 * g4 + 1] * inv),
+                                  pack_bf16(o[ds][4 * g4 + 2] * inv, o[ds][4 * g4 + 3] * inv));
+            reinterpret_cast<uint2*>(&lk[qr * T::KCH + (chunk ^ (qr % T::KCH))])[half] = v2;
+        }
+    __syncthreads();
+    for (int i = tid; i < nI * T::KCH; i += T::NT) {
+        const int row = i / T::KCH, ch = i % T::KCH;
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(q0 + row) * a.Hq + h) * D + ch * 8) =
+            lk[row * T::KCH + (ch ^ (row % T::KCH))];
+    }
+    if (a.lse && half == 0 && qr < nI)
+        a.lse[(int64_t)h * t.total_tokens + q0 + qr] = (m + __log2f(l_tot)) * kLn2;
+}
+
+template <int D, int BLK>
+hipError_t launch_attn_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+    dim3 grid((unsigned)t.total_items * a.Hq);
+    if (paged)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, true>), grid, dim3(2 * BLK), 0, s, a, t);
+    else
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, false>), grid, dim3(2 * BLK), 0, s, a, t);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s) {
+    if (t.total_items == 0) return hipSuccess;
+    if (D == 128 && B == 128) return launch_attn_t<128, 128>(a, t, paged, s);
+    if (D == 128 && B == 64) return launch_attn_t<128, 64>(a, t, paged, s);
+    if (D == 64 && B == 128) return launch_attn_t<64, 128>(a, t, paged, s);
+    if (D == 64 && B == 64) return launch_attn_t<64, 64>(a, t, paged, s);
+    return hipErrorInvalidValue;
+}

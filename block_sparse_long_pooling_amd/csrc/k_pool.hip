@@ -1,0 +1,97 @@
+// Block-mean pooling of Q, K and V (FlashPrefill, gist.science technical
+// summary, section 2.A: keys are replaced by their block mean; queries are
+// pooled the same way, and V is pooled for the V2 mean-correction term).
+//
+// One workgroup covers one query block of one request and 256 column chunks
+// of 8 bf16 (16 bytes) taken from the concatenated row [Q | K | V].  Each
+// thread walks the block's tokens, so a wave reads 1 KiB contiguous per
+// token step; the token loop is unrolled 8 deep so that every thread keeps 8
+// loads in flight.  Sums are fp32 in token order, then divided by n_J.
+#include "fp_launch.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+__device__ __forceinline__ void add8(float* acc, uint4 x) {
+    acc[0] += bf16_lo(x.x); acc[1] += bf16_hi(x.x);
+    acc[2] += bf16_lo(x.y); acc[3] += bf16_hi(x.y);
+    acc[4] += bf16_lo(x.z); acc[5] += bf16_hi(x.z);
+    acc[6] += bf16_lo(x.w); acc[7] += bf16_hi(x.w);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
+    const int gb = blockIdx.x;
+    const int c = blockIdx.y * kThreads + threadIdx.x;
+    if (c >= a.total_chunks) return;
+    const int b = request_of_block(t, gb);
+    const int I = gb - t.blk_off[b];
+    const int tok0 = t.tok_off[b];
+    const int len = t.tok_off[b + 1] - tok0;
+    const int t0 = I * a.B;
+    const int n = min(a.B, len - t0);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float* dst;
+    int col;
+    if (c < a.q_chunks) {
+        // Q: packed rows, never paged.
+        col = c * 8;
+        dst = a.pq;
+        const int64_t row_elems = (int64_t)a.Hq * a.D;
+        const uint16_t* p = a.q + (int64_t)(tok0 + t0) * row_elems + col;
+        int r = 0;
+        for (; r + kUnroll <= n; r += kUnroll) {
+            uint4 x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                x[u] = *reinterpret_cast<const uint4*>(p + (int64_t)(r + u) * row_elems);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
+        }
+        for (; r < n; ++r) add8(acc, *reinterpret_cast<const uint4*>(p + (int64_t)r * row_elems));
+    } else {
+        int cc = c - a.q_chunks;
+        const uint16_t* base = a.k;
+        dst = a.pk;
+        if (cc >= a.k_chunks) { cc -= a.k_chunks; base = a.v; dst = a.pv; }
+        col = cc * 8;
+        const int64_t row_elems = (int64_t)a.Hkv * a.D;
+        int r = 0;
+        for (; r + kUnroll <= n; r += kUnroll) {
+            uint4 x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t row = kv_row<PAGED>(a.kv, b, tok0, t0 + r + u);
+                x[u] = row >= 0 ? *reinterpret_cast<const uint4*>(base + row * row_elems + col)
+                                : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
+        }
+        for (; r < n; ++r) {
+            const int64_t row = kv_row<PAGED>(a.kv, b, tok0, t0 + r);
+            if (row >= 0) add8(acc, *reinterpret_cast<const uint4*>(base + row * row_elems + col));
+        }
+    }
+    const int h = col / a.D;
+    const int dd = col % a.D;
+    const float fn = (float)n;
+    float* o = dst + ((int64_t)h * t.total_blocks + gb) * a.D + dd;
+    reinterpret_cast<float4*>(o)[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+    reinterpret_cast<float4*>(o)[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+    if (t.total_blocks == 0) return hipSuccess;
+    dim3 grid(t.total_blocks, (a.total_chunks + kThreads - 1) / kThreads);
+    if (paged)
+        hipLaunchKernelGGL(k_pool<true>, grid, dim3(kThreads), 0, s, a, t);
+    else
+        hipLaunchKernelGGL(k_pool<false>, grid, dim3(kThreads), 0, s, a, t);
+    return hipGetLastError();
+}

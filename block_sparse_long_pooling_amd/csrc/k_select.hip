@@ -1,0 +1,179 @@
+// Pooled block scores, max-based dynamic threshold and list compaction
+// (FlashPrefill, gist.science technical summary, sections 2.A-2.C).
+//
+// For query head h and query block I, s[J] = sigma * q_bar[h,I] . k_bar[h/g,J]
+// over J <= I.  Block J is kept iff its softmax score is at least alpha times
+// the row's largest, i.e. s[J] - max_J s >= ln(alpha).  Kept blocks are
+// written in ascending J to the (h, I) list, which is never empty.
+//
+// One wave owns 32 score rows: TI consecutive query blocks x the g query
+// heads of one KV head, so every k_bar row it loads serves 32 rows.  The
+// (L/B)^2 score matrix is never stored: pass 1 takes each row's max, pass 2
+// recomputes the same scores (same instruction sequence, bit-identical) and
+// compacts with a wave ballot.  The dot products run on bf16 MFMA with each
+// fp32 operand split into hi + lo bf16 parts (hi*hi + hi*lo + lo*hi), which
+// is within ~2^-17 of the fp32 product sum -- far below the 1e-3 band in
+// which the threshold decision is allowed to differ from an exact one.
+#include "fp_launch.h"
+
+// Scores feed both the row max (pass 1) and the compare s - max (pass 2); no
+// multiply may be fused into a later add, or the two passes would disagree.
+#pragma clang fp contract(off)
+
+namespace {
+
+__device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& lo) {
+    float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __bf16 h = (__bf16)x[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(x[i] - (float)h);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 tile_scores(const bf16x8* qh, const bf16x8* ql, const float4* kb, float scale) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        bf16x8 kh, kl;
+        split8(kb[2 * kk], kb[2 * kk + 1], kh, kl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] *= scale;
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ void load_kbar(const float* pk, int64_t row0, int J, int nb, int half, float4* kb) {
+    if (J < nb) {
+        const float4* src = reinterpret_cast<const float4*>(pk + (row0 + J) * D + 8 * half);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            kb[2 * kk] = src[4 * kk];       // d = 8*half + 16*kk .. +3
+            kb[2 * kk + 1] = src[4 * kk + 1];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) kb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void k_select(SelArgs a, SeqTable t) {
+    const int lane = threadIdx.x;
+    const int rank = blockIdx.x / a.Hkv;
+    const int hk = blockIdx.x % a.Hkv;
+    int b, local;
+    item_of(t, rank, b, local);
+    const int nb = seq_blocks(t, b);
+    const int ntiles = (nb + a.TI - 1) / a.TI;
+    const int I0 = (ntiles - 1 - local) * a.TI;
+    const int gblk0 = t.blk_off[b];
+    const int rows = a.TI * a.g;
+    const int rho = lane & 31;
+    const int half = lane >> 5;
+
+    // A operand: row rho = (query block I0 + rho / g, head hk*g + rho % g).
+    bf16x8 qh[D / 16], ql[D / 16];
+    {
+        const int I = I0 + rho / a.g;
+        const int h = hk * a.g + rho % a.g;
+        const bool valid = rho < rows && I < nb;
+        const float4* src = reinterpret_cast<const float4*>(
+            a.pq + ((int64_t)h * t.total_blocks + gblk0 + (valid ? I : 0)) * D + 8 * half);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            float4 x0 = valid ? src[4 * kk] : make_float4(0.f, 0.f, 0.f, 0.f);
+            float4 x1 = valid ? src[4 * kk + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+            split8(x0, x1, qh[kk], ql[kk]);
+        }
+    }
+    // Output register r of this lane holds row (r%4) + 8*(r/4) + 4*half.
+    int rowI[16];
+    bool rowOk[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int rr = (r & 3) + 8 * (r >> 2) + 4 * half;
+        rowI[r] = I0 + rr / a.g;
+        rowOk[r] = rr < rows && rowI[r] < nb;
+    }
+    const int ncol = min(nb, I0 + a.TI);
+    const int64_t krow0 = (int64_t)hk * t.total_blocks + gblk0;
+
+    // Pass 1: row maxima over the causal blocks.
+    float m[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = -INFINITY;
+    float4 kb[D / 8], kn[D / 8];
+    load_kbar<D>(a.pk, krow0, rho, nb, half, kb);
+    for (int c0 = 0; c0 < ncol; c0 += 32) {
+        if (c0 + 32 < ncol) load_kbar<D>(a.pk, krow0, c0 + 32 + rho, nb, half, kn);
+        const f32x16 s = tile_scores<D>(qh, ql, kb, a.scale);
+        const int J = c0 + rho;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (rowOk[r] && J <= rowI[r]) m[r] = fmaxf(m[r], s[r]);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) kb[i] = kn[i];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
+    }
+
+    // Pass 2: same scores, threshold, ordered compaction by ballot.
+    int cnt[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cnt[r] = 0;
+    load_kbar<D>(a.pk, krow0, rho, nb, half, kb);
+    const uint32_t below = (1u << rho) - 1u;
+    for (int c0 = 0; c0 < ncol; c0 += 32) {
+        if (c0 + 32 < ncol) load_kbar<D>(a.pk, krow0, c0 + 32 + rho, nb, half, kn);
+        const f32x16 s = tile_scores<D>(qh, ql, kb, a.scale);
+        const int J = c0 + rho;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const bool keep = rowOk[r] && J <= rowI[r] && (s[r] - m[r] >= a.ln_alpha);
+            const uint64_t mask = __ballot(keep);
+            const uint32_t bits = half ? (uint32_t)(mask >> 32) : (uint32_t)mask;
+            if (keep) {
+                const int rr = (r & 3) + 8 * (r >> 2) + 4 * half;
+                const int h = hk * a.g + rr % a.g;
+                const int I = rowI[r];
+                const int64_t base = t.idx_off[b] + (int64_t)h * ((int64_t)nb * (nb + 1) / 2) +
+                                     (int64_t)I * (I + 1) / 2;
+                a.kv_idx[base + cnt[r] + __popc(bits & below)] = J;
+            }
+            cnt[r] += __popc(bits);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) kb[i] = kn[i];
+    }
+    if (rho == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (!rowOk[r]) continue;
+            const int rr = (r & 3) + 8 * (r >> 2) + 4 * half;
+            const int h = hk * a.g + rr % a.g;
+            a.kv_cnt[(int64_t)a.Hq * gblk0 + (int64_t)h * nb + rowI[r]] = cnt[r];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s) {
+    if (t.total_items == 0) return hipSuccess;
+    dim3 grid(t.total_items * a.Hkv);
+    if (a.D == 64)
+        hipLaunchKernelGGL(k_select<64>, grid, dim3(64), 0, s, a, t);
+    else
+        hipLaunchKernelGGL(k_select<128>, grid, dim3(64), 0, s, a, t);
+    return hipGetLastError();
+}

@@ -1,0 +1,151 @@
+/*
+ * flashprefill.h -- block-sparse causal prefill attention for MI355X (gfx950).
+ *
+ * The method (FlashPrefill, gist.science technical summary, section 2; and
+ * FlashPrefill V2, abstract):
+ *   1. block-mean pooling of Q and K ("Approximation par Blocs", 2.A), and of
+ *      V for the mean-correction term;
+ *   2. pooled block logits s[h,I,J] = sigma * q_bar[h,I] . k_bar[h/g,J], J <= I,
+ *      whose row softmax is the block score (2.A, fused 2D reduction: the
+ *      L x L/B score matrix never exists, and the L/B x L/B one stays on chip);
+ *   3. max-based dynamic threshold (2.B, threshold equation):
+ *      keep J iff Score[I,J] >= alpha * max_{J' <= I} Score[I,J'],
+ *      evaluated as s - max(s) >= ln(alpha);
+ *   4. one ascending list of kept KV blocks per (query head, query block),
+ *      walked by index so skipped blocks cost nothing (2.C, physical skip);
+ *   5. flash attention over the kept blocks, plus the mean-correction term of
+ *      V2 (abstract): every skipped block J < I enters row i's softmax as one
+ *      entry with logit sigma * q_i . k_bar_J + ln n_J and value v_bar_J.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless the name ends in _host.  Device
+ *     buffers are contiguous, row-major and 16-byte aligned.
+ *   - bf16 tensors are IEEE bfloat16; fp8 tensors are OCP e4m3fn bytes.
+ *   - Q is [S, Hq, d] token-major; K and V are [S, Hkv, d]; query head h reads
+ *     KV head h / (Hq / Hkv).
+ *   - B = block_size; nB = ceil(S / B); n_J = tokens in block J.
+ *   - Block lists: kv_idx holds, for each sequence, a triangular region of
+ *     Hq * nB * (nB + 1) / 2 int32; the list of (h, I) starts at
+ *     h * nB * (nB + 1) / 2 + I * (I + 1) / 2 and has capacity I + 1.  kv_cnt
+ *     holds Hq * nB int32 per sequence, entry h * nB + I = list length.  In a
+ *     batch, sequence b's regions follow sequence b-1's.
+ *   - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream: it never allocates, frees or synchronises,
+ *     and keeps no pointer after it returns.  The caller owns every buffer and
+ *     keeps it alive until the stream has passed the work.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued.  On a non-zero return nothing was launched and no output was
+ *     written; fp_last_error() then describes the problem.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ */
+#ifndef FLASHPREFILL_H
+#define FLASHPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define FP_OK                   0
+#define FP_INVALID_ARGUMENT     1   /* NULL / misaligned pointer, bad size, alpha outside [0,1] ... */
+#define FP_UNSUPPORTED          2   /* a valid request this build does not implement (e.g. d = 96) */
+#define FP_WORKSPACE_TOO_SMALL  3
+#define FP_DEVICE_ERROR         4   /* a launch was rejected by the HIP runtime */
+
+/* Element type of the q/k/v that an attention call reads. */
+#define FP_DTYPE_BF16        0
+#define FP_DTYPE_FP8_E4M3FN  1
+
+typedef struct {
+    int32_t num_q_heads;      /* Hq, a multiple of num_kv_heads */
+    int32_t num_kv_heads;     /* Hkv >= 1 */
+    int32_t head_dim;         /* d: 64 or 128 */
+    int32_t block_size;       /* B: 64 or 128 (query block = KV block = pooling block) */
+    float   alpha;            /* threshold ratio, 0 <= alpha <= 1; 0 keeps every causal block */
+    float   softmax_scale;    /* sigma for scores and attention; <= 0 means 1/sqrt(d) */
+    int32_t mean_correction;  /* 1: add the mean-correction entries of skipped blocks */
+    int32_t dtype;            /* FP_DTYPE_*: element type of q/k/v in the attention call */
+} fp_params;
+
+/*
+ * Selection: steps 1-4 for one sequence of length seqlen (FlashPrefill 2.A-2.C).
+ *   q [S,Hq,d], k [S,Hkv,d], v [S,Hkv,d]: bf16, whatever params->dtype says
+ *     (fp8 attention selects on the bf16 data).  v may be NULL when pooled_v is.
+ *   pooled_q [Hq,nB,d], pooled_k [Hkv,nB,d], pooled_v [Hkv,nB,d]: fp32 outputs,
+ *     means over the valid tokens of each block.  pooled_v may be NULL (then V
+ *     is not read); the mean correction in fp_sparse_prefill_fwd needs it.
+ *   kv_idx, kv_cnt: int32 outputs in the list layout above.
+ * Lists are ascending and never empty: the row's best block always passes.
+ */
+int fp_select_blocks(const fp_params* params,
+                     const void* q, const void* k, const void* v, int32_t seqlen,
+                     float* pooled_q, float* pooled_k, float* pooled_v,
+                     int32_t* kv_idx, int32_t* kv_cnt, void* stream);
+
+/*
+ * Attention: step 5 for one sequence, over the lists from fp_select_blocks
+ * (FlashPrefill 2.C; V2 abstract for the correction, PackGQA and FP8).
+ *   q [S,Hq,d], k, v [S,Hkv,d]: bf16, or e4m3fn bytes when params->dtype is
+ *     FP_DTYPE_FP8_E4M3FN; then q_scale [Hq,nB], k_scale, v_scale [Hkv,nB] are
+ *     fp32 per-(head, block) scales, x = code * scale, and block = block_size.
+ *     The scale pointers are ignored for bf16.
+ *   kv_idx, kv_cnt: lists in the layout above.
+ *   pooled_k, pooled_v: fp32 [Hkv,nB,d] from fp_select_blocks; required when
+ *     params->mean_correction is 1, ignored otherwise.
+ *   out [S,Hq,d] bf16 (written); lse [Hq,S] fp32 natural-log sum of exp of
+ *     each row's logits (written when not NULL).
+ */
+int fp_sparse_prefill_fwd(const fp_params* params,
+                          const void* q, const void* k, const void* v,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          int32_t seqlen, const int32_t* kv_idx, const int32_t* kv_cnt,
+                          const float* pooled_k, const float* pooled_v,
+                          void* out, float* lse, void* stream);
+
+/*
+ * Continuous batch over a paged KV cache: steps 1-5 for `batch` requests
+ * (FlashPrefill V2 abstract: paged KV cache and continuous batching).  Each
+ * request is a pure prefill (query length = KV length = its length); blocks
+ * start at each request's first token and no request sees another's tokens.
+ *   q [T,Hq,d] bf16, T = cu_seqlens_host[batch]: requests packed back to back.
+ *   k_cache, v_cache [num_pages, page_size, Hkv, d] bf16.  Token t of request b
+ *     lives in page block_table[b * max_pages_per_seq + t / page_size], slot
+ *     t % page_size.  block_size must be a multiple of page_size.  Page ids
+ *     outside [0, num_pages) read as zeros.
+ *   cu_seqlens_host [batch+1] int32, host memory read during the call:
+ *     0 = cu[0] <= cu[1] <= ... (request b is tokens cu[b] .. cu[b+1]-1 of q).
+ *   kv_idx, kv_cnt: list outputs, regions of consecutive requests concatenated
+ *     (sizes from fp_index_capacity / fp_count_entries).
+ *   workspace: device scratch of at least fp_varlen_workspace_bytes() bytes
+ *     (pooled means); contents on return are unspecified.
+ *   out [T,Hq,d] bf16, lse [Hq,T] fp32 or NULL.
+ * bf16 only (FP_UNSUPPORTED for fp8).  batch <= FP_MAX_BATCH.
+ */
+#define FP_MAX_BATCH 128
+int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   int32_t page_size, int32_t num_pages,
+                                   const int32_t* block_table, int32_t max_pages_per_seq,
+                                   const int32_t* cu_seqlens_host, int32_t batch, int32_t* kv_idx, int32_t* kv_cnt,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* out, float* lse, void* stream);
+
+/* Sizes (host only, no device work).  A single sequence of length S is
+ * cu_seqlens_host = {0, S}, batch = 1.  Return -1 / 0 on invalid arguments. */
+int64_t fp_index_capacity(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch);
+int64_t fp_count_entries(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch);
+size_t  fp_varlen_workspace_bytes(const fp_params* params, const int32_t* cu_seqlens_host,
+                                  int32_t batch);
+
+/* Static text for a return code. */
+const char* fp_status_string(int status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* fp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHPREFILL_H */

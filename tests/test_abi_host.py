@@ -1,0 +1,133 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every entry point the header declares, sizes its buffers as documented, and
+rejects bad arguments with the documented status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_pooling_amd as fp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashprefill.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"fp_select_blocks", "fp_sparse_prefill_fwd", "fp_sparse_prefill_varlen_paged"} <= set(names)
+    l = fp.lib()
+    for n in names:
+        assert hasattr(l, n), n
+    assert set(names) == set(fp.EXPORTS)
+
+
+def test_status_strings():
+    l = fp.lib()
+    assert l.fp_status_string(0) == b"ok"
+    assert l.fp_status_string(3) == b"workspace too small"
+    assert l.fp_status_string(99) == b"unknown status"
+
+
+def _p(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=128, alpha=0.1)
+    base.update(kw)
+    return fp.make_params(**base)
+
+
+def test_sizes():
+    p = _p()
+    S = 1000
+    nB = 8
+    assert fp.fp_index_capacity(p, [0, S]) == 32 * nB * (nB + 1) // 2
+    assert fp.fp_count_entries(p, [0, S]) == 32 * nB
+    cu = [0, 100, 300, 300, 1000]
+    nbs = [1, 2, 0, 6]
+    assert fp.fp_index_capacity(p, cu) == sum(32 * n * (n + 1) // 2 for n in nbs)
+    assert fp.fp_count_entries(p, cu) == 32 * sum(nbs)
+    ws = fp.fp_varlen_workspace_bytes(p, cu)
+    per = sum(nbs) * 128 * 4
+    assert ws >= per * (32 + 8 + 8)
+    p0 = _p(mean_correction=False)
+    assert fp.fp_varlen_workspace_bytes(p0, cu) < ws
+    assert fp.fp_index_capacity(_p(head_dim=96), [0, S]) == -1
+    assert fp.fp_index_capacity(p, [1, S]) == -1
+
+
+BAD_PARAMS = [
+    (dict(num_q_heads=30, num_kv_heads=8), fp.FP_INVALID_ARGUMENT),
+    (dict(num_kv_heads=0), fp.FP_INVALID_ARGUMENT),
+    (dict(head_dim=96), fp.FP_UNSUPPORTED),
+    (dict(block_size=32), fp.FP_UNSUPPORTED),
+    (dict(alpha=-0.1), fp.FP_INVALID_ARGUMENT),
+    (dict(alpha=1.5), fp.FP_INVALID_ARGUMENT),
+    (dict(alpha=float("nan")), fp.FP_INVALID_ARGUMENT),
+    (dict(num_q_heads=64, num_kv_heads=1), fp.FP_UNSUPPORTED),
+]
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+@pytest.mark.parametrize("kw,status", BAD_PARAMS)
+def test_bad_params_rejected(kw, status):
+    l = fp.lib()
+    p = _p(**kw)
+    rc = l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == status
+    assert l.fp_last_error().decode()
+    rc = l.fp_sparse_prefill_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, None, None)
+    assert rc == status
+
+
+def test_bad_pointers_rejected():
+    l = fp.lib()
+    p = _p()
+    assert l.fp_select_blocks(ctypes.byref(p), None, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(ctypes.byref(p), MISALIGNED, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(None, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    # empty sequence: nothing to do, nothing launched
+    assert l.fp_select_blocks(ctypes.byref(p), None, None, None, 0, None, None, None, None, None,
+                              None) == fp.FP_OK
+    # correction without pooled inputs
+    assert l.fp_sparse_prefill_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
+                                   None, None, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
+    # fp8 without scales
+    p8 = _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    assert l.fp_sparse_prefill_fwd(ctypes.byref(p8), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
+    assert "scale" in l.fp_last_error().decode()
+
+
+def _varlen(p, cu, page_size=64, num_pages=100, max_pages=64, ws=1 << 30):
+    l = fp.lib()
+    c = (ctypes.c_int32 * len(cu))(*cu)
+    return l.fp_sparse_prefill_varlen_paged(ctypes.byref(p), FAKE, FAKE, FAKE, page_size, num_pages, FAKE,
+                                            max_pages, c, len(cu) - 1, FAKE, FAKE, ctypes.c_void_p(1 << 24),
+                                            ws, FAKE, None, None)
+
+
+def test_varlen_validation():
+    p = _p()
+    assert _varlen(p, [0, 100, 50]) == fp.FP_INVALID_ARGUMENT           # non-monotone
+    assert _varlen(p, [5, 100]) == fp.FP_INVALID_ARGUMENT               # cu[0] != 0
+    assert _varlen(p, [0, 100], page_size=48) == fp.FP_INVALID_ARGUMENT  # 128 % 48 != 0
+    assert _varlen(p, [0, 4096], max_pages=10) == fp.FP_INVALID_ARGUMENT
+    assert _varlen(p, [0, 100], num_pages=0) == fp.FP_INVALID_ARGUMENT
+    assert _varlen(p, [0, 1000], ws=16) == fp.FP_WORKSPACE_TOO_SMALL
+    assert _varlen(_p(dtype=fp.FP_DTYPE_FP8_E4M3FN), [0, 100]) == fp.FP_UNSUPPORTED
+    assert _varlen(p, [0] * 130) == fp.FP_UNSUPPORTED                  # batch > 128
+    assert _varlen(p, [0, 0, 0]) == fp.FP_OK                            # nothing to do
+    assert fp.lib().fp_last_error() == b""
