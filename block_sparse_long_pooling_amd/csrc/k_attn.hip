@@ -170,31 +170,44 @@ __device__ __forceinline__ void pv_tile(const uint4* lv, const uint32_t (*pk)[8]
     }
 }
 
-// Online-softmax update with logits x (log2 units, -inf = masked) already in s.
-// Packs P to bf16 pairs pk[sub][0..7] (registers 2i, 2i+1 of subtile sub).
+// Online-softmax update.  s holds raw scores q.k (masked entries -inf); the
+// logit in log2 units is s * c + bias.  The running max m only moves when a
+// tile raises it by more than kLazy (log2 units): P then stays below 2^kLazy,
+// which bf16 and the fp32 accumulators hold exactly enough, and most tiles
+// skip rescaling O.  Packs P to bf16 pairs pk[sub][0..7].
+#ifndef FP_LAZY_LOG2
+#define FP_LAZY_LOG2 8.f
+#endif
+constexpr float kLazy = FP_LAZY_LOG2;
+
 template <int NSUB, int NDS>
-__device__ __forceinline__ void softmax_update(f32x16* s, float& m, float& l, f32x16* o, uint32_t (*pk)[8]) {
+__device__ __forceinline__ void softmax_update(f32x16* s, float c, float bias, float& m, float& l, f32x16* o,
+                                               uint32_t (*pk)[8]) {
     float mt = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
+    const float mt2 = (mt == -INFINITY) ? -INFINITY : fmaf(mt, c, bias);
+    const bool grow = mt2 > m + kLazy;
+    if (__ballot(grow)) {
+        const float m_new = grow ? mt2 : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        m = m_new;
+        l *= alpha;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
+        for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[ds][r] *= alpha;
+            for (int r = 0; r < 16; ++r) o[ds][r] *= alpha;
+    }
+    const float off = bias - (m == -INFINITY ? 0.f : m);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(s[sub][2 * i] - m_use);
-            const float p1 = __builtin_amdgcn_exp2f(s[sub][2 * i + 1] - m_use);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[sub][2 * i], c, off));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[sub][2 * i + 1], c, off));
             l += p0 + p1;
             pk[sub][i] = pack_bf16(p0, p1);
         }
@@ -202,7 +215,7 @@ __device__ __forceinline__ void softmax_update(f32x16* s, float& m, float& l, f3
 }
 
 template <int D, int BLK, bool PAGED>
-__global__ __launch_bounds__(2 * BLK) void k_attn_bf16(AttnArgs a, SeqTable t) {
+__global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t) {
     using T = Tile<D, BLK>;
     __shared__ uint4 lk[BLK * T::KCH];
     __shared__ uint4 lv[D * T::VCH];
@@ -253,15 +266,16 @@ __global__ __launch_bounds__(2 * BLK) void k_attn_bf16(AttnArgs a, SeqTable t) {
         load_kv_tile<D, BLK, PAGED>(kb, vb, a.kv, b, tok0, len, J, a.Hkv, hk, lk, lv, tid);
         __syncthreads();
         qk_tile<D, BLK>(lk, qf, col, half, s);
-        const bool diag = (J == I);
+        if (J == I) {
 #pragma unroll
-        for (int sub = 0; sub < T::NSUB; ++sub)
+            for (int sub = 0; sub < T::NSUB; ++sub)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
-                s[sub][r] = (diag && key > qr) ? -INFINITY : s[sub][r] * c;
-            }
-        softmax_update<T::NSUB, T::NDS>(s, m, l, o, pk);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
+                    s[sub][r] = key > qr ? -INFINITY : s[sub][r];
+                }
+        }
+        softmax_update<T::NSUB, T::NDS>(s, c, 0.f, m, l, o, pk);
         pv_tile<D, BLK>(lv, pk, col, half, o);
     }
 
@@ -278,28 +292,30 @@ __global__ __launch_bounds__(2 * BLK) void k_attn_bf16(AttnArgs a, SeqTable t) {
         // Every block J < I of a request is full, so ln n_J = ln BLK (log2 units here).
         const float log2_blk = __log2f((float)BLK);
         for (int c0 = 0; c0 < I; c0 += BLK) {
-            const int c1 = min(I, c0 + BLK);
-            int kept = 0;
-            for (int wd = c0 >> 5; wd < (c1 + 31) >> 5; ++wd) {
-                uint32_t bits = kept_bits[wd];
-                const int lo = max(c0, wd * 32) - wd * 32, hi = min(c1, wd * 32 + 32) - wd * 32;
-                const uint32_t mask = (hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
-                kept += __popc(bits & mask);
+            // Bit j of skip[sub] <=> block c0 + 32 sub + j is strictly past (< I) and not kept.
+            uint32_t skip[T::NSUB];
+            int nskip = 0;
+#pragma unroll
+            for (int sub = 0; sub < T::NSUB; ++sub) {
+                const int j0 = c0 + 32 * sub;
+                const int nvalid = min(32, max(0, I - j0));
+                const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+                skip[sub] = ~kept_bits[j0 >> 5] & valid;
+                nskip += __popc(skip[sub]);
             }
-            if (kept == c1 - c0) continue;                 // nothing skipped in this range
+            if (nskip == 0) continue;                      // every past block here is kept
             __syncthreads();
             load_pooled_tile<D, BLK>(a.pk, a.pv, prow0, c0, I, lk, lv, tid);
             __syncthreads();
             qk_tile<D, BLK>(lk, qf, col, half, s);
 #pragma unroll
-            for (int sub = 0; sub < T::NSUB; ++sub)
+            for (int sub = 0; sub < T::NSUB; ++sub) {
+                const uint32_t bits = skip[sub] >> (4 * half);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int J = c0 + 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
-                    const bool skipped = J < I && !((kept_bits[min(J, I - 1) >> 5] >> (J & 31)) & 1u);
-                    s[sub][r] = skipped ? fmaf(s[sub][r], c, log2_blk) : -INFINITY;
-                }
-            softmax_update<T::NSUB, T::NDS>(s, m, l, o, pk);
+                for (int r = 0; r < 16; ++r)
+                    s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
+            }
+            softmax_update<T::NSUB, T::NDS>(s, c, log2_blk, m, l, o, pk);
             pv_tile<D, BLK>(lv, pk, col, half, o);
         }
     }
