@@ -1,0 +1,126 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times: every block list against the oracle's selection (bit-exact
+outside the threshold band), and outputs of a sample of (head, query block)
+pairs -- always including the first and last query blocks -- against the
+oracle evaluated under the GPU's mask."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_pooling_amd as fp
+import oracle as O
+from block_sparse_long_pooling_amd import synth
+
+from gpu_util import BF16_TOL, LSE_TOL, check_lists, compare_mask, dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _sample_pairs(Hq, nB, n, seed):
+    r = np.random.default_rng(seed)
+    pairs = {(0, 0), (Hq - 1, nB - 1), (Hq // 2, nB - 1), (1 % Hq, nB // 2)}
+    while len(pairs) < n:
+        pairs.add((int(r.integers(Hq)), int(r.integers(nB))))
+    return sorted(pairs)
+
+
+class _Seq:
+    def __init__(self, name):
+        w = synth.WORKLOADS[name]
+        self.w = w
+        self.S, self.Hq, self.Hkv, self.d, self.B = (w.seqlens[0], w.num_q_heads, w.num_kv_heads,
+                                                     w.head_dim, w.block_size)
+        print(f"generating {name}", flush=True)
+        q, k, v = synth.make_sequence(self.S, self.Hq, self.Hkv, self.d, w.seed, w.verticals)
+        self.cpu = (q, k, v)
+        self.gpu = tuple(t.to(dev()) for t in (q, k, v))
+        self.np = tuple(t.float().numpy() for t in (q, k, v))
+
+
+@pytest.fixture(scope="module")
+def s32k():
+    return _Seq("llama8b_s32k")
+
+
+@pytest.fixture(scope="module")
+def s128k():
+    return _Seq("llama8b_s128k")
+
+
+def _check_full(seq, alpha, n_pairs, seed):
+    S, Hq, Hkv, d, B = seq.S, seq.Hq, seq.Hkv, seq.d, seq.B
+    nB = (S + B - 1) // B
+    p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True)
+    qd, kd, vd = seq.gpu
+    sel = fp.fp_select_blocks(p, qd, kd, vd)
+    out, lse = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, return_lse=True)
+    torch.cuda.synchronize()
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    qn, kn, vn = seq.np
+    ref = O.select_blocks(qn, kn, vn, B, alpha)
+    outside, inside, band = compare_mask(mask, ref)
+    density = mask.sum() / (Hq * nB * (nB + 1) / 2)
+    print(f"  alpha={alpha}: density {density:.4f}, band {band}, mismatches in band {inside}, "
+          f"outside {outside}", flush=True)
+    assert outside == 0
+    # pooled means against the oracle's
+    np.testing.assert_allclose(sel.pooled_k.cpu().numpy(), ref.k_bar, rtol=0, atol=1e-5)
+    pairs = _sample_pairs(Hq, nB, n_pairs, seed)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, ref, True, pairs=pairs, keep=mask)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    worst, lworst = 0.0, 0.0
+    for h, I in pairs:
+        r0, r1 = I * B, min(S, (I + 1) * B)
+        worst = max(worst, float(np.abs(o[r0:r1, h] - o_ref[r0:r1, h]).max()))
+        lworst = max(lworst, float(np.abs(l[h, r0:r1] - lse_ref[h, r0:r1]).max()))
+    print(f"  {len(pairs)} sampled pairs: max|o-ref| {worst:.3e}, max|lse-ref| {lworst:.3e}", flush=True)
+    assert worst <= BF16_TOL and lworst <= LSE_TOL
+    assert np.isfinite(o).all()
+
+
+def test_32k_full_size(s32k):
+    _check_full(s32k, 0.1, 96, seed=2)
+
+
+@pytest.mark.parametrize("alpha", [0.05, 0.1, 0.2])
+def test_128k_full_size(s128k, alpha):
+    _check_full(s128k, alpha, 48, seed=int(alpha * 100))
+
+
+def test_paged_batch8_full_size():
+    w = synth.WORKLOADS["paged_batch8"]
+    Hq, Hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print("generating paged_batch8", flush=True)
+    pb = synth.workload_inputs(w)
+    p = fp.make_params(Hq, Hkv, d, B, w.alphas[0], mean_correction=True)
+    res = fp.fp_sparse_prefill_varlen_paged(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
+                                            pb.block_table.to(dev()), pb.cu_seqlens, return_lse=True)
+    torch.cuda.synchronize()
+    out = res.out.float().cpu().numpy()
+    lse = res.lse.cpu().numpy()
+    assert np.isfinite(out).all()
+    idx_off, cnt_off = 0, 0
+    kept_total, causal_total = 0, 0
+    for b, L in enumerate(pb.seqlens):
+        nb = (L + B - 1) // B
+        mask = check_lists(res.kv_idx, res.kv_cnt, Hq, nb, offset=idx_off, cnt_offset=cnt_off)
+        qb, kb, vb = (t.float().numpy() for t in pb.requests[b])
+        ref = O.select_blocks(qb, kb, vb, B, w.alphas[0])
+        outside, inside, band = compare_mask(mask, ref)
+        assert outside == 0, (b, outside)
+        pairs = _sample_pairs(Hq, nb, 8, seed=b)
+        o_ref, lse_ref = O.sparse_attention(qb, kb, vb, ref, True, pairs=pairs, keep=mask)
+        t0 = int(pb.cu_seqlens[b])
+        for h, I in pairs:
+            r0, r1 = I * B, min(L, (I + 1) * B)
+            err = np.abs(out[t0 + r0:t0 + r1, h] - o_ref[r0:r1, h]).max()
+            lerr = np.abs(lse[h, t0 + r0:t0 + r1] - lse_ref[h, r0:r1]).max()
+            assert err <= BF16_TOL and lerr <= LSE_TOL, (b, h, I, err, lerr)
+        kept_total += int(mask.sum())
+        causal_total += Hq * nb * (nb + 1) // 2
+        print(f"  request {b} L={L}: density {mask.sum() / (Hq * nb * (nb + 1) / 2):.4f}, band {band}, "
+              f"in-band mismatches {inside}", flush=True)
+        idx_off += Hq * nb * (nb + 1) // 2
+        cnt_off += Hq * nb
+    print(f"  overall density {kept_total / causal_total:.4f}", flush=True)
