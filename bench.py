@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--quick", action="store_true",
                     help="headline alpha only: no sweep, no dense references, no CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -125,6 +127,12 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     stream = torch.cuda.current_stream(dev)
     out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def measure(alpha, steps, warmup):
         p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr)

@@ -1,43 +1,190 @@
 // Sparse flash attention over the kept KV blocks, with the mean-correction
-// term (FlashPrefill, gist.science technical summary, section 2.C: the kernel
-// walks per-query-block index lists, so skipped blocks cost no work; FlashPrefill
-// V2 abstract: mean correction, PackGQA-style memory access, FP8, paged KV).
+// term, bf16 (FlashPrefill, gist.science technical summary, section 2.C: the
+// kernel walks per-query-block index lists, so skipped blocks cost no work;
+// FlashPrefill V2 abstract: mean correction, PackGQA-style memory access,
+// paged KV).
 //
-// A workgroup owns one (query head h, query block I) of one request; each of
-// its BLK/32 waves owns 32 query rows.  Per kept block J the K tile and the V
-// tile go to LDS, then every wave computes
-//     S^T = K Q^T        (v_mfma_f32_32x32x16_bf16; lane = query, 16 keys per
-//                         32-key subtile in registers)
-//     online softmax     (exp2 domain, row statistics are per-lane scalars
-//                         combined with the partner lane l ^ 32)
-//     O^T += V^T P^T     (P straight from registers; V^T from LDS)
-// Transposed products keep the query index on the MFMA column (= lane), so
-// neither P nor the softmax statistics ever cross lanes through LDS.  V^T is
-// written to LDS through registers (8x8 transposes), with keys permuted inside
-// each 16-key group so that the 32x32 output layout of S^T is directly the
-// B operand layout of the PV product.
+// Work item: (query block I, HP query heads that share one KV head).  Each
+// head's BLK query rows belong to BLK/32 waves, so a workgroup is HP*BLK/32
+// waves.  The workgroup walks the union of the HP heads' ascending lists; a
+// K/V tile is fetched once and serves every head whose list holds it (the
+// others' waves skip it).  Per tile, each active wave computes
+//     S^T = K Q^T        v_mfma_f32_32x32x16_bf16, lane = query, 16 keys per
+//                        32-key subtile in registers
+//     online softmax     exp2 domain; row statistics are per-lane scalars
+//                        combined with the partner lane l ^ 32
+//     O^T += V^T P^T     P straight from registers; V^T operand read from the
+//                        row-major V tile with ds_read_b64_tr_b16
+// K and V tiles are row-major [BLK][D] bf16 in LDS, 16-byte chunks XOR-
+// swizzled per row.  They are fetched by global_load_lds_dwordx4 (DMA into
+// LDS, no registers) into two buffers: the next tile is issued right after
+// the one barrier per tile and lands while the current tile is computed.
+// Rows past a request's end (and out-of-range pages) read a zero chunk.
 //
-// Mean correction: after the kept blocks, the pooled K_bar / V_bar of the
-// skipped blocks J < I go through the same pipeline as one more "tile" per
-// BLK pooled blocks, with logit sigma*q.k_bar_J + ln n_J and every kept or
-// non-past block masked out.  Query heads of one KV head are placed on one
-// XCD so their K/V tiles meet in that XCD's L2.
+// Mean correction: after the kept tiles, the pooled K_bar / V_bar rows of
+// blocks c0 .. c0+BLK-1 (fp32 -> bf16) form one more tile per BLK blocks,
+// with logit sigma*q.k_bar_J + ln n_J, masked per head to its skipped J < I.
+// Query heads of one KV head are placed on one XCD so their tiles meet in
+// that XCD's L2.
 #include "fp_attn.h"
 
 namespace {
 using namespace fp_attn;
 
-template <int D, int BLK, bool PAGED>
-__global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t) {
-    using T = Tile<D, BLK>;
-    __shared__ uint4 lk[BLK * T::KCH];
-    __shared__ uint4 lv[D * T::VCH];
-    __shared__ uint32_t kept_bits[FP_MAX_BLOCKS / 32];
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+
+// XOR swizzle of 16-byte chunks within a row: conflict-free for the MFMA K
+// reads (16 consecutive rows, one chunk) and for the transposing V reads
+// (4 consecutive rows, 2 adjacent chunks).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    return (row >> 1) & 7;
+}
+
+template <int D, int BLK, int HP>
+struct Geo {
+    static constexpr int WPH = BLK / 32;          // waves per head
+    static constexpr int NW = WPH * HP;           // waves per workgroup
+    static constexpr int NT = 64 * NW;            // threads
+    static constexpr int NCH = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE = BLK * D * 2;      // bytes per K or V tile
+    static constexpr int NSUB = BLK / 32;
+    static constexpr int NDS = D / 32;
+};
+
+// DMA one [BLK][D] bf16 tile (rows J*BLK .. of request b) into LDS.
+template <int D, int BLK, int HP, bool PAGED>
+__device__ __forceinline__ void issue_tile(const uint16_t* base, const KVLayout& L, int b, int tok0, int len, int J,
+                                           int64_t rs, int hk, char* lds, int tid, int w) {
+    using G = Geo<D, BLK, HP>;
+    static_assert((BLK * G::NCH) % G::NT == 0, "tile chunks must split evenly");
+#pragma unroll
+    for (int i = 0; i < BLK * G::NCH / G::NT; ++i) {
+        const int p = i * G::NT + tid;             // chunk position in LDS
+        const int row = p / G::NCH;
+        const int c = (p % G::NCH) ^ swz<D>(row);  // logical chunk stored there
+        const int tr = J * BLK + row;
+        const void* src = &kZeroChunk;
+        if (tr < len) {
+            const int64_t r = kv_row<PAGED>(L, b, tok0, tr);
+            if (r >= 0) src = base + r * rs + (int64_t)hk * D + c * 8;
+        }
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT + 64 * w) * 16), 16, 0, 0);
+    }
+}
+
+// Pooled rows c0 .. c0+BLK-1 (zero for blocks >= I) as bf16 into a tile buffer.
+template <int D, int BLK, int HP>
+__device__ __forceinline__ void store_pooled_tile(const float* src, int64_t prow0, int c0, int I, uint4* tile,
+                                                  int tid) {
+    using G = Geo<D, BLK, HP>;
+    for (int i = tid; i < BLK * G::NCH; i += G::NT) {
+        const int row = i / G::NCH, c = i % G::NCH;
+        const int J = c0 + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (J < I) {
+            const float4* s = reinterpret_cast<const float4*>(src + (prow0 + J) * D + c * 8);
+            v = f32x8_to_bf16(s[0], s[1]);
+        }
+        tile[row * G::NCH + (c ^ swz<D>(row))] = v;
+    }
+}
+
+// S^T[sub] = K[32 sub + .., :] Q^T for this wave's 32 queries.
+template <int D, int BLK, int HP>
+__device__ __forceinline__ void qk(const uint4* kt, const bf16x8* qf, int col, int half, f32x16* s) {
+    using G = Geo<D, BLK, HP>;
+#pragma unroll
+    for (int sub = 0; sub < G::NSUB; ++sub) {
+        f32x16 acc = {};
+        const int row = 32 * sub + col;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const uint4 av = kt[row * G::NCH + ((half + 2 * kk) ^ swz<D>(row))];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), qf[kk], acc, 0, 0, 0);
+        }
+        s[sub] = acc;
+    }
+}
+
+// O^T[ds] += V^T[32 ds + .., :] P^T.  A operand of key step st for lane
+// (group gi = lane/16, gl = lane%16): d = 32 ds + 16 (gi&1) + gl, keys
+// 32 (st/2) + 16 (st&1) + 4 (gi/2) + 8 r + t (r = 0, 1; t = 0..3) -- the same
+// key order as the P registers.  Each ds_read_b64_tr_b16 reads, per source
+// lane, 4 columns of one key row; the hardware transpose hands each lane its
+// column for 4 consecutive keys.
+template <int D, int BLK, int HP>
+__device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int lane, f32x16* o) {
+    using G = Geo<D, BLK, HP>;
+    const int gl = lane & 15, gi = lane >> 4;
+    const int hf = gi >> 1;
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds) {
+        const int col_e = 32 * ds + 16 * (gi & 1) + 4 * (gl & 3);
+        const int chunk = col_e >> 3, within = (col_e & 7) * 2;
+#pragma unroll
+        for (int st = 0; st < BLK / 16; ++st) {
+            s16x4 part[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int key = 32 * (st >> 1) + 16 * (st & 1) + 4 * hf + 8 * r + (gl >> 2);
+                const char* addr = vt + key * (D * 2) + ((chunk ^ swz<D>(key)) << 4) + within;
+                part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+            }
+            const uint32_t* p = &pk[st >> 1][4 * (st & 1)];
+            const uint4 bp = make_uint4(p[0], p[1], p[2], p[3]);
+            const s16x8 av = {part[0][0], part[0][1], part[0][2], part[0][3],
+                              part[1][0], part[1][1], part[1][2], part[1][3]};
+            o[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                            __builtin_bit_cast(bf16x8, bp), o[ds], 0, 0, 0);
+        }
+    }
+}
+
+// Ascending-merge cursor over the lists of the HP heads of a workgroup.
+template <int HP>
+struct Union {
+    const int32_t* list[HP];
+    int cnt[HP];
+    int pos[HP];
+    __device__ __forceinline__ int head(int h) const { return pos[h] < cnt[h] ? list[h][pos[h]] : INT_MAX; }
+    // Next block of the union and the heads that keep it (bit mask); INT_MAX when done.
+    __device__ __forceinline__ int next(int& act) {
+        int J = INT_MAX;
+#pragma unroll
+        for (int h = 0; h < HP; ++h) J = min(J, head(h));
+        act = 0;
+#pragma unroll
+        for (int h = 0; h < HP; ++h)
+            if (J != INT_MAX && head(h) == J) { act |= 1 << h; ++pos[h]; }
+        return J;
+    }
+};
+
+template <int D, int BLK, int HP, bool PAGED>
+__global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, SeqTable t) {
+    using G = Geo<D, BLK, HP>;
+    // Four separate LDS objects: the compiler then sees that a DMA into one
+    // buffer does not touch the buffer being read, and does not wait on it.
+    __shared__ __attribute__((aligned(16))) char kb0[G::TILE];
+    __shared__ __attribute__((aligned(16))) char kb1[G::TILE];
+    __shared__ __attribute__((aligned(16))) char vb0[G::TILE];
+    __shared__ __attribute__((aligned(16))) char vb1[G::TILE];
+    __shared__ uint32_t kept_bits[HP][FP_MAX_BLOCKS / 32];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-    const int rank = blockIdx.x / a.Hq;
-    const int h = xcd_head(blockIdx.x % a.Hq, a.Hq);
+    const int hs = w / G::WPH;                   // which of the HP heads this wave serves
+    const int rw = w % G::WPH;                   // 32-row group inside the query block
+    const int npairs = a.Hq / HP;
+    const int rank = blockIdx.x / npairs;
+    const int h = HP * xcd_head(blockIdx.x % npairs, npairs) + hs;
     int b, local;
     item_of(t, rank, b, local);
     const int nb = seq_blocks(t, b);
@@ -47,17 +194,24 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     const int q0 = tok0 + I * BLK;
     const int nI = min(BLK, len - I * BLK);
     const int hk = h / a.g;
-    const int32_t* list = a.kv_idx + t.idx_off[b] + (int64_t)h * ((int64_t)nb * (nb + 1) / 2) +
-                          (int64_t)I * (I + 1) / 2;
-    const int cnt = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)h * nb + I];
-    const int qr = 32 * w + col;
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+    const int64_t rs = (int64_t)a.Hkv * D;
+    const int64_t tri = (int64_t)nb * (nb + 1) / 2;
+    const int h0 = h - hs;
+
+    Union<HP> u;
+#pragma unroll
+    for (int j = 0; j < HP; ++j) {
+        u.list[j] = a.kv_idx + t.idx_off[b] + (int64_t)(h0 + j) * tri + (int64_t)I * (I + 1) / 2;
+        u.cnt[j] = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)(h0 + j) * nb + I];
+        u.pos[j] = 0;
+    }
+    const int qr = 32 * rw + col;
     const uint16_t* kb = static_cast<const uint16_t*>(a.k);
     const uint16_t* vb = static_cast<const uint16_t*>(a.v);
 
     bf16x8 qf[D / 16];
     {
-        const uint16_t* qp = qb + ((int64_t)(q0 + qr) * a.Hq + h) * D + 8 * half;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + qr) * a.Hq + h) * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             uint4 x = make_uint4(0, 0, 0, 0);
@@ -67,53 +221,146 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     }
     const float c = a.scale_log2;
     float m = -INFINITY, l = 0.f;
-    f32x16 o[T::NDS];
+    f32x16 o[G::NDS];
 #pragma unroll
-    for (int ds = 0; ds < T::NDS; ++ds) o[ds] = f32x16{};
-    f32x16 s[T::NSUB];
-    uint32_t pk[T::NSUB][8];
+    for (int ds = 0; ds < G::NDS; ++ds) o[ds] = f32x16{};
+    f32x16 s[G::NSUB];
+    uint32_t pk[G::NSUB][8];
 
-    for (int it = 0; it < cnt; ++it) {
-        const int J = list[it];
-        __syncthreads();
-        load_kv_tile<D, BLK, PAGED>(kb, vb, a.kv, b, tok0, len, J, a.Hkv, hk, lk, lv, tid);
-        __syncthreads();
-        qk_tile<D, BLK>(lk, qf, col, half, s);
-        if (J == I) {
-#pragma unroll
-            for (int sub = 0; sub < T::NSUB; ++sub)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
-                    s[sub][r] = key > qr ? -INFINITY : s[sub][r];
-                }
+    int act, act_next;
+    int J = u.next(act);
+    if (J != INT_MAX) {
+        issue_tile<D, BLK, HP, PAGED>(kb, a.kv, b, tok0, len, J, rs, hk, kb0, tid, w);
+        issue_tile<D, BLK, HP, PAGED>(vb, a.kv, b, tok0, len, J, rs, hk, vb0, tid, w);
+    }
+    // One kept tile: wait for its DMA, release the other buffers by the
+    // barrier, prefetch the next tile into them, compute on this one.
+    auto step = [&](char* kcur, char* vcur, char* knext, char* vnext) {
+        const int Jn = u.next(act_next);
+        __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA for tile J is done
+        __syncthreads();                                 // ... every thread's; the other buffers are free
+        if (Jn != INT_MAX) {
+            issue_tile<D, BLK, HP, PAGED>(kb, a.kv, b, tok0, len, Jn, rs, hk, knext, tid, w);
+            issue_tile<D, BLK, HP, PAGED>(vb, a.kv, b, tok0, len, Jn, rs, hk, vnext, tid, w);
         }
-        softmax_update<T::NSUB, T::NDS>(s, c, 0.f, m, l, o, pk);
-        pv_tile<D, BLK>(lv, pk, col, half, o);
+        if ((act >> hs) & 1) {
+            qk<D, BLK, HP>(reinterpret_cast<const uint4*>(kcur), qf, col, half, s);
+            if (J == I) {
+#pragma unroll
+                for (int sub = 0; sub < G::NSUB; ++sub)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
+                        s[sub][r] = key > qr ? -INFINITY : s[sub][r];
+                    }
+            }
+            softmax_update<G::NSUB, G::NDS>(s, c, 0.f, m, l, o, pk);
+            pv<D, BLK, HP>(vcur, pk, lane, o);
+        }
+        J = Jn;
+        act = act_next;
+    };
+    while (J != INT_MAX) {
+        step(kb0, vb0, kb1, vb1);
+        if (J == INT_MAX) break;
+        step(kb1, vb1, kb0, vb0);
     }
 
-    if (a.correction && I > 0)
-        correction_pass<D, BLK>(a, t, b, I, hk, cnt, list, qf, lk, lv, kept_bits, tid, col, half, c, m, l, o);
-    store_output<D, BLK>(a, t, h, q0, nI, qr, half, m, l, o, lk, tid);
+    if (a.correction && I > 0) {
+        const int nwords = (I + 31) >> 5;
+        __syncthreads();                                 // last tile's reads are done
+        for (int i = tid; i < HP * nwords; i += G::NT) kept_bits[i / nwords][i % nwords] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < HP; ++j)
+            for (int i = tid; i < u.cnt[j]; i += G::NT) {
+                const int Jk = u.list[j][i];
+                if (Jk < I) atomicOr(&kept_bits[j][Jk >> 5], 1u << (Jk & 31));
+            }
+        __syncthreads();
+        const int64_t prow0 = (int64_t)hk * t.total_blocks + t.blk_off[b];
+        const float log2_blk = __log2f((float)BLK);      // past blocks are full: ln n_J = ln BLK
+        for (int c0 = 0; c0 < I; c0 += BLK) {
+            // Bit j of skip[sub] <=> block c0 + 32 sub + j is strictly past and not kept by this head.
+            uint32_t skip[G::NSUB];
+            int nskip = 0, nany = 0;
+#pragma unroll
+            for (int sub = 0; sub < G::NSUB; ++sub) {
+                const int j0 = c0 + 32 * sub;
+                const int nvalid = min(32, max(0, I - j0));
+                const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+                skip[sub] = ~kept_bits[hs][j0 >> 5] & valid;
+                nskip += __popc(skip[sub]);
+#pragma unroll
+                for (int j = 0; j < HP; ++j) nany += __popc(~kept_bits[j][j0 >> 5] & valid);
+            }
+            if (nany == 0) continue;                     // every head keeps every past block here
+            __syncthreads();
+            store_pooled_tile<D, BLK, HP>(a.pk, prow0, c0, I, reinterpret_cast<uint4*>(kb0), tid);
+            store_pooled_tile<D, BLK, HP>(a.pv, prow0, c0, I, reinterpret_cast<uint4*>(vb0), tid);
+            __syncthreads();
+            if (nskip == 0) continue;
+            qk<D, BLK, HP>(reinterpret_cast<const uint4*>(kb0), qf, col, half, s);
+#pragma unroll
+            for (int sub = 0; sub < G::NSUB; ++sub) {
+                const uint32_t bits = skip[sub] >> (4 * half);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
+            }
+            softmax_update<G::NSUB, G::NDS>(s, c, log2_blk, m, l, o, pk);
+            pv<D, BLK, HP>(vb0, pk, lane, o);
+        }
+    }
+
+    // Epilogue: normalise, stage each head's bf16 tile in LDS, store full rows.
+    const float l_tot = l + __shfl_xor(l, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __syncthreads();
+    uint4* stage = reinterpret_cast<uint4*>(hs == 0 ? kb0 : kb1);
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int chunk = 4 * ds + g4;               // d0 = 32 ds + 8 g4 + 4 half
+            const uint2 v2 = make_uint2(pack_bf16(o[ds][4 * g4] * inv, o[ds][4 * g4 + 1] * inv),
+                                        pack_bf16(o[ds][4 * g4 + 2] * inv, o[ds][4 * g4 + 3] * inv));
+            reinterpret_cast<uint2*>(&stage[qr * G::NCH + (chunk ^ swz<D>(qr))])[half] = v2;
+        }
+    __syncthreads();
+    const int ht = tid % (64 * G::WPH);                  // thread index within this head's waves
+    for (int i = ht; i < nI * G::NCH; i += 64 * G::WPH) {
+        const int row = i / G::NCH, ch = i % G::NCH;
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)(q0 + row) * a.Hq + h) * D + ch * 8) =
+            stage[row * G::NCH + (ch ^ swz<D>(row))];
+    }
+    if (a.lse && half == 0 && qr < nI)
+        a.lse[(int64_t)h * t.total_tokens + q0 + qr] = (m + __log2f(l_tot)) * kLn2;
+}
+
+template <int D, int BLK, int HP>
+hipError_t launch_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+    dim3 grid((unsigned)t.total_items * (a.Hq / HP));
+    dim3 block(64 * HP * (BLK / 32));
+    if (paged)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, true>), grid, block, 0, s, a, t);
+    else
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, false>), grid, block, 0, s, a, t);
+    return hipGetLastError();
 }
 
 template <int D, int BLK>
-hipError_t launch_attn_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
-    dim3 grid((unsigned)t.total_items * a.Hq);
-    if (paged)
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, true>), grid, dim3(2 * BLK), 0, s, a, t);
-    else
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, false>), grid, dim3(2 * BLK), 0, s, a, t);
-    return hipGetLastError();
+hipError_t launch_db(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+    return (a.g % 2 == 0) ? launch_t<D, BLK, 2>(a, t, paged, s) : launch_t<D, BLK, 1>(a, t, paged, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s) {
     if (t.total_items == 0) return hipSuccess;
-    if (D == 128 && B == 128) return launch_attn_t<128, 128>(a, t, paged, s);
-    if (D == 128 && B == 64) return launch_attn_t<128, 64>(a, t, paged, s);
-    if (D == 64 && B == 128) return launch_attn_t<64, 128>(a, t, paged, s);
-    if (D == 64 && B == 64) return launch_attn_t<64, 64>(a, t, paged, s);
+    if (D == 128 && B == 128) return launch_db<128, 128>(a, t, paged, s);
+    if (D == 128 && B == 64) return launch_db<128, 64>(a, t, paged, s);
+    if (D == 64 && B == 128) return launch_db<64, 128>(a, t, paged, s);
+    if (D == 64 && B == 64) return launch_db<64, 64>(a, t, paged, s);
     return hipErrorInvalidValue;
 }
