@@ -26,6 +26,8 @@
 // with logit sigma*q.k_bar_J + ln n_J, masked per head to its skipped J < I.
 // Query heads of one KV head are placed on one XCD so their tiles meet in
 // that XCD's L2.
+#include <type_traits>
+
 #include "fp_attn.h"
 
 namespace {
@@ -58,24 +60,49 @@ struct Geo {
     static constexpr int NDS = D / 32;
 };
 
-// DMA one [BLK][D] bf16 tile (rows J*BLK .. of request b) into LDS.
+// Per-thread DMA plan for a [BLK][D] bf16 tile: load i of this thread fills
+// LDS chunk i*NT + tid, i.e. row row[i], logical chunk (chunk position XOR
+// swizzle).  off[i] is that chunk's element offset inside the tile's rows for
+// contiguous K/V (row * row_stride + kv head * D + chunk * 8).
+template <int D, int BLK, int HP>
+struct DmaPlan {
+    static constexpr int NLOAD = BLK * (D / 8) / (64 * HP * (BLK / 32));
+    int row[NLOAD];
+    int coff[NLOAD];   // element offset inside one token row: hk * D + chunk * 8
+    __device__ __forceinline__ void init(int tid, int hk) {
+        constexpr int NT = 64 * HP * (BLK / 32);
+        constexpr int NCH = D / 8;
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int p = i * NT + tid;
+            row[i] = p / NCH;
+            coff[i] = hk * D + ((p % NCH) ^ swz<D>(row[i])) * 8;
+        }
+    }
+};
+
+// DMA one tile: rows J*BLK .. of the request whose first row is `first`
+// (contiguous) or whose pages are listed in `pages` (paged).
 template <int D, int BLK, int HP, bool PAGED>
-__device__ __forceinline__ void issue_tile(const uint16_t* base, const KVLayout& L, int b, int tok0, int len, int J,
-                                           int64_t rs, int hk, char* lds, int tid, int w) {
+__device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t* pages, const KVLayout& L,
+                                           int64_t rs, int J, int nvalid, const DmaPlan<D, BLK, HP>& plan,
+                                           const uint4* zero, char* lds, int wave_base) {
     using G = Geo<D, BLK, HP>;
     static_assert((BLK * G::NCH) % G::NT == 0, "tile chunks must split evenly");
 #pragma unroll
-    for (int i = 0; i < BLK * G::NCH / G::NT; ++i) {
-        const int p = i * G::NT + tid;             // chunk position in LDS
-        const int row = p / G::NCH;
-        const int c = (p % G::NCH) ^ swz<D>(row);  // logical chunk stored there
-        const int tr = J * BLK + row;
-        const void* src = &kZeroChunk;
-        if (tr < len) {
-            const int64_t r = kv_row<PAGED>(L, b, tok0, tr);
-            if (r >= 0) src = base + r * rs + (int64_t)hk * D + c * 8;
+    for (int i = 0; i < DmaPlan<D, BLK, HP>::NLOAD; ++i) {
+        const int row = plan.row[i];
+        const void* src;
+        if (!PAGED) {
+            const uint16_t* p = first + ((int64_t)J * BLK + row) * rs + plan.coff[i];
+            src = row < nvalid ? (const void*)p : (const void*)zero;
+        } else {
+            const int tr = J * BLK + row;
+            const int page = pages[tr / L.page_size];
+            const uint16_t* p = first + ((int64_t)page * L.page_size + tr % L.page_size) * rs + plan.coff[i];
+            src = (row < nvalid && (unsigned)page < (unsigned)L.num_pages) ? (const void*)p : (const void*)zero;
         }
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT + 64 * w) * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT) * 16 + wave_base), 16, 0, 0);
     }
 }
 
@@ -96,30 +123,33 @@ __device__ __forceinline__ void store_pooled_tile(const float* src, int64_t prow
     }
 }
 
-// S^T[sub] = K[32 sub + .., :] Q^T for this wave's 32 queries.
-template <int D, int BLK, int HP>
+// S^T for subtiles SUB0 .. SUB0+NS-1 (keys 32 SUB0 ..) of this wave's 32
+// queries; each subtile's 8 K operands are read before its MFMA chain.
+template <int D, int BLK, int HP, int SUB0, int NS>
 __device__ __forceinline__ void qk(const uint4* kt, const bf16x8* qf, int col, int half, f32x16* s) {
     using G = Geo<D, BLK, HP>;
 #pragma unroll
-    for (int sub = 0; sub < G::NSUB; ++sub) {
-        f32x16 acc = {};
-        const int row = 32 * sub + col;
+    for (int j = 0; j < NS; ++j) {
+        const int row = 32 * (SUB0 + j) + col;
+        uint4 av[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const uint4 av = kt[row * G::NCH + ((half + 2 * kk) ^ swz<D>(row))];
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), qf[kk], acc, 0, 0, 0);
-        }
-        s[sub] = acc;
+        for (int kk = 0; kk < D / 16; ++kk) av[kk] = kt[row * G::NCH + ((half + 2 * kk) ^ swz<D>(row))];
+        __builtin_amdgcn_sched_barrier(0);               // keep the reads ahead of the MFMA chain
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[kk]), qf[kk], acc, 0, 0, 0);
+        s[j] = acc;
     }
 }
 
-// O^T[ds] += V^T[32 ds + .., :] P^T.  A operand of key step st for lane
-// (group gi = lane/16, gl = lane%16): d = 32 ds + 16 (gi&1) + gl, keys
-// 32 (st/2) + 16 (st&1) + 4 (gi/2) + 8 r + t (r = 0, 1; t = 0..3) -- the same
-// key order as the P registers.  Each ds_read_b64_tr_b16 reads, per source
-// lane, 4 columns of one key row; the hardware transpose hands each lane its
-// column for 4 consecutive keys.
-template <int D, int BLK, int HP>
+// O^T[ds] += V^T[32 ds + .., keys of subtiles SUB0 .. SUB0+NS-1] P^T.  A
+// operand of key step st for lane (group gi = lane/16, gl = lane%16):
+// d = 32 ds + 16 (gi&1) + gl, keys 32 (st/2) + 16 (st&1) + 4 (gi/2) + 8 r + t
+// (r = 0, 1; t = 0..3) -- the same key order as the P registers.  Each
+// ds_read_b64_tr_b16 reads, per source lane, 4 columns of one key row; the
+// hardware transpose hands each lane its column for 4 consecutive keys.
+template <int D, int BLK, int HP, int SUB0, int NS>
 __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int lane, f32x16* o) {
     using G = Geo<D, BLK, HP>;
     const int gl = lane & 15, gi = lane >> 4;
@@ -128,19 +158,22 @@ __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int 
     for (int ds = 0; ds < G::NDS; ++ds) {
         const int col_e = 32 * ds + 16 * (gi & 1) + 4 * (gl & 3);
         const int chunk = col_e >> 3, within = (col_e & 7) * 2;
+        s16x4 part[2 * NS][2];
 #pragma unroll
-        for (int st = 0; st < BLK / 16; ++st) {
-            s16x4 part[2];
+        for (int st = 0; st < 2 * NS; ++st)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int key = 32 * (st >> 1) + 16 * (st & 1) + 4 * hf + 8 * r + (gl >> 2);
+                const int key = 32 * (SUB0 + (st >> 1)) + 16 * (st & 1) + 4 * hf + 8 * r + (gl >> 2);
                 const char* addr = vt + key * (D * 2) + ((chunk ^ swz<D>(key)) << 4) + within;
-                part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+                part[st][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
             }
+        __builtin_amdgcn_sched_barrier(0);               // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int st = 0; st < 2 * NS; ++st) {
             const uint32_t* p = &pk[st >> 1][4 * (st & 1)];
             const uint4 bp = make_uint4(p[0], p[1], p[2], p[3]);
-            const s16x8 av = {part[0][0], part[0][1], part[0][2], part[0][3],
-                              part[1][0], part[1][1], part[1][2], part[1][3]};
+            const s16x8 av = {part[st][0][0], part[st][0][1], part[st][0][2], part[st][0][3],
+                              part[st][1][0], part[st][1][1], part[st][1][2], part[st][1][3]};
             o[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                             __builtin_bit_cast(bf16x8, bp), o[ds], 0, 0, 0);
         }
@@ -206,8 +239,15 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         u.pos[j] = 0;
     }
     const int qr = 32 * rw + col;
-    const uint16_t* kb = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vb = static_cast<const uint16_t*>(a.v);
+    // Tile DMA: contiguous K/V start at this request's first row; paged K/V
+    // start at the pool and go through the request's block-table row.
+    const uint16_t* kfirst = static_cast<const uint16_t*>(a.k) + (PAGED ? 0 : (int64_t)tok0 * rs);
+    const uint16_t* vfirst = static_cast<const uint16_t*>(a.v) + (PAGED ? 0 : (int64_t)tok0 * rs);
+    const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
+    DmaPlan<D, BLK, HP> plan;
+    plan.init(tid, hk);
+    const uint4* zero = &kZeroChunk;
+    const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
 
     bf16x8 qf[D / 16];
     {
@@ -224,14 +264,15 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
     f32x16 o[G::NDS];
 #pragma unroll
     for (int ds = 0; ds < G::NDS; ++ds) o[ds] = f32x16{};
-    f32x16 s[G::NSUB];
-    uint32_t pk[G::NSUB][8];
+    constexpr int SH = G::NSUB > 1 ? G::NSUB / 2 : 1;   // subtiles per half tile
+    f32x16 s[SH];
+    uint32_t pk[SH][8];
 
     int act, act_next;
     int J = u.next(act);
     if (J != INT_MAX) {
-        issue_tile<D, BLK, HP, PAGED>(kb, a.kv, b, tok0, len, J, rs, hk, kb0, tid, w);
-        issue_tile<D, BLK, HP, PAGED>(vb, a.kv, b, tok0, len, J, rs, hk, vb0, tid, w);
+        issue_tile<D, BLK, HP, PAGED>(kfirst, pages, a.kv, rs, J, len - J * BLK, plan, zero, kb0, wave_base);
+        issue_tile<D, BLK, HP, PAGED>(vfirst, pages, a.kv, rs, J, len - J * BLK, plan, zero, vb0, wave_base);
     }
     // One kept tile: wait for its DMA, release the other buffers by the
     // barrier, prefetch the next tile into them, compute on this one.
@@ -240,22 +281,31 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA for tile J is done
         __syncthreads();                                 // ... every thread's; the other buffers are free
         if (Jn != INT_MAX) {
-            issue_tile<D, BLK, HP, PAGED>(kb, a.kv, b, tok0, len, Jn, rs, hk, knext, tid, w);
-            issue_tile<D, BLK, HP, PAGED>(vb, a.kv, b, tok0, len, Jn, rs, hk, vnext, tid, w);
+            issue_tile<D, BLK, HP, PAGED>(kfirst, pages, a.kv, rs, Jn, len - Jn * BLK, plan, zero, knext,
+                                          wave_base);
+            issue_tile<D, BLK, HP, PAGED>(vfirst, pages, a.kv, rs, Jn, len - Jn * BLK, plan, zero, vnext,
+                                          wave_base);
         }
         if ((act >> hs) & 1) {
-            qk<D, BLK, HP>(reinterpret_cast<const uint4*>(kcur), qf, col, half, s);
-            if (J == I) {
+            // Two halves of SH subtiles each: online softmax per half keeps S and
+            // P at half size, which leaves registers to read operands ahead.
+            auto half_tile = [&](auto sub0) {
+                constexpr int S0 = decltype(sub0)::value;
+                qk<D, BLK, HP, S0, SH>(reinterpret_cast<const uint4*>(kcur), qf, col, half, s);
+                if (J == I) {
 #pragma unroll
-                for (int sub = 0; sub < G::NSUB; ++sub)
+                    for (int j = 0; j < SH; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = 32 * sub + (r & 3) + 8 * (r >> 2) + 4 * half;
-                        s[sub][r] = key > qr ? -INFINITY : s[sub][r];
-                    }
-            }
-            softmax_update<G::NSUB, G::NDS>(s, c, 0.f, m, l, o, pk);
-            pv<D, BLK, HP>(vcur, pk, lane, o);
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = 32 * (S0 + j) + (r & 3) + 8 * (r >> 2) + 4 * half;
+                            s[j][r] = key > qr ? -INFINITY : s[j][r];
+                        }
+                }
+                softmax_update<SH, G::NDS>(s, c, 0.f, m, l, o, pk);
+                pv<D, BLK, HP, S0, SH>(vcur, pk, lane, o);
+            };
+            half_tile(std::integral_constant<int, 0>());
+            if (G::NSUB > SH) half_tile(std::integral_constant<int, (G::NSUB > SH ? SH : 0)>());
         }
         J = Jn;
         act = act_next;
@@ -300,16 +350,21 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
             store_pooled_tile<D, BLK, HP>(a.pv, prow0, c0, I, reinterpret_cast<uint4*>(vb0), tid);
             __syncthreads();
             if (nskip == 0) continue;
-            qk<D, BLK, HP>(reinterpret_cast<const uint4*>(kb0), qf, col, half, s);
+            auto corr_half = [&](auto sub0) {
+                constexpr int S0 = decltype(sub0)::value;
+                qk<D, BLK, HP, S0, SH>(reinterpret_cast<const uint4*>(kb0), qf, col, half, s);
 #pragma unroll
-            for (int sub = 0; sub < G::NSUB; ++sub) {
-                const uint32_t bits = skip[sub] >> (4 * half);
+                for (int j = 0; j < SH; ++j) {
+                    const uint32_t bits = skip[S0 + j] >> (4 * half);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
-            }
-            softmax_update<G::NSUB, G::NDS>(s, c, log2_blk, m, l, o, pk);
-            pv<D, BLK, HP>(vb0, pk, lane, o);
+                    for (int r = 0; r < 16; ++r)
+                        s[j][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[j][r] : -INFINITY;
+                }
+                softmax_update<SH, G::NDS>(s, c, log2_blk, m, l, o, pk);
+                pv<D, BLK, HP, S0, SH>(vb0, pk, lane, o);
+            };
+            corr_half(std::integral_constant<int, 0>());
+            if (G::NSUB > SH) corr_half(std::integral_constant<int, (G::NSUB > SH ? SH : 0)>());
         }
     }
 
