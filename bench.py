@@ -27,9 +27,24 @@ METRIC = "sparse prefill attn latency + effective TFLOP/s (% MFMA peak) at 128K,
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBPS = 8000.0
-# Averages of the attention kernel's rocprofv3 counters on this workload
-# (KiB per dispatch); None until measured on the current kernel.
-TRAFFIC_KIB = None
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attn_bf16_llama8b_s128k_traffic.json")
+ATTN_SOURCES = ("k_attn.hip", "fp_attn.h", "fp_device.h", "fp_launch.h")
+
+
+def measured_traffic():
+    """Calibrated HBM bytes per attention launch from the committed rocprofv3
+    counter record, or None when the kernel sources changed since it was taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_sparse_long_pooling_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def log(*a):
@@ -211,7 +226,8 @@ def main():
 
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "kernel": "k_attn_bf16<128,128>", "traffic": TRAFFIC_KIB}
+            "kernel": "k_attn_bf16<128,128,2>", "traffic": measured_traffic(),
+            "traffic_unit": "bytes/launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)"}
     rec = {
         "metric": METRIC, "value": round(step_tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
