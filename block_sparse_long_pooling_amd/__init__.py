@@ -44,9 +44,9 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 
 EXPORTS = {
     "fp_select_blocks": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, ctypes.c_int32,
-                                        _P, _P, _P, _P, _P, _P]),
+                                        _P, _P, _P, _P, _P, _P, _P]),
     "fp_sparse_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, _P, _P, _P,
-                                             ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
+                                             ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "fp_sparse_prefill_varlen_paged": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
                                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                       _I32P, ctypes.c_int32, _P, _P, _P,
@@ -119,7 +119,8 @@ class Selection:
     """Outputs of fp_select_blocks (device tensors)."""
     pooled_q: torch.Tensor      # fp32 [Hq, nB, d]
     pooled_k: torch.Tensor      # fp32 [Hkv, nB, d]
-    pooled_v: Optional[torch.Tensor]
+    pooled_v: Optional[torch.Tensor]    # fp32 [Hkv, nB, d]
+    pooled_kv: Optional[torch.Tensor]   # bf16 [2, Hkv, nB, d]: K_bar, V_bar (mean correction)
     kv_idx: torch.Tensor        # int32, triangular-packed lists
     kv_cnt: torch.Tensor        # int32 [Hq, nB]
     block_size: int
@@ -134,10 +135,11 @@ def alloc_selection(params: fp_params, seqlen: int, device, pool_v: Optional[boo
     pq = torch.empty((Hq, nB, d), dtype=torch.float32, device=device)
     pk = torch.empty((params.num_kv_heads, nB, d), dtype=torch.float32, device=device)
     pv = torch.empty_like(pk) if pool_v else None
+    pkv = torch.empty((2, params.num_kv_heads, nB, d), dtype=torch.bfloat16, device=device) if pool_v else None
     cap = fp_index_capacity(params, [0, seqlen])
     kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
     kv_cnt = torch.empty((Hq, nB), dtype=torch.int32, device=device)
-    return Selection(pq, pk, pv, kv_idx, kv_cnt, B)
+    return Selection(pq, pk, pv, pkv, kv_idx, kv_cnt, B)
 
 
 def fp_select_blocks(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
@@ -149,11 +151,10 @@ def fp_select_blocks(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: Opt
     dev = q.device
     if sel is None:
         sel = alloc_selection(params, S, dev, pool_v)
-    pool_v = sel.pooled_v is not None
-    pq, pk, pv, kv_idx, kv_cnt = sel.pooled_q, sel.pooled_k, sel.pooled_v, sel.kv_idx, sel.kv_cnt
+    pool_v = sel.pooled_v is not None or sel.pooled_kv is not None
     _check(lib().fp_select_blocks(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v) if pool_v else None,
-                                  S, _ptr(pq), _ptr(pk), _ptr(pv), _ptr(kv_idx), _ptr(kv_cnt),
-                                  _stream(dev)))
+                                  S, _ptr(sel.pooled_q), _ptr(sel.pooled_k), _ptr(sel.pooled_v),
+                                  _ptr(sel.pooled_kv), _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _stream(dev)))
     return sel
 
 
@@ -175,8 +176,8 @@ def fp_sparse_prefill_fwd(params: fp_params, q: torch.Tensor, k: torch.Tensor, v
         lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
     _check(lib().fp_sparse_prefill_fwd(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), S,
-                                       _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _ptr(sel.pooled_k),
-                                       _ptr(sel.pooled_v), _ptr(out), _ptr(lse), _stream(dev)))
+                                       _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _ptr(sel.pooled_kv),
+                                       _ptr(out), _ptr(lse), _stream(dev)))
     return (out, lse) if return_lse else out
 
 

@@ -124,18 +124,20 @@ int device_status(hipError_t e, const char* what) {
 int select_tile(const fp_params& p) { return 32 / (p.num_q_heads / p.num_kv_heads); }
 
 int run_select(const fp_params& p, const int32_t* cu, int32_t batch, const void* q, const void* k, const void* v,
-               const KVLayout& kv, bool paged, float* pq, float* pk, float* pv, int32_t* kv_idx,
-               int32_t* kv_cnt, hipStream_t st) {
+               const KVLayout& kv, bool paged, float* pq, float* pk, float* pv, uint16_t* pkv16,
+               int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
     SeqTable t;
     int rc = build_table(p, cu, batch, 1, t);
     if (rc) return rc;
     PoolArgs pa;
     pa.q = static_cast<const uint16_t*>(q);
     pa.k = static_cast<const uint16_t*>(k);
-    pa.v = pv ? static_cast<const uint16_t*>(v) : nullptr;
+    const bool pool_v = pv || pkv16;
+    pa.v = pool_v ? static_cast<const uint16_t*>(v) : nullptr;
     pa.pq = pq;
     pa.pk = pk;
     pa.pv = pv;
+    pa.pkv16 = pkv16;
     pa.kv = kv;
     pa.Hq = p.num_q_heads;
     pa.Hkv = p.num_kv_heads;
@@ -143,7 +145,7 @@ int run_select(const fp_params& p, const int32_t* cu, int32_t batch, const void*
     pa.B = p.block_size;
     pa.q_chunks = p.num_q_heads * p.head_dim / 8;
     pa.k_chunks = p.num_kv_heads * p.head_dim / 8;
-    pa.total_chunks = pa.q_chunks + pa.k_chunks * (pv ? 2 : 1);
+    pa.total_chunks = pa.q_chunks + pa.k_chunks * (pool_v ? 2 : 1);
     rc = device_status(launch_pool(pa, t, paged, st), "pool");
     if (rc) return rc;
 
@@ -196,15 +198,15 @@ FP_EXPORT int64_t fp_count_entries(const fp_params* params, const int32_t* cu_se
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WsLayout {
-    size_t q, k, v, total;
+    size_t q, k, kv16, total;   // fp32 Q_bar, fp32 K_bar, bf16 K_bar | V_bar
 };
 WsLayout ws_layout(const fp_params& p, int64_t total_blocks) {
     WsLayout w;
-    const size_t per = (size_t)total_blocks * p.head_dim * sizeof(float);
+    const size_t per = (size_t)total_blocks * p.head_dim;
     w.q = 0;
-    w.k = align256(per * p.num_q_heads);
-    w.v = w.k + align256(per * p.num_kv_heads);
-    w.total = w.v + (p.mean_correction ? align256(per * p.num_kv_heads) : 0);
+    w.k = align256(per * p.num_q_heads * sizeof(float));
+    w.kv16 = w.k + align256(per * p.num_kv_heads * sizeof(float));
+    w.total = w.kv16 + (p.mean_correction ? align256(2 * per * p.num_kv_heads * sizeof(uint16_t)) : 0);
     return w;
 }
 }  // namespace
@@ -216,8 +218,8 @@ FP_EXPORT size_t fp_varlen_workspace_bytes(const fp_params* params, const int32_
 }
 
 FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const void* k, const void* v, int32_t seqlen,
-                               float* pooled_q, float* pooled_k, float* pooled_v, int32_t* kv_idx, int32_t* kv_cnt,
-                               void* stream) {
+                               float* pooled_q, float* pooled_k, float* pooled_v, void* pooled_kv_bf16,
+                               int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
     int rc = check_params(params);
     if (rc) return rc;
     if (seqlen < 0) return fail(FP_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", seqlen);
@@ -229,18 +231,20 @@ FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const voi
         return fail(FP_INVALID_ARGUMENT, "kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
     if (pooled_v && (!aligned(pooled_v, 16) || !aligned(v, 16)))
         return fail(FP_INVALID_ARGUMENT, "pooled_v needs a non-NULL, 16-byte aligned v (and itself aligned)");
+    if (pooled_kv_bf16 && (!aligned(pooled_kv_bf16, 16) || !aligned(v, 16)))
+        return fail(FP_INVALID_ARGUMENT, "pooled_kv_bf16 needs a non-NULL, 16-byte aligned v (and itself aligned)");
     const int32_t cu[2] = {0, seqlen};
     KVLayout kv = {nullptr, 1, 0, 0};
     (void)hipGetLastError();
-    rc = run_select(*params, cu, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v, kv_idx, kv_cnt,
-                    static_cast<hipStream_t>(stream));
+    rc = run_select(*params, cu, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v,
+                    static_cast<uint16_t*>(pooled_kv_bf16), kv_idx, kv_cnt, static_cast<hipStream_t>(stream));
     return rc ? rc : ok();
 }
 
 FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, const void* k, const void* v,
                                     const float* q_scale, const float* k_scale, const float* v_scale, int32_t seqlen,
-                                    const int32_t* kv_idx, const int32_t* kv_cnt, const float* pooled_k,
-                                    const float* pooled_v, void* out, float* lse, void* stream) {
+                                    const int32_t* kv_idx, const int32_t* kv_cnt, const void* pooled_kv_bf16,
+                                    void* out, float* lse, void* stream) {
     int rc = check_params(params);
     if (rc) return rc;
     const fp_params& p = *params;
@@ -250,8 +254,8 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
         return fail(FP_INVALID_ARGUMENT, "q, k, v and out must be non-NULL and 16-byte aligned");
     if (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
         return fail(FP_INVALID_ARGUMENT, "kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
-    if (p.mean_correction && (!aligned(pooled_k, 16) || !aligned(pooled_v, 16)))
-        return fail(FP_INVALID_ARGUMENT, "mean_correction needs 16-byte aligned pooled_k and pooled_v");
+    if (p.mean_correction && !aligned(pooled_kv_bf16, 16))
+        return fail(FP_INVALID_ARGUMENT, "mean_correction needs a 16-byte aligned pooled_kv_bf16");
     if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
     const bool fp8 = p.dtype == FP_DTYPE_FP8_E4M3FN;
     if (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
@@ -269,8 +273,8 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
     a.v_scale = v_scale;
     a.kv_idx = kv_idx;
     a.kv_cnt = kv_cnt;
-    a.pk = pooled_k;
-    a.pv = pooled_v;
+    a.pk16 = static_cast<const uint16_t*>(pooled_kv_bf16);
+    a.pv16 = a.pk16 ? a.pk16 + (int64_t)p.num_kv_heads * t.total_blocks * p.head_dim : nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.kv = KVLayout{nullptr, 1, 0, 0};
@@ -321,11 +325,12 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     char* wsb = static_cast<char*>(workspace);
     float* pq = reinterpret_cast<float*>(wsb + ws.q);
     float* pk = reinterpret_cast<float*>(wsb + ws.k);
-    float* pv = p.mean_correction ? reinterpret_cast<float*>(wsb + ws.v) : nullptr;
+    uint16_t* pkv16 = p.mean_correction ? reinterpret_cast<uint16_t*>(wsb + ws.kv16) : nullptr;
     KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = run_select(p, cu_seqlens_host, batch, q, k_cache, v_cache, kv, true, pq, pk, pv, kv_idx, kv_cnt, st);
+    rc = run_select(p, cu_seqlens_host, batch, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, kv_idx, kv_cnt,
+                    st);
     if (rc) return rc;
     AttnArgs a;
     a.q = q;
@@ -334,8 +339,8 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     a.q_scale = a.k_scale = a.v_scale = nullptr;
     a.kv_idx = kv_idx;
     a.kv_cnt = kv_cnt;
-    a.pk = pk;
-    a.pv = pv;
+    a.pk16 = pkv16;
+    a.pv16 = pkv16 ? pkv16 + (int64_t)p.num_kv_heads * t.total_blocks * p.head_dim : nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.kv = kv;

@@ -6,6 +6,15 @@
 
 namespace fp_attn {
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS
+// operations complete (lgkmcnt 0), then all waves meet.  __syncthreads(), and
+// any release fence, also waits for every outstanding global access and LDS
+// DMA (vmcnt 0), which would stall on tile DMAs and loads that are meant to
+// stay in flight across the barrier.  Callers that need a DMA's data wait for
+// it explicitly first.  The memory clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Swap bits 2 and 3 of a key position inside its 16-key group.
@@ -79,19 +88,16 @@ __device__ __forceinline__ void load_kv_tile(const uint16_t* kb, const uint16_t*
     }
 }
 
-// Pooled K_bar / V_bar of blocks c0 .. c0+BLK-1 (zero for blocks >= I), as bf16.
+// Pooled K_bar / V_bar (bf16) of blocks c0 .. c0+BLK-1 (zero for blocks >= I).
 template <int D, int BLK>
-__device__ __forceinline__ void load_pooled_tile(const float* pk, const float* pv, int64_t prow0, int c0, int I,
+__device__ __forceinline__ void load_pooled_tile(const uint16_t* pk, const uint16_t* pv, int64_t prow0, int c0, int I,
                                                  uint4* lk, uint4* lv, int tid) {
     using T = Tile<D, BLK>;
     for (int i = tid; i < BLK * T::KCH; i += T::NT) {
         const int row = i / T::KCH, ch = i % T::KCH;
         const int J = c0 + row;
         uint4 val = make_uint4(0, 0, 0, 0);
-        if (J < I) {
-            const float4* s = reinterpret_cast<const float4*>(pk + (prow0 + J) * D + ch * 8);
-            val = f32x8_to_bf16(s[0], s[1]);
-        }
+        if (J < I) val = *reinterpret_cast<const uint4*>(pk + (prow0 + J) * D + ch * 8);
         lk[row * T::KCH + (ch ^ (row % T::KCH))] = val;
     }
     for (int i = tid; i < T::VCH * T::KCH; i += T::NT) {
@@ -101,10 +107,7 @@ __device__ __forceinline__ void load_pooled_tile(const float* pk, const float* p
         for (int u = 0; u < 8; ++u) {
             const int J = c0 + key_perm(8 * kg + u);
             x[u] = make_uint4(0, 0, 0, 0);
-            if (J < I) {
-                const float4* s = reinterpret_cast<const float4*>(pv + (prow0 + J) * D + dc * 8);
-                x[u] = f32x8_to_bf16(s[0], s[1]);
-            }
+            if (J < I) x[u] = *reinterpret_cast<const uint4*>(pv + (prow0 + J) * D + dc * 8);
         }
         transpose8(x, y);
 #pragma unroll
@@ -233,7 +236,7 @@ __device__ __forceinline__ void correction_pass(const AttnArgs& a, const SeqTabl
         }
         if (nskip == 0) continue;                      // every past block here is kept
         __syncthreads();
-        load_pooled_tile<D, BLK>(a.pk, a.pv, prow0, c0, I, lk, lv, tid);
+        load_pooled_tile<D, BLK>(a.pk16, a.pv16, prow0, c0, I, lk, lv, tid);
         __syncthreads();
         qk_tile<D, BLK>(lk, qf, col, half, s);
 #pragma unroll

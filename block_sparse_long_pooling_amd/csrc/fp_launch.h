@@ -12,6 +12,7 @@ struct PoolArgs {
     float* pq;           // [Hq, total_blocks, d]
     float* pk;           // [Hkv, total_blocks, d]
     float* pv;           // [Hkv, total_blocks, d] or null
+    uint16_t* pkv16;     // bf16 [2, Hkv, total_blocks, d] (K_bar then V_bar) or null
     KVLayout kv;
     int32_t Hq, Hkv, D, B;
     int32_t q_chunks;    // Hq * d / 8
@@ -38,8 +39,8 @@ struct AttnArgs {
     const float* v_scale;
     const int32_t* kv_idx;
     const int32_t* kv_cnt;
-    const float* pk;             // pooled [Hkv, total_blocks, d] (correction)
-    const float* pv;
+    const uint16_t* pk16;        // bf16 pooled K_bar [Hkv, total_blocks, d] (correction)
+    const uint16_t* pv16;        // bf16 pooled V_bar, same layout
     uint16_t* out;               // bf16 [T, Hq, d]
     float* lse;                  // [Hq, T] or null
     KVLayout kv;

@@ -26,6 +26,7 @@
 // with logit sigma*q.k_bar_J + ln n_J, masked per head to its skipped J < I.
 // Query heads of one KV head are placed on one XCD so their tiles meet in
 // that XCD's L2.
+#include <atomic>
 #include <type_traits>
 
 #include "fp_attn.h"
@@ -61,24 +62,22 @@ struct Geo {
 };
 
 // Per-thread DMA plan for a [BLK][D] bf16 tile: load i of this thread fills
-// LDS chunk i*NT + tid, i.e. row row[i], logical chunk (chunk position XOR
-// swizzle).  off[i] is that chunk's element offset inside the tile's rows for
-// contiguous K/V (row * row_stride + kv head * D + chunk * 8).
+// LDS chunk i*NT + tid, i.e. row row0 + i*NT/NCH and chunk position chunk0,
+// which holds logical chunk (chunk0 XOR swizzle of the row).  Two registers;
+// the rest is recomputed per load.
 template <int D, int BLK, int HP>
 struct DmaPlan {
-    static constexpr int NLOAD = BLK * (D / 8) / (64 * HP * (BLK / 32));
-    int row[NLOAD];
-    int coff[NLOAD];   // element offset inside one token row: hk * D + chunk * 8
-    __device__ __forceinline__ void init(int tid, int hk) {
-        constexpr int NT = 64 * HP * (BLK / 32);
-        constexpr int NCH = D / 8;
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            const int p = i * NT + tid;
-            row[i] = p / NCH;
-            coff[i] = hk * D + ((p % NCH) ^ swz<D>(row[i])) * 8;
-        }
+    static constexpr int NT = 64 * HP * (BLK / 32);
+    static constexpr int NCH = D / 8;
+    static constexpr int NLOAD = BLK * NCH / NT;
+    static constexpr int ROWSTEP = NT / NCH;
+    int row0, chunk0;
+    __device__ __forceinline__ void init(int tid) {
+        row0 = tid / NCH;
+        chunk0 = tid % NCH;
     }
+    __device__ __forceinline__ int row(int i) const { return row0 + i * ROWSTEP; }
+    __device__ __forceinline__ int coff(int i) const { return (chunk0 ^ swz<D>(row(i))) * 8; }
 };
 
 // DMA one tile: rows J*BLK .. of the request whose first row is `first`
@@ -91,35 +90,31 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t*
     static_assert((BLK * G::NCH) % G::NT == 0, "tile chunks must split evenly");
 #pragma unroll
     for (int i = 0; i < DmaPlan<D, BLK, HP>::NLOAD; ++i) {
-        const int row = plan.row[i];
+        const int row = plan.row(i);
         const void* src;
         if (!PAGED) {
-            const uint16_t* p = first + ((int64_t)J * BLK + row) * rs + plan.coff[i];
-            src = row < nvalid ? (const void*)p : (const void*)zero;
+            // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
+            // addressing form).  Rows past the end of the sequence re-read its
+            // last row: they occur only in the diagonal tile, where the causal
+            // mask removes them, and finite values keep 0 * v at 0.
+            // The row index is opaque so the compiler does not keep a
+            // precomputed offset per chunk and row stride (it would spill).
+            int r = row;
+            asm volatile("" : "+v"(r));
+            const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * BLK * rs);
+            const uint32_t off = (uint32_t)(min(r, nvalid - 1) * (int)rs + plan.coff(i)) * 2u;
+            src = tile + off;
         } else {
             const int tr = J * BLK + row;
             const int page = pages[tr / L.page_size];
-            const uint16_t* p = first + ((int64_t)page * L.page_size + tr % L.page_size) * rs + plan.coff[i];
+            // Opaque column offset: keeps the compiler from holding a 64-bit
+            // pointer per chunk across the loop (it would spill).
+            int co = plan.coff(i);
+            asm volatile("" : "+v"(co));
+            const uint16_t* p = first + ((int64_t)page * L.page_size + tr % L.page_size) * rs + co;
             src = (row < nvalid && (unsigned)page < (unsigned)L.num_pages) ? (const void*)p : (const void*)zero;
         }
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT) * 16 + wave_base), 16, 0, 0);
-    }
-}
-
-// Pooled rows c0 .. c0+BLK-1 (zero for blocks >= I) as bf16 into a tile buffer.
-template <int D, int BLK, int HP>
-__device__ __forceinline__ void store_pooled_tile(const float* src, int64_t prow0, int c0, int I, uint4* tile,
-                                                  int tid) {
-    using G = Geo<D, BLK, HP>;
-    for (int i = tid; i < BLK * G::NCH; i += G::NT) {
-        const int row = i / G::NCH, c = i % G::NCH;
-        const int J = c0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (J < I) {
-            const float4* s = reinterpret_cast<const float4*>(src + (prow0 + J) * D + c * 8);
-            v = f32x8_to_bf16(s[0], s[1]);
-        }
-        tile[row * G::NCH + (c ^ swz<D>(row))] = v;
     }
 }
 
@@ -185,123 +180,293 @@ template <int HP>
 struct Union {
     const int32_t* list[HP];
     int cnt[HP];
-    int pos[HP];
-    __device__ __forceinline__ int head(int h) const { return pos[h] < cnt[h] ? list[h][pos[h]] : INT_MAX; }
+    int cap;         // capacity of each list (I + 1): windows never read past it
+    int pos[HP];     // entries of list h consumed so far
+    int wbase[HP];   // list index held by lane 0 of win[h]
+    int win[HP];     // lane l: list[h][wbase[h] + l] (INT_MAX past the end)
+    // Lists are read 64 entries at a time, one per lane, so the walk waits
+    // on memory once per 64 kept blocks instead of once per block.  A window
+    // is bounded by the list's capacity, not its count, so it need not wait
+    // for the count; entries past the count are never used.
+    __device__ __forceinline__ void load_window(int h) {
+        wbase[h] = pos[h];
+        const int i = pos[h] + (int)__lane_id();
+        win[h] = i < cap ? list[h][i] : INT_MAX;
+    }
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int h = 0; h < HP; ++h) {
+            pos[h] = 0;
+            load_window(h);
+        }
+    }
+    __device__ __forceinline__ int val(int h) const {
+        return pos[h] < cnt[h] ? __builtin_amdgcn_readlane(win[h], pos[h] - wbase[h]) : INT_MAX;
+    }
     // Next block of the union and the heads that keep it (bit mask); INT_MAX when done.
     __device__ __forceinline__ int next(int& act) {
+        int v[HP];
         int J = INT_MAX;
 #pragma unroll
-        for (int h = 0; h < HP; ++h) J = min(J, head(h));
+        for (int h = 0; h < HP; ++h) {
+            v[h] = val(h);
+            J = min(J, v[h]);
+        }
         act = 0;
 #pragma unroll
         for (int h = 0; h < HP; ++h)
-            if (J != INT_MAX && head(h) == J) { act |= 1 << h; ++pos[h]; }
+            if (J != INT_MAX && v[h] == J) {
+                act |= 1 << h;
+                if (++pos[h] - wbase[h] == 64) load_window(h);
+            }
         return J;
     }
 };
 
+// One work item: query block I of one request, HP heads of one KV head.
+template <int D, int BLK, int HP, bool PAGED>
+struct Item {
+    int b, nb, I, tok0, len, q0, nI, hk, h;      // h: this wave's query head
+    int nct;                                      // correction tiles (blocks 0 .. I-1 in tiles of BLK)
+    int ct;                                       // next correction tile to examine; -1 while kept blocks remain
+    Union<HP> u;
+    const uint16_t* kfirst;                       // K rows of this request / KV head (or the pool)
+    const uint16_t* vfirst;
+    const int32_t* pages;                         // block-table row (paged)
+
+    __device__ __forceinline__ void setup(const AttnArgs& a, const SeqTable& t, int idx, int hs) {
+        const int npairs = a.Hq / HP;
+        const int rank = idx / npairs;
+        h = HP * xcd_head(idx % npairs, npairs) + hs;
+        int local;
+        item_of(t, rank, b, local);
+        nb = seq_blocks(t, b);
+        I = nb - 1 - local;
+        tok0 = t.tok_off[b];
+        len = t.tok_off[b + 1] - tok0;
+        q0 = tok0 + I * BLK;
+        nI = min(BLK, len - I * BLK);
+        hk = h / a.g;
+        const int64_t rs = (int64_t)a.Hkv * D;
+        const int64_t tri = (int64_t)nb * (nb + 1) / 2;
+        const int h0 = h - hs;
+#pragma unroll
+        for (int j = 0; j < HP; ++j) {
+            u.list[j] = a.kv_idx + t.idx_off[b] + (int64_t)(h0 + j) * tri + (int64_t)I * (I + 1) / 2;
+            u.cnt[j] = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)(h0 + j) * nb + I];
+        }
+        u.cap = I + 1;
+        u.init();
+        nct = (a.correction && I > 0) ? (I + BLK - 1) / BLK : 0;
+        ct = -1;
+        const int64_t base = (PAGED ? 0 : (int64_t)tok0 * rs) + (int64_t)hk * D;
+        kfirst = static_cast<const uint16_t*>(a.k) + base;
+        vfirst = static_cast<const uint16_t*>(a.v) + base;
+        pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
+    }
+};
+
+// Tiles of a work item are coded as ints: a kept KV block J (0 <= J <= I), or
+// kCorr + ct for correction tile ct (pooled blocks ct*BLK .. ct*BLK+BLK-1).
+constexpr int kCorr = FP_MAX_BLOCKS;
+
+// Persistent: each workgroup takes one work item from each band of G =
+// gridDim consecutive items (items run longest first; G is a multiple of 8 so
+// an item keeps its XCD).  An item walks its tiles -- the kept blocks of its
+// HP heads in ascending order, then the tiles of skipped past blocks whose
+// pooled means form the correction -- through one double-buffered DMA
+// pipeline.  As soon as the walk ends, the next item's first tile is DMA'd
+// into buffer pair 1 while this item's output is normalised and stored.
 template <int D, int BLK, int HP, bool PAGED>
 __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, SeqTable t) {
     using G = Geo<D, BLK, HP>;
+    using It = Item<D, BLK, HP, PAGED>;
     // Four separate LDS objects: the compiler then sees that a DMA into one
     // buffer does not touch the buffer being read, and does not wait on it.
     __shared__ __attribute__((aligned(16))) char kb0[G::TILE];
     __shared__ __attribute__((aligned(16))) char kb1[G::TILE];
     __shared__ __attribute__((aligned(16))) char vb0[G::TILE];
     __shared__ __attribute__((aligned(16))) char vb1[G::TILE];
+    // Bit J of head j: block J < I is kept by head j of the current item.
     __shared__ uint32_t kept_bits[HP][FP_MAX_BLOCKS / 32];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int hs = w / G::WPH;                   // which of the HP heads this wave serves
     const int rw = w % G::WPH;                   // 32-row group inside the query block
-    const int npairs = a.Hq / HP;
-    const int rank = blockIdx.x / npairs;
-    const int h = HP * xcd_head(blockIdx.x % npairs, npairs) + hs;
-    int b, local;
-    item_of(t, rank, b, local);
-    const int nb = seq_blocks(t, b);
-    const int I = nb - 1 - local;
-    const int tok0 = t.tok_off[b];
-    const int len = t.tok_off[b + 1] - tok0;
-    const int q0 = tok0 + I * BLK;
-    const int nI = min(BLK, len - I * BLK);
-    const int hk = h / a.g;
+    const int nitems = t.total_items * (a.Hq / HP);
     const int64_t rs = (int64_t)a.Hkv * D;
-    const int64_t tri = (int64_t)nb * (nb + 1) / 2;
-    const int h0 = h - hs;
+    const float c = a.scale_log2;
+    const float log2_blk = __log2f((float)BLK);  // past blocks are full: ln n_J = ln BLK
+    // Band k of gridDim items goes to the workgroups rotated by k rows of 8,
+    // so a workgroup stays on its XCD (item % 8) but does not always draw the
+    // same head pair (heads differ in density).
+    const int G8 = gridDim.x % 8 == 0 ? (int)gridDim.x / 8 : 0;
+    auto item_index = [&](int k) {
+        return G8 ? k * (int)gridDim.x + (((int)blockIdx.x / 8 + k) % G8) * 8 + (int)blockIdx.x % 8
+                  : k * (int)gridDim.x + (int)blockIdx.x;
+    };
+    int band = 0;
+    int idx = item_index(0);
+    if (idx >= nitems) return;
 
-    Union<HP> u;
-#pragma unroll
-    for (int j = 0; j < HP; ++j) {
-        u.list[j] = a.kv_idx + t.idx_off[b] + (int64_t)(h0 + j) * tri + (int64_t)I * (I + 1) / 2;
-        u.cnt[j] = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)(h0 + j) * nb + I];
-        u.pos[j] = 0;
-    }
-    const int qr = 32 * rw + col;
-    // Tile DMA: contiguous K/V start at this request's first row; paged K/V
-    // start at the pool and go through the request's block-table row.
-    const uint16_t* kfirst = static_cast<const uint16_t*>(a.k) + (PAGED ? 0 : (int64_t)tok0 * rs);
-    const uint16_t* vfirst = static_cast<const uint16_t*>(a.v) + (PAGED ? 0 : (int64_t)tok0 * rs);
-    const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
+    // Lane-dependent values.  They are re-derived through an opaque copy of the
+    // thread index at the start of each item and of the epilogue, so the
+    // compiler keeps only the current phase's LDS addresses in registers
+    // instead of hoisting all of them out of the item loop.
+    int lane, col, half, qr, tphase;
+    auto phase = [&]() {
+        tphase = tid;
+        asm volatile("" : "+v"(tphase));
+        lane = tphase & 63;
+        col = lane & 31;
+        half = lane >> 5;
+        qr = 32 * rw + col;
+    };
+    phase();
+
+    // Per-thread DMA plan: chunk offsets relative to a tile's first row.
     DmaPlan<D, BLK, HP> plan;
-    plan.init(tid, hk);
     const uint4* zero = &kZeroChunk;
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
-
-    bf16x8 qf[D / 16];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + qr) * a.Hq + h) * D + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (qr < nI) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
-            qf[kk] = __builtin_bit_cast(bf16x8, x);
+    auto issue = [&](const It& itm, int code, char* kdst, char* vdst) {
+        if (code < kCorr) {
+            issue_tile<D, BLK, HP, PAGED>(itm.kfirst, itm.pages, a.kv, rs, code, itm.len - code * BLK, plan, zero,
+                                          kdst, wave_base);
+            issue_tile<D, BLK, HP, PAGED>(itm.vfirst, itm.pages, a.kv, rs, code, itm.len - code * BLK, plan, zero,
+                                          vdst, wave_base);
+        } else {
+            // Pooled rows of this request's blocks for the KV head (contiguous, row stride D).
+            const int ct = code - kCorr;
+            const int64_t prow = ((int64_t)itm.hk * t.total_blocks + t.blk_off[itm.b]) * D;
+            issue_tile<D, BLK, HP, false>(a.pk16 + prow, nullptr, a.kv, D, ct, itm.I - ct * BLK, plan, zero, kdst,
+                                          wave_base);
+            issue_tile<D, BLK, HP, false>(a.pv16 + prow, nullptr, a.kv, D, ct, itm.I - ct * BLK, plan, zero, vdst,
+                                          wave_base);
         }
-    }
-    const float c = a.scale_log2;
-    float m = -INFINITY, l = 0.f;
-    f32x16 o[G::NDS];
+    };
+    // Record a kept block in the bitmap (each wave sets it itself, so its own
+    // later reads see it without a barrier).
+    auto mark = [&](const It& itm, int code, int act) {
+        if (code < itm.I && lane == 0) {
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) o[ds] = f32x16{};
+            for (int j = 0; j < HP; ++j)
+                if ((act >> j) & 1) atomicOr(&kept_bits[j][code >> 5], 1u << (code & 31));
+        }
+    };
+    // Next tile of an item: its kept blocks, then the correction tiles in
+    // which some head skips a past block (act: the heads that use the tile).
+    auto next_tile = [&](It& itm, int& act) -> int {
+        if (itm.ct < 0) {
+            const int J = itm.u.next(act);
+            if (J != INT_MAX) {
+                mark(itm, J, act);
+                return J;
+            }
+            itm.ct = 0;
+        }
+        while (itm.ct < itm.nct) {
+            const int ct = itm.ct++;
+            int any = 0;
+#pragma unroll
+            for (int sub = 0; sub < G::NSUB; ++sub) {
+                const int j0 = ct * BLK + 32 * sub;
+                const int nvalid = min(32, max(0, itm.I - j0));
+                const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+#pragma unroll
+                for (int j = 0; j < HP; ++j)
+                    if (~kept_bits[j][j0 >> 5] & valid) any |= 1 << j;
+            }
+            any = __builtin_amdgcn_readfirstlane(any);
+            if (any) {
+                act = any;
+                return kCorr + ct;
+            }
+        }
+        return INT_MAX;
+    };
+    auto zero_bits = [&](const It& itm) {
+        const int nwords = (itm.I + 31) >> 5;
+        for (int i = tphase; i < HP * nwords; i += G::NT) kept_bits[i / nwords][i % nwords] = 0u;
+    };
+    bf16x8 qf[D / 16];
+    // Rows past the end of a ragged last block re-read the last valid row:
+    // their outputs are never stored, and unconditional loads keep the
+    // compiler from waiting on them (and on DMAs issued before) when the
+    // registers are written.
+    auto load_q = [&](const It& itm) {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(itm.q0 + min(qr, itm.nI - 1)) * a.Hq + itm.h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 16 * kk));
+    };
+
+    It cur;
+    cur.setup(a, t, idx, hs);
+    int act, act_next;
+    plan.init(tphase);
+    zero_bits(cur);
+    lds_barrier();
+    int J = next_tile(cur, act);
+    if (J != INT_MAX) issue(cur, J, kb1, vb1);
+    load_q(cur);
+
+    float m, l;
+    f32x16 o[G::NDS];
     constexpr int SH = G::NSUB > 1 ? G::NSUB / 2 : 1;   // subtiles per half tile
     f32x16 s[SH];
     uint32_t pk[SH][8];
 
-    int act, act_next;
-    int J = u.next(act);
-    if (J != INT_MAX) {
-        issue_tile<D, BLK, HP, PAGED>(kfirst, pages, a.kv, rs, J, len - J * BLK, plan, zero, kb0, wave_base);
-        issue_tile<D, BLK, HP, PAGED>(vfirst, pages, a.kv, rs, J, len - J * BLK, plan, zero, vb0, wave_base);
-    }
-    // One kept tile: wait for its DMA, release the other buffers by the
-    // barrier, prefetch the next tile into them, compute on this one.
+    // One tile: wait for its DMA, release the other buffers by the barrier,
+    // prefetch the next tile into them, compute on this one.
     auto step = [&](char* kcur, char* vcur, char* knext, char* vnext) {
-        const int Jn = u.next(act_next);
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA for tile J is done
-        __syncthreads();                                 // ... every thread's; the other buffers are free
-        if (Jn != INT_MAX) {
-            issue_tile<D, BLK, HP, PAGED>(kfirst, pages, a.kv, rs, Jn, len - Jn * BLK, plan, zero, knext,
-                                          wave_base);
-            issue_tile<D, BLK, HP, PAGED>(vfirst, pages, a.kv, rs, Jn, len - Jn * BLK, plan, zero, vnext,
-                                          wave_base);
-        }
+        lds_barrier();                                   // ... every thread's; the other buffers are free
+        const int Jn = next_tile(cur, act_next);
+        if (Jn != INT_MAX) issue(cur, Jn, knext, vnext);
         if ((act >> hs) & 1) {
+            const bool corr = J >= kCorr;
+            // Correction tile: bit j of skip[sub] <=> pooled block ct*BLK + 32 sub + j
+            // is strictly past and not kept by this head.
+            uint32_t skip[G::NSUB];
+            if (corr) {
+#pragma unroll
+                for (int sub = 0; sub < G::NSUB; ++sub) {
+                    const int j0 = (J - kCorr) * BLK + 32 * sub;
+                    const int nvalid = min(32, max(0, cur.I - j0));
+                    const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+                    skip[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[hs][j0 >> 5] & valid);
+                }
+            }
             // Two halves of SH subtiles each: online softmax per half keeps S and
             // P at half size, which leaves registers to read operands ahead.
             auto half_tile = [&](auto sub0) {
                 constexpr int S0 = decltype(sub0)::value;
                 qk<D, BLK, HP, S0, SH>(reinterpret_cast<const uint4*>(kcur), qf, col, half, s);
-                if (J == I) {
+                if (corr) {
+#pragma unroll
+                    for (int j = 0; j < SH; ++j) {
+                        const uint32_t bits = skip[S0 + j] >> (4 * half);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            s[j][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[j][r] : -INFINITY;
+                    }
+                } else if (J == cur.I) {
+                    // Causal mask of the diagonal tile.  The limit is made opaque so
+                    // the 16 * SH lane masks are computed here, once per item, instead
+                    // of being hoisted out of the loops and held in registers.
+                    int lim = qr - 4 * half;
+                    asm volatile("" : "+v"(lim));
 #pragma unroll
                     for (int j = 0; j < SH; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int key = 32 * (S0 + j) + (r & 3) + 8 * (r >> 2) + 4 * half;
-                            s[j][r] = key > qr ? -INFINITY : s[j][r];
+                            const int key = 32 * (S0 + j) + (r & 3) + 8 * (r >> 2);
+                            s[j][r] = key > lim ? -INFINITY : s[j][r];
                         }
                 }
-                softmax_update<SH, G::NDS>(s, c, 0.f, m, l, o, pk);
+                softmax_update<SH, G::NDS>(s, c, corr ? log2_blk : 0.f, m, l, o, pk);
                 pv<D, BLK, HP, S0, SH>(vcur, pk, lane, o);
             };
             half_tile(std::integral_constant<int, 0>());
@@ -310,97 +475,125 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         J = Jn;
         act = act_next;
     };
-    while (J != INT_MAX) {
-        step(kb0, vb0, kb1, vb1);
-        if (J == INT_MAX) break;
-        step(kb1, vb1, kb0, vb0);
-    }
 
-    if (a.correction && I > 0) {
-        const int nwords = (I + 31) >> 5;
-        __syncthreads();                                 // last tile's reads are done
-        for (int i = tid; i < HP * nwords; i += G::NT) kept_bits[i / nwords][i % nwords] = 0u;
-        __syncthreads();
+    while (true) {
+        phase();
+        plan.init(tphase);
+        m = -INFINITY;
+        l = 0.f;
 #pragma unroll
-        for (int j = 0; j < HP; ++j)
-            for (int i = tid; i < u.cnt[j]; i += G::NT) {
-                const int Jk = u.list[j][i];
-                if (Jk < I) atomicOr(&kept_bits[j][Jk >> 5], 1u << (Jk & 31));
-            }
-        __syncthreads();
-        const int64_t prow0 = (int64_t)hk * t.total_blocks + t.blk_off[b];
-        const float log2_blk = __log2f((float)BLK);      // past blocks are full: ln n_J = ln BLK
-        for (int c0 = 0; c0 < I; c0 += BLK) {
-            // Bit j of skip[sub] <=> block c0 + 32 sub + j is strictly past and not kept by this head.
-            uint32_t skip[G::NSUB];
-            int nskip = 0, nany = 0;
+        for (int ds = 0; ds < G::NDS; ++ds) o[ds] = f32x16{};
+        // All tiles; the first one is already in pair 1.
+        while (J != INT_MAX) {
+            step(kb1, vb1, kb0, vb0);
+            if (J == INT_MAX) break;
+            step(kb0, vb0, kb1, vb1);
+        }
+        lds_barrier();                                   // all reads of the last tile and the bitmap are done
+
+        // Next item: its lists and first tile (pair 1) go in flight now.
+        const int nidx = item_index(band + 1);
+        const bool has_next = nidx < nitems;
+        It nxt;
+        int Jn0 = INT_MAX, actn0 = 0;
+        if (has_next) {
+            nxt.setup(a, t, nidx, hs);
+            zero_bits(nxt);
+            Jn0 = nxt.u.next(actn0);                     // a kept block (lists are never empty)
+            if (Jn0 != INT_MAX) issue(nxt, Jn0, kb1, vb1);
+        }
+
+        // Epilogue: normalise, stage each head's bf16 tile in LDS (kb0 for the
+        // first head, vb0 for the second; the next item's first tile is
+        // arriving in kb1/vb1), store full rows.  Each buffer is named in a
+        // branch of its own, kept apart by distinct empty asm statements, so
+        // the compiler sees which object is accessed and does not wait for
+        // the DMA.
+        phase();
+        const float l_tot = l + __shfl_xor(l, 32);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        lds_barrier();                                   // zeroed bitmap; staging buffers free
+        if (has_next) mark(nxt, Jn0, actn0);
+        auto stage_rows = [&](char* buf) {
+            uint4* stage = reinterpret_cast<uint4*>(buf);
 #pragma unroll
-            for (int sub = 0; sub < G::NSUB; ++sub) {
-                const int j0 = c0 + 32 * sub;
-                const int nvalid = min(32, max(0, I - j0));
-                const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-                skip[sub] = ~kept_bits[hs][j0 >> 5] & valid;
-                nskip += __popc(skip[sub]);
+            for (int ds = 0; ds < G::NDS; ++ds)
 #pragma unroll
-                for (int j = 0; j < HP; ++j) nany += __popc(~kept_bits[j][j0 >> 5] & valid);
-            }
-            if (nany == 0) continue;                     // every head keeps every past block here
-            __syncthreads();
-            store_pooled_tile<D, BLK, HP>(a.pk, prow0, c0, I, reinterpret_cast<uint4*>(kb0), tid);
-            store_pooled_tile<D, BLK, HP>(a.pv, prow0, c0, I, reinterpret_cast<uint4*>(vb0), tid);
-            __syncthreads();
-            if (nskip == 0) continue;
-            auto corr_half = [&](auto sub0) {
-                constexpr int S0 = decltype(sub0)::value;
-                qk<D, BLK, HP, S0, SH>(reinterpret_cast<const uint4*>(kb0), qf, col, half, s);
-#pragma unroll
-                for (int j = 0; j < SH; ++j) {
-                    const uint32_t bits = skip[S0 + j] >> (4 * half);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[j][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[j][r] : -INFINITY;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int chunk = 4 * ds + g4;       // d0 = 32 ds + 8 g4 + 4 half
+                    const uint2 v2 = make_uint2(pack_bf16(o[ds][4 * g4] * inv, o[ds][4 * g4 + 1] * inv),
+                                                pack_bf16(o[ds][4 * g4 + 2] * inv, o[ds][4 * g4 + 3] * inv));
+                    reinterpret_cast<uint2*>(&stage[qr * G::NCH + (chunk ^ swz<D>(qr))])[half] = v2;
                 }
-                softmax_update<SH, G::NDS>(s, c, log2_blk, m, l, o, pk);
-                pv<D, BLK, HP, S0, SH>(vb0, pk, lane, o);
-            };
-            corr_half(std::integral_constant<int, 0>());
-            if (G::NSUB > SH) corr_half(std::integral_constant<int, (G::NSUB > SH ? SH : 0)>());
+        };
+        auto store_rows = [&](const char* buf) {
+            const uint4* stage = reinterpret_cast<const uint4*>(buf);
+            const int ht = tphase % (64 * G::WPH);       // thread index within this head's waves
+            for (int i = ht; i < cur.nI * G::NCH; i += 64 * G::WPH) {
+                const int row = i / G::NCH, ch = i % G::NCH;
+                *reinterpret_cast<uint4*>(a.out + ((int64_t)(cur.q0 + row) * a.Hq + cur.h) * D + ch * 8) =
+                    stage[row * G::NCH + (ch ^ swz<D>(row))];
+            }
+        };
+        if (hs == 0) {
+            stage_rows(kb0);
+            asm volatile("; staged head 0");
+        } else {
+            stage_rows(vb0);
+            asm volatile("; staged head 1");
         }
+        if (has_next) load_q(nxt);                       // O is staged: its registers take the next Q
+        lds_barrier();
+        if (hs == 0) {
+            store_rows(kb0);
+            asm volatile("; stored head 0");
+        } else {
+            store_rows(vb0);
+            asm volatile("; stored head 1");
+        }
+        if (a.lse && half == 0 && qr < cur.nI)
+            a.lse[(int64_t)cur.h * t.total_tokens + cur.q0 + qr] = (m + __log2f(l_tot)) * kLn2;
+        if (!has_next) break;
+        cur = nxt;
+        idx = nidx;
+        ++band;
+        J = Jn0;
+        act = actn0;
     }
+}
 
-    // Epilogue: normalise, stage each head's bf16 tile in LDS, store full rows.
-    const float l_tot = l + __shfl_xor(l, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __syncthreads();
-    uint4* stage = reinterpret_cast<uint4*>(hs == 0 ? kb0 : kb1);
-#pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int chunk = 4 * ds + g4;               // d0 = 32 ds + 8 g4 + 4 half
-            const uint2 v2 = make_uint2(pack_bf16(o[ds][4 * g4] * inv, o[ds][4 * g4 + 1] * inv),
-                                        pack_bf16(o[ds][4 * g4 + 2] * inv, o[ds][4 * g4 + 3] * inv));
-            reinterpret_cast<uint2*>(&stage[qr * G::NCH + (chunk ^ swz<D>(qr))])[half] = v2;
-        }
-    __syncthreads();
-    const int ht = tid % (64 * G::WPH);                  // thread index within this head's waves
-    for (int i = ht; i < nI * G::NCH; i += 64 * G::WPH) {
-        const int row = i / G::NCH, ch = i % G::NCH;
-        *reinterpret_cast<uint4*>(a.out + ((int64_t)(q0 + row) * a.Hq + h) * D + ch * 8) =
-            stage[row * G::NCH + (ch ^ swz<D>(row))];
+// Persistent grid: as many workgroups as the device holds at once (a multiple
+// of the 8 XCDs), at most one per item.  The resident count is computed once
+// per kernel and device.
+template <typename K>
+int persistent_grid(K kernel, int block, int nitems) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> resident[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nitems;
+    int n = resident[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int ncu = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
+            return nitems;
+        n = max(8, (ncu * max(per_cu, 1)) / 8 * 8);
+        resident[dev].store(n, std::memory_order_relaxed);
     }
-    if (a.lse && half == 0 && qr < nI)
-        a.lse[(int64_t)h * t.total_tokens + q0 + qr] = (m + __log2f(l_tot)) * kLn2;
+    return max(1, min(nitems, n));
 }
 
 template <int D, int BLK, int HP>
 hipError_t launch_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
-    dim3 grid((unsigned)t.total_items * (a.Hq / HP));
-    dim3 block(64 * HP * (BLK / 32));
-    if (paged)
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, true>), grid, block, 0, s, a, t);
-    else
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, false>), grid, block, 0, s, a, t);
+    const int nitems = t.total_items * (a.Hq / HP);
+    const int block = 64 * HP * (BLK / 32);
+    if (paged) {
+        auto k = k_attn_bf16<D, BLK, HP, true>;
+        hipLaunchKernelGGL(k, dim3(persistent_grid(k, block, nitems)), dim3(block), 0, s, a, t);
+    } else {
+        auto k = k_attn_bf16<D, BLK, HP, false>;
+        hipLaunchKernelGGL(k, dim3(persistent_grid(k, block, nitems)), dim3(block), 0, s, a, t);
+    }
     return hipGetLastError();
 }
 

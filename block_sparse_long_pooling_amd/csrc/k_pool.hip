@@ -1,6 +1,8 @@
 // Block-mean pooling of Q, K and V (FlashPrefill, gist.science technical
 // summary, section 2.A: keys are replaced by their block mean; queries are
 // pooled the same way, and V is pooled for the V2 mean-correction term).
+// K_bar and V_bar are also written rounded to bf16, the form in which the
+// attention kernels consume them.
 //
 // One workgroup covers one query block of one request and 256 column chunks
 // of 8 bf16 (16 bytes) taken from the concatenated row [Q | K | V].  Each
@@ -35,6 +37,7 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float* dst;
+    uint16_t* dst16 = nullptr;   // bf16 copy (K_bar / V_bar only)
     int col;
     if (c < a.q_chunks) {
         // Q: packed rows, never paged.
@@ -56,7 +59,13 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
         int cc = c - a.q_chunks;
         const uint16_t* base = a.k;
         dst = a.pk;
-        if (cc >= a.k_chunks) { cc -= a.k_chunks; base = a.v; dst = a.pv; }
+        dst16 = a.pkv16;
+        if (cc >= a.k_chunks) {
+            cc -= a.k_chunks;
+            base = a.v;
+            dst = a.pv;
+            if (dst16) dst16 += (int64_t)a.Hkv * t.total_blocks * a.D;
+        }
         col = cc * 8;
         const int64_t row_elems = (int64_t)a.Hkv * a.D;
         int r = 0;
@@ -79,9 +88,18 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
     const int h = col / a.D;
     const int dd = col % a.D;
     const float fn = (float)n;
-    float* o = dst + ((int64_t)h * t.total_blocks + gb) * a.D + dd;
-    reinterpret_cast<float4*>(o)[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
-    reinterpret_cast<float4*>(o)[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+    float mean[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
+    const int64_t off = ((int64_t)h * t.total_blocks + gb) * a.D + dd;
+    if (dst) {
+        reinterpret_cast<float4*>(dst + off)[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
+        reinterpret_cast<float4*>(dst + off)[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
+    }
+    if (dst16)   // the same means rounded to bf16 (nearest even): the correction's operands
+        *reinterpret_cast<uint4*>(dst16 + off) =
+            make_uint4(pack_bf16(mean[0], mean[1]), pack_bf16(mean[2], mean[3]), pack_bf16(mean[4], mean[5]),
+                       pack_bf16(mean[6], mean[7]));
 }
 
 }  // namespace

@@ -73,16 +73,19 @@ typedef struct {
 /*
  * Selection: steps 1-4 for one sequence of length seqlen (FlashPrefill 2.A-2.C).
  *   q [S,Hq,d], k [S,Hkv,d], v [S,Hkv,d]: bf16, whatever params->dtype says
- *     (fp8 attention selects on the bf16 data).  v may be NULL when pooled_v is.
+ *     (fp8 attention selects on the bf16 data).  v may be NULL when pooled_v
+ *     and pooled_kv_bf16 both are (then V is not read).
  *   pooled_q [Hq,nB,d], pooled_k [Hkv,nB,d], pooled_v [Hkv,nB,d]: fp32 outputs,
- *     means over the valid tokens of each block.  pooled_v may be NULL (then V
- *     is not read); the mean correction in fp_sparse_prefill_fwd needs it.
+ *     means over the valid tokens of each block.  pooled_v may be NULL.
+ *   pooled_kv_bf16 [2,Hkv,nB,d] bf16 output or NULL: the K and V block means
+ *     rounded to bf16 (nearest even), K_bar first.  The mean correction in
+ *     fp_sparse_prefill_fwd reads it.
  *   kv_idx, kv_cnt: int32 outputs in the list layout above.
  * Lists are ascending and never empty: the row's best block always passes.
  */
 int fp_select_blocks(const fp_params* params,
                      const void* q, const void* k, const void* v, int32_t seqlen,
-                     float* pooled_q, float* pooled_k, float* pooled_v,
+                     float* pooled_q, float* pooled_k, float* pooled_v, void* pooled_kv_bf16,
                      int32_t* kv_idx, int32_t* kv_cnt, void* stream);
 
 /*
@@ -93,8 +96,9 @@ int fp_select_blocks(const fp_params* params,
  *     fp32 per-(head, block) scales, x = code * scale, and block = block_size.
  *     The scale pointers are ignored for bf16.
  *   kv_idx, kv_cnt: lists in the layout above.
- *   pooled_k, pooled_v: fp32 [Hkv,nB,d] from fp_select_blocks; required when
- *     params->mean_correction is 1, ignored otherwise.
+ *   pooled_kv_bf16: bf16 [2,Hkv,nB,d] block means (K_bar then V_bar) from
+ *     fp_select_blocks; required when params->mean_correction is 1, ignored
+ *     otherwise.
  *   out [S,Hq,d] bf16 (written); lse [Hq,S] fp32 natural-log sum of exp of
  *     each row's logits (written when not NULL).
  */
@@ -102,7 +106,7 @@ int fp_sparse_prefill_fwd(const fp_params* params,
                           const void* q, const void* k, const void* v,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           int32_t seqlen, const int32_t* kv_idx, const int32_t* kv_cnt,
-                          const float* pooled_k, const float* pooled_v,
+                          const void* pooled_kv_bf16,
                           void* out, float* lse, void* stream);
 
 /*

@@ -79,35 +79,42 @@ MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
 def test_bad_params_rejected(kw, status):
     l = fp.lib()
     p = _p(**kw)
-    rc = l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    rc = l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == status
     assert l.fp_last_error().decode()
     rc = l.fp_sparse_prefill_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
-                                 FAKE, FAKE, FAKE, None, None)
+                                 FAKE, FAKE, None, None)
     assert rc == status
 
 
 def test_bad_pointers_rejected():
     l = fp.lib()
     p = _p()
-    assert l.fp_select_blocks(ctypes.byref(p), None, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert l.fp_select_blocks(ctypes.byref(p), None, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               None) == fp.FP_INVALID_ARGUMENT
     assert l.fp_select_blocks(ctypes.byref(p), MISALIGNED, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(None, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    # bf16 pooled means need V
+    assert l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, None, 1024, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                              None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, None, MISALIGNED, FAKE,
                               FAKE, None) == fp.FP_INVALID_ARGUMENT
-    assert l.fp_select_blocks(ctypes.byref(p), FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              None) == fp.FP_INVALID_ARGUMENT
-    assert l.fp_select_blocks(None, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              None) == fp.FP_INVALID_ARGUMENT
     # empty sequence: nothing to do, nothing launched
-    assert l.fp_select_blocks(ctypes.byref(p), None, None, None, 0, None, None, None, None, None,
+    assert l.fp_select_blocks(ctypes.byref(p), None, None, None, 0, None, None, None, None, None, None,
                               None) == fp.FP_OK
     # correction without pooled inputs
     assert l.fp_sparse_prefill_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
-                                   None, None, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
+                                   None, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
+    assert l.fp_sparse_prefill_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
+                                   MISALIGNED, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
     # fp8 without scales
     p8 = _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
     assert l.fp_sparse_prefill_fwd(ctypes.byref(p8), FAKE, FAKE, FAKE, None, None, None, 1024, FAKE, FAKE,
-                                   FAKE, FAKE, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
+                                   FAKE, FAKE, None, None) == fp.FP_INVALID_ARGUMENT
     assert "scale" in l.fp_last_error().decode()
 
 

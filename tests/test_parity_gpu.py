@@ -42,6 +42,9 @@ def test_pooled_means(shape):
     for got, x in ((sel.pooled_q, qn), (sel.pooled_k, kn), (sel.pooled_v, vn)):
         ref = O.block_means(x, B)
         np.testing.assert_allclose(got.cpu().numpy(), ref, rtol=0, atol=2e-6 * max(1.0, np.abs(ref).max()))
+    # The bf16 copies are the fp32 means rounded to nearest even, bit for bit.
+    for i, got32 in enumerate((sel.pooled_k, sel.pooled_v)):
+        assert torch.equal(sel.pooled_kv[i].cpu(), got32.cpu().to(torch.bfloat16))
 
 
 @pytest.mark.parametrize("alpha", [0.0, 0.1, 0.3, 0.5, 0.9, 1.0])
