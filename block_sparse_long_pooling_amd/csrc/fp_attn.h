@@ -185,16 +185,23 @@ __device__ __forceinline__ void softmax_update(f32x16* s, float c, float bias, f
             for (int r = 0; r < 16; ++r) o[ds][r] *= alpha;
     }
     const float off = bias - (m == -INFINITY ? 0.f : m);
+    // The row sum adds the bf16-rounded P pairs (one dot2 per pair), i.e.
+    // exactly the weights the PV product applies.
+    // Four independent partial sums keep the accumulate chain short.
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(s[sub][2 * i], c, off));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[sub][2 * i + 1], c, off));
-            l += p0 + p1;
             pk[sub][i] = pack_bf16(p0, p1);
+            part[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[sub][i]), ones, part[i & 3],
+                                                         false);
         }
     }
+    l += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // Mean-correction pass (FlashPrefill V2 abstract): every skipped block J < I

@@ -87,24 +87,28 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t*
                                            int64_t rs, int J, int nvalid, const DmaPlan<D, BLK, HP>& plan,
                                            const uint4* zero, char* lds, int wave_base) {
     using G = Geo<D, BLK, HP>;
+    using P = DmaPlan<D, BLK, HP>;
     static_assert((BLK * G::NCH) % G::NT == 0, "tile chunks must split evenly");
+    if (!PAGED) {
+        // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
+        // addressing form).
+        const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * BLK * rs);
+        // Rows past the end of the sequence re-read its last row: they occur
+        // only in the diagonal tile, where the causal mask removes them, and
+        // finite values keep 0 * v at 0.  The row index is opaque so the
+        // compiler does not keep a precomputed offset per chunk and row stride
+        // (it would spill).
 #pragma unroll
-    for (int i = 0; i < DmaPlan<D, BLK, HP>::NLOAD; ++i) {
-        const int row = plan.row(i);
-        const void* src;
-        if (!PAGED) {
-            // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
-            // addressing form).  Rows past the end of the sequence re-read its
-            // last row: they occur only in the diagonal tile, where the causal
-            // mask removes them, and finite values keep 0 * v at 0.
-            // The row index is opaque so the compiler does not keep a
-            // precomputed offset per chunk and row stride (it would spill).
-            int r = row;
+        for (int i = 0; i < P::NLOAD; ++i) {
+            int r = plan.row(i);
             asm volatile("" : "+v"(r));
-            const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * BLK * rs);
             const uint32_t off = (uint32_t)(min(r, nvalid - 1) * (int)rs + plan.coff(i)) * 2u;
-            src = tile + off;
-        } else {
+            __builtin_amdgcn_global_load_lds(tile + off, (lds_void*)(lds + (i * G::NT) * 16 + wave_base), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < P::NLOAD; ++i) {
+            const int row = plan.row(i);
             const int tr = J * BLK + row;
             const int page = pages[tr / L.page_size];
             // Opaque column offset: keeps the compiler from holding a 64-bit
@@ -112,9 +116,10 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t*
             int co = plan.coff(i);
             asm volatile("" : "+v"(co));
             const uint16_t* p = first + ((int64_t)page * L.page_size + tr % L.page_size) * rs + co;
-            src = (row < nvalid && (unsigned)page < (unsigned)L.num_pages) ? (const void*)p : (const void*)zero;
+            const void* src =
+                (row < nvalid && (unsigned)page < (unsigned)L.num_pages) ? (const void*)p : (const void*)zero;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT) * 16 + wave_base), 16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * G::NT) * 16 + wave_base), 16, 0, 0);
     }
 }
 
@@ -445,13 +450,18 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
                 constexpr int S0 = decltype(sub0)::value;
                 qk<D, BLK, HP, S0, SH>(reinterpret_cast<const uint4*>(kcur), qf, col, half, s);
                 if (corr) {
+                    // Element r of a lane in half hf is block 32 sub + (r & 3) + 8 (r >> 2) + 4 hf:
+                    // the keep mask is uniform per half, so it is built on the scalar
+                    // unit as a 64-lane mask and applied with one select.
 #pragma unroll
-                    for (int j = 0; j < SH; ++j) {
-                        const uint32_t bits = skip[S0 + j] >> (4 * half);
+                    for (int j = 0; j < SH; ++j)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            s[j][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[j][r] : -INFINITY;
-                    }
+                        for (int r = 0; r < 16; ++r) {
+                            const int k0 = (r & 3) + 8 * (r >> 2);
+                            const uint64_t keep = (((skip[S0 + j] >> k0) & 1u) ? 0xffffffffull : 0ull) |
+                                                  (((skip[S0 + j] >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+                            s[j][r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[j][r] : -INFINITY;
+                        }
                 } else if (J == cur.I) {
                     // Causal mask of the diagonal tile.  The limit is made opaque so
                     // the 16 * SH lane masks are computed here, once per item, instead
