@@ -28,7 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attn_bf16_llama8b_s128k_traffic.json")
-ATTN_SOURCES = ("k_attn.hip", "fp_attn.h", "fp_device.h", "fp_launch.h")
+ATTN_SOURCES = ("k_attn.hip", "attn_walk.h", "fp_attn.h", "fp_device.h", "fp_launch.h")
 
 
 def measured_traffic():
@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--quick", action="store_true",
                     help="headline alpha only: no sweep, no dense references, no CPU baseline")
+    ap.add_argument("--layouts", action="store_true",
+                    help="with --quick: still time the fp8 layer and the paged batch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates the HBM byte counters)")
@@ -219,6 +221,9 @@ def main():
             extra["dense_ref"]["torch_sdpa_error"] = str(ex)[:200]
         log(f"bench: dense {extra['dense_ref']}")
 
+    if not args.quick or args.layouts:
+        extra.update(other_layouts(fp, synth, q, k, v, head, stream, dev, corr))
+
     cpu = None
     if not args.quick:
         cpu = cpu_baseline(q, k, v, B, args.alpha, corr, head, args.cpu_seconds)
@@ -243,6 +248,81 @@ def main():
     }
     rec.update(extra)
     print(json.dumps(rec), flush=True)
+
+
+def timed_ms(fn, n, stream):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
+    """The two other input layouts of the path, timed beside the headline:
+    the same 128K layer in fp8 e4m3 (per (head, 128-token block) scales;
+    selection from the bf16 data, so the same lists and work as the
+    headline), and the paged continuous batch of 8 requests (selection and
+    attention in one call)."""
+    import torch
+    res = {}
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = head["p"].block_size
+    q8, qs = synth.quantize_fp8_blockwise(q, B)
+    k8, ks = synth.quantize_fp8_blockwise(k, B)
+    v8, vs = synth.quantize_fp8_blockwise(v, B)
+    q8, k8, v8, qs, ks, vs = (x.to(dev) for x in (q8, k8, v8, qs, ks, vs))
+    p8 = fp.make_params(Hq, Hkv, d, B, head["alpha"], mean_correction=corr, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    t8 = timed_ms(lambda: fp.fp_sparse_prefill_fwd(p8, q8, k8, v8, head["sel"], q_scale=qs, k_scale=ks,
+                                                   v_scale=vs, out=out), 5, stream)
+    f_alg = head["f_kept"] + head["f_corr"]
+    res["fp8"] = {"workload": "llama8b_s128k_fp8", "dtype": "fp8_e4m3", "attn_ms": round(t8, 4),
+                  "attn_tflops": round(f_alg / (t8 * 1e-3) / 1e12, 2),
+                  "frac_fp8_peak": round(f_alg / (t8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    log(f"bench: fp8 {res['fp8']}")
+    del q8, k8, v8, out
+    torch.cuda.empty_cache()
+
+    w = synth.WORKLOADS["paged_batch8"]
+    pb = synth.workload_inputs(w, keep_requests=False)
+    p = fp.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, head["alpha"],
+                       mean_correction=corr)
+    qd, kc, vc, bt = (x.to(dev) for x in (pb.q, pb.k_cache, pb.v_cache, pb.block_table))
+    r = fp.fp_sparse_prefill_varlen_paged(p, qd, kc, vc, bt, pb.cu_seqlens)
+    tv = timed_ms(lambda: fp.fp_sparse_prefill_varlen_paged(p, qd, kc, vc, bt, pb.cu_seqlens,
+                                                            workspace=r.workspace, out=r.out), 5, stream)
+    # every request length is a multiple of the block, so all blocks are full
+    cu = [int(x) for x in pb.cu_seqlens]
+    Bp, dp, Hqp = w.block_size, w.head_dim, w.num_q_heads
+    cnt = r.kv_cnt.to(torch.int64)
+    idx = r.kv_idx.to(torch.int64)
+    kept = skipped = 0
+    ioff = coff = 0
+    for b in range(len(cu) - 1):
+        nb = (cu[b + 1] - cu[b] + Bp - 1) // Bp
+        c = cnt[coff:coff + Hqp * nb].view(Hqp, nb)
+        I = torch.arange(nb, device=dev)
+        tri = nb * (nb + 1) // 2
+        base = ioff + torch.arange(Hqp, device=dev)[:, None] * tri + (I * (I + 1) // 2)[None, :]
+        diag = (idx[base + c - 1] == I[None, :]).to(torch.int64)
+        kept += int(c.sum())
+        skipped += int((I[None, :] - (c - diag)).sum())
+        ioff += Hqp * tri
+        coff += Hqp * nb
+    # kept blocks cost B keys per query row, a skipped past block one pooled entry
+    f_v = 4.0 * dp * Bp * (Bp * kept + (skipped if corr else 0))
+    res["paged"] = {"workload": w.name, "tokens": cu[-1], "requests": len(cu) - 1, "step_ms": round(tv, 4),
+                    "tokens_per_s": round(cu[-1] / (tv * 1e-3), 1), "kept_blocks": kept,
+                    "tflops": round(f_v / (tv * 1e-3) / 1e12, 2)}
+    log(f"bench: paged {res['paged']}")
+    return res
 
 
 def cpu_baseline(q, k, v, B, alpha, corr, head, seconds):
