@@ -32,13 +32,23 @@ partial last blocks average their valid tokens; the correction form (5); a
 skipped diagonal block gets no correction entry (its mean mixes future
 tokens).  fp8 inputs are judged on their dequantized values.
 
+Chunked prefill (FlashPrefill V2 abstract and the authors' post: the
+operator serves continuous batching over a paged KV cache): a call brings q_len new queries at the end of a context of kv_len
+tokens whose keys and values are all present.  Blocks are counted from the
+start of the context; the chunk starts on a block boundary (reading), so query
+block I >= first = (kv_len - q_len) / block is pooled over the chunk's tokens
+exactly as in a full prefill, sees blocks J <= I, and row i of the chunk sits
+at position kv_len - q_len + i (bottom-right causal alignment).  Under that
+reading a chunk's result equals the last q_len rows of the full prefill.
+
 Pins (tests/test_oracle.py): alpha = 0 reduces to dense causal attention
 computed by an independent routine; masks equal brute-force per-block scoring
 on tiny inputs; every probability row sums to 1; the correction equals dense
 attention in closed form when K and V are constant within blocks; constant V
 gives constant output; the argmax block is always kept and masks nest in
-alpha; GQA equals MHA with repeated K/V; a varlen batch equals its requests.
-The correction's definition itself is a reading, not a formula from the pages;
+alpha; GQA equals MHA with repeated K/V; a varlen batch equals its requests;
+a chunk equals per-token brute force written from positions, and the last
+rows of the full prefill.  The correction's definition itself is a reading, not a formula from the pages;
 only its implementation under that reading is pinned.
 """
 from __future__ import annotations
@@ -76,13 +86,21 @@ def block_means(x, block: int) -> np.ndarray:
     return out
 
 
-def block_logits(q_bar: np.ndarray, k_bar: np.ndarray, sigma: float) -> np.ndarray:
-    """s[h, I, J] = sigma * q_bar[h, I] . k_bar[h // g, J] for J <= I; -inf above."""
-    Hq, nB, _ = q_bar.shape
-    Hkv = k_bar.shape[0]
+def causal_blocks(nq: int, nB: int, first: int = 0) -> np.ndarray:
+    """[nq, nB]: query block first + i may see KV blocks J <= first + i."""
+    return np.arange(nB)[None, :] <= (first + np.arange(nq))[:, None]
+
+
+def block_logits(q_bar: np.ndarray, k_bar: np.ndarray, sigma: float, first: int = 0) -> np.ndarray:
+    """s[h, i, J] = sigma * q_bar[h, i] . k_bar[h // g, J] for J <= first + i; -inf above.
+
+    Row i is query block first + i (first = 0 for a whole sequence).
+    """
+    Hq, nq, _ = q_bar.shape
+    Hkv, nB, _ = k_bar.shape
     g = Hq // Hkv
-    causal = np.tril(np.ones((nB, nB), dtype=bool))
-    s = np.full((Hq, nB, nB), -np.inf)
+    causal = causal_blocks(nq, nB, first)
+    s = np.full((Hq, nq, nB), -np.inf)
     for h in range(Hq):
         full = sigma * (q_bar[h] @ k_bar[h // g].T)
         s[h] = np.where(causal, full, -np.inf)
@@ -96,14 +114,15 @@ def block_scores(s: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def threshold(score: np.ndarray, alpha: float) -> Tuple[np.ndarray, np.ndarray]:
+def threshold(score: np.ndarray, alpha: float, first: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """keep = Score >= alpha * max_{J<=I} Score over causal blocks.
 
     Also returns the band flags: causal blocks whose score lies within
     BAND_REL relative of the threshold (only meaningful for alpha > 0).
+    Row i is query block first + i.
     """
-    nB = score.shape[-1]
-    causal = np.tril(np.ones((nB, nB), dtype=bool))[None]
+    nq, nB = score.shape[-2:]
+    causal = causal_blocks(nq, nB, first)[None]
     thresh = alpha * score.max(axis=-1, keepdims=True)
     keep = causal & (score >= thresh)
     if alpha > 0:
@@ -116,15 +135,16 @@ def threshold(score: np.ndarray, alpha: float) -> Tuple[np.ndarray, np.ndarray]:
 class Selection:
     """Everything the selection step produces for one sequence."""
 
-    def __init__(self, q_bar, k_bar, v_bar, s, score, keep, band, block):
+    def __init__(self, q_bar, k_bar, v_bar, s, score, keep, band, block, first=0):
         self.q_bar, self.k_bar, self.v_bar = q_bar, k_bar, v_bar
         self.s, self.score, self.keep, self.band = s, score, keep, band
         self.block = block
+        self.first = first     # query block of row 0 (chunked prefill), else 0
 
     def lists(self) -> List[List[np.ndarray]]:
-        """Kept KV blocks per (query head, query block), ascending."""
-        Hq, nB, _ = self.keep.shape
-        return [[np.flatnonzero(self.keep[h, I, :I + 1]) for I in range(nB)]
+        """Kept KV blocks per (query head, query block row), ascending."""
+        Hq, nq, _ = self.keep.shape
+        return [[np.flatnonzero(self.keep[h, i, :self.first + i + 1]) for i in range(nq)]
                 for h in range(Hq)]
 
 
@@ -147,17 +167,19 @@ def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = No
 
 
 def block_entries(q, k, v, keep_row: np.ndarray, h: int, I: int, block: int, sigma: float,
-                  g: int, correction: bool, k_bar=None, v_bar=None):
+                  g: int, correction: bool, k_bar=None, v_bar=None, q_offset: int = 0):
     """Logits z [n_I, n_entries] and values [n_entries, d] for query block I of head h.
 
     Entries: the tokens of every kept block J <= I (token j masked to -inf for
     rows i < j), then, with the correction, one pooled entry per skipped J < I.
+    Positions count from the start of the keys; q row r holds position
+    r + q_offset (q_offset > 0 for a chunk at the end of a longer context).
     """
-    S = q.shape[0]
+    S = k.shape[0]
     hk = h // g
     r0, r1 = I * block, min(S, (I + 1) * block)
     rows = np.arange(r0, r1)
-    q_i = _f64(q[r0:r1, h])                                    # [n_I, d]
+    q_i = _f64(q[r0 - q_offset:r1 - q_offset, h])              # [n_I, d]
     kept = [J for J in range(I + 1) if keep_row[J]]
     if kept:
         tok = np.concatenate([np.arange(J * block, min(S, (J + 1) * block)) for J in kept])
@@ -211,6 +233,62 @@ def sparse_attention(q, k, v, sel: Selection, correction: bool, sigma: Optional[
         r0, r1 = I * block, min(S, (I + 1) * block)
         o[r0:r1, h] = (w @ vals) / l[:, None]
         lse[h, r0:r1] = M + np.log(l)
+    return o, lse
+
+
+def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
+                          pool_v: bool = True) -> Selection:
+    """Pooling, block scores and thresholding for a chunk of new queries.
+
+    q [q_len, Hq, d] are the last q_len tokens of a context whose keys and
+    values are k, v [kv_len, Hkv, d].  kv_len - q_len must be a multiple of
+    ``block``.  Row i of the result is query block first + i, first =
+    (kv_len - q_len) / block; keys are pooled over the whole context.
+    """
+    q_len, kv_len = q.shape[0], k.shape[0]
+    if not 0 <= q_len <= kv_len:
+        raise ValueError(f"chunk of {q_len} queries for a context of {kv_len} tokens")
+    if (kv_len - q_len) % block:
+        raise ValueError("the chunk must start on a block boundary")
+    d = q.shape[-1]
+    if sigma is None:
+        sigma = 1.0 / math.sqrt(d)
+    first = (kv_len - q_len) // block
+    q_bar = block_means(q, block)          # the chunk's blocks are the context's blocks first, first+1, ...
+    k_bar = block_means(k, block)
+    v_bar = block_means(v, block) if pool_v else None
+    s = block_logits(q_bar, k_bar, sigma, first)
+    score = block_scores(s)
+    keep, band = threshold(score, alpha, first)
+    return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block, first)
+
+
+def sparse_attention_chunked(q, k, v, sel: Selection, correction: bool, sigma: Optional[float] = None,
+                             keep: Optional[np.ndarray] = None):
+    """Attention of a chunk (see select_blocks_chunked): o [q_len, Hq, d], lse [Hq, q_len].
+
+    Row r of the chunk is position kv_len - q_len + r and sees every key at or
+    before it in the kept blocks, plus the correction entries.
+    """
+    q_len, Hq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    block = sel.block
+    if sigma is None:
+        sigma = 1.0 / math.sqrt(d)
+    keep = sel.keep if keep is None else keep
+    P0 = k.shape[0] - q_len
+    o = np.full((q_len, Hq, d), np.nan)
+    lse = np.full((Hq, q_len), np.nan)
+    for h in range(Hq):
+        for i in range(keep.shape[1]):
+            I = sel.first + i
+            z, vals = block_entries(q, k, v, keep[h, i], h, I, block, sigma, g, correction,
+                                    sel.k_bar, sel.v_bar, q_offset=P0)
+            M, w, l = softmax_rows(z)
+            r0, r1 = I * block - P0, min(k.shape[0], (I + 1) * block) - P0
+            o[r0:r1, h] = (w @ vals) / l[:, None]
+            lse[h, r0:r1] = M + np.log(l)
     return o, lse
 
 

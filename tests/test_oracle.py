@@ -326,3 +326,116 @@ def test_dequantize_blockwise_elementwise():
     for t in range(70):
         for h in range(3):
             assert np.allclose(x[t, h], x8[t, h] * sc[h, t // 32], rtol=0, atol=0)
+
+
+# ----------------------------------------------------------- chunked prefill
+
+def _brute_force_chunk(qc, k, v, B, alpha, corr):
+    """A chunk of new queries at the end of a context, written from token
+    positions with Python loops: query row r is position P0 + r and sees the
+    keys at or before it in the kept blocks, plus one pooled entry per skipped
+    past block (n_J copies of its mean key and value)."""
+    q_len, Hq, d = qc.shape
+    S, Hkv, _ = k.shape
+    g = Hq // Hkv
+    P0 = S - q_len
+    sig = 1.0 / math.sqrt(d)
+    nB = (S + B - 1) // B
+
+    def mean(x, rows, h):
+        return [math.fsum(float(x[t, h, c]) for t in rows) / len(rows) for c in range(d)]
+
+    def dot(a, b):
+        return math.fsum(x * y for x, y in zip(a, b))
+
+    o = np.zeros((q_len, Hq, d))
+    lse = np.zeros((Hq, q_len))
+    keep_rows = {}
+    for h in range(Hq):
+        hk = h // g
+        kb = [mean(k, range(J * B, min(S, J * B + B)), hk) for J in range(nB)]
+        vb = [mean(v, range(J * B, min(S, J * B + B)), hk) for J in range(nB)]
+        for I in range(P0 // B, nB):
+            qb = mean(qc, range(I * B - P0, min(S, I * B + B) - P0), h)
+            s = [sig * dot(qb, kb[J]) for J in range(I + 1)]
+            m = max(s)
+            den = math.fsum(math.exp(x - m) for x in s)
+            score = [math.exp(x - m) / den for x in s]
+            keep = [score[J] >= alpha * max(score) for J in range(I + 1)]
+            keep_rows[h, I] = keep
+            for p in range(I * B, min(S, I * B + B)):
+                qr = [float(x) for x in qc[p - P0, h]]
+                z, vals = [], []
+                for J in range(I + 1):
+                    if keep[J]:
+                        for t in range(J * B, min(S, J * B + B)):
+                            if t <= p:
+                                z.append(sig * dot(qr, k[t, hk]))
+                                vals.append([float(x) for x in v[t, hk]])
+                    elif corr and J < I:
+                        n = min(S, J * B + B) - J * B
+                        z.append(sig * dot(qr, kb[J]) + math.log(n))
+                        vals.append(vb[J])
+                M = max(z)
+                w = [math.exp(x - M) for x in z]
+                l = math.fsum(w)
+                for c in range(d):
+                    o[p - P0, h, c] = math.fsum(wi * vi[c] for wi, vi in zip(w, vals)) / l
+                lse[h, p - P0] = M + math.log(l)
+    return o, lse, keep_rows
+
+
+@pytest.mark.parametrize("P0", [0, 8, 24])
+@pytest.mark.parametrize("corr", [False, True])
+def test_chunk_matches_brute_force(P0, corr):
+    q, k, v = _rand_qkv(45, 2, 1, 4, seed=11 + P0, scale=3.0)
+    qc = q[P0:]
+    alpha = 0.5
+    sel = O.select_blocks_chunked(qc, k, v, 8, alpha)
+    assert sel.first == P0 // 8 and sel.keep.shape == (2, 6 - P0 // 8, 6)
+    o, lse = O.sparse_attention_chunked(qc, k, v, sel, corr)
+    o_bf, lse_bf, keep_bf = _brute_force_chunk(qc, k, v, 8, alpha, corr)
+    for (h, I), keep in keep_bf.items():
+        i = I - sel.first
+        row = sel.keep[h, i, :I + 1]
+        outside = ~sel.band[h, i, :I + 1]
+        assert np.array_equal(row[outside], np.array(keep)[outside])
+        assert not sel.keep[h, i, I + 1:].any()
+    if not sel.band.any():
+        np.testing.assert_allclose(o, o_bf, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse, lse_bf, atol=1e-12, rtol=0)
+    # something is skipped, so the correction entries are exercised
+    assert (~sel.keep & O.causal_blocks(sel.keep.shape[1], 6, sel.first)[None]).any()
+
+
+@pytest.mark.parametrize("P0", [0, 32, 64, 96])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 3)])
+def test_chunk_equals_last_rows_of_full_prefill(P0, Hq, Hkv):
+    S, B = 133, 32
+    q, k, v = _rand_qkv(S, Hq, Hkv, 8, seed=P0 + Hq, scale=1.3)
+    full = O.select_blocks(q, k, v, B, 0.2)
+    o_f, lse_f = O.sparse_attention(q, k, v, full, correction=True)
+    sel = O.select_blocks_chunked(q[P0:], k, v, B, 0.2)
+    o_c, lse_c = O.sparse_attention_chunked(q[P0:], k, v, sel, correction=True)
+    assert np.array_equal(sel.keep, full.keep[:, P0 // B:, :])
+    np.testing.assert_allclose(o_c, o_f[P0:], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse_c, lse_f[:, P0:], atol=1e-12, rtol=0)
+    lists = sel.lists()
+    assert all(list(lists[h][i]) == list(full.lists()[h][i + P0 // B]) for h in range(Hq)
+               for i in range(len(lists[h])))
+
+
+def test_chunk_rejects_unaligned_or_too_long():
+    q, k, v = _rand_qkv(40, 2, 1, 4, seed=5)
+    with pytest.raises(ValueError):
+        O.select_blocks_chunked(q[3:], k, v, 8, 0.1)
+    with pytest.raises(ValueError):
+        O.select_blocks_chunked(np.concatenate([q, q[:8]]), k, v, 8, 0.1)
+
+
+def test_empty_chunk():
+    q, k, v = _rand_qkv(40, 2, 1, 4, seed=6)
+    sel = O.select_blocks_chunked(q[40:], k, v, 8, 0.1)
+    assert sel.keep.shape == (2, 0, 5)
+    o, lse = O.sparse_attention_chunked(q[40:], k, v, sel, True)
+    assert o.shape == (0, 2, 4) and lse.shape == (2, 0)
