@@ -51,6 +51,13 @@ EXPORTS = {
                                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                       _I32P, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P, _P, _P]),
+    "fp_sparse_prefill_chunked_paged": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
+                                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                       _I32P, _I32P, ctypes.c_int32, _P, ctypes.c_int32,
+                                                       _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "fp_chunked_sizes": (ctypes.c_int, [ctypes.POINTER(fp_params), _I32P, _I32P, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_size_t)]),
     "fp_index_capacity": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
     "fp_count_entries": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
     "fp_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
@@ -214,6 +221,51 @@ def fp_sparse_prefill_varlen_paged(params: fp_params, q: torch.Tensor, k_cache: 
         ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
         _ptr(block_table), block_table.shape[1], cu, batch, _ptr(kv_idx), _ptr(kv_cnt),
         _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
+
+
+def fp_chunked_sizes(params: fp_params, cu_seqlens_q: Sequence[int], kv_lens: Sequence[int]):
+    """(kv_idx entries, kv_cnt entries, workspace bytes) for fp_sparse_prefill_chunked_paged."""
+    cu = _cu_host(cu_seqlens_q)
+    kl = _cu_host(kv_lens)
+    cap, cnt, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib().fp_chunked_sizes(ctypes.byref(params), cu, kl, len(cu) - 1, ctypes.byref(cap),
+                                  ctypes.byref(cnt), ctypes.byref(ws)))
+    return int(cap.value), int(cnt.value), int(ws.value)
+
+
+def alloc_pooled_cache(params: fp_params, num_pages: int, device) -> torch.Tensor:
+    """fp32 [2, num_pages, Hkv, d]: the pooled-means cache kept between chunked calls."""
+    return torch.zeros((2, num_pages, params.num_kv_heads, params.head_dim), dtype=torch.float32,
+                       device=device)
+
+
+def fp_sparse_prefill_chunked_paged(params: fp_params, q: torch.Tensor, k_cache: torch.Tensor,
+                                    v_cache: torch.Tensor, block_table: torch.Tensor, cu_seqlens_q,
+                                    kv_lens, pooled_cache: Optional[torch.Tensor] = None,
+                                    prefix_pooled: bool = False, return_lse: bool = False,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    out: Optional[torch.Tensor] = None) -> VarlenResult:
+    """Chunked prefill over a paged KV cache (bf16): request b's q rows are the
+    last q_len of its kv_lens[b]-token context; selection + attention."""
+    T, Hq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    dev = q.device
+    cu = _cu_host(cu_seqlens_q)
+    kl = _cu_host(kv_lens)
+    batch = len(cu) - 1
+    cap, ncnt, wsb = fp_chunked_sizes(params, list(cu), list(kl))
+    kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty(max(ncnt, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().fp_sparse_prefill_chunked_paged(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
+        _ptr(block_table), block_table.shape[1], cu, kl, batch, _ptr(pooled_cache), int(bool(prefix_pooled)),
+        _ptr(kv_idx), _ptr(kv_cnt), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
     return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
 
 

@@ -226,19 +226,19 @@ struct Item {
         int local;
         item_of(t, rank, b, local);
         nb = seq_blocks(t, b);
+        const int first = first_block(t, b);          // query blocks are first .. nb-1
         I = nb - 1 - local;
         tok0 = t.tok_off[b];
-        len = t.tok_off[b + 1] - tok0;
-        q0 = tok0 + I * BLK;
+        len = context_len(t, b, BLK);
+        q0 = tok0 + (I - first) * BLK;
         nI = min(BLK, len - I * BLK);
         hk = h / a.g;
         const int64_t rs = (int64_t)a.Hkv * D;
-        const int64_t tri = (int64_t)nb * (nb + 1) / 2;
         const int h0 = h - hs;
 #pragma unroll
         for (int j = 0; j < HP; ++j) {
-            u.list[j] = a.kv_idx + t.idx_off[b] + (int64_t)(h0 + j) * tri + (int64_t)I * (I + 1) / 2;
-            u.cnt[j] = __builtin_amdgcn_readfirstlane(a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)(h0 + j) * nb + I]);
+            u.list[j] = a.kv_idx + list_row(t, b, h0 + j, I, nb, first);
+            u.cnt[j] = __builtin_amdgcn_readfirstlane(a.kv_cnt[count_index(t, a.Hq, b, h0 + j, I, nb, first)]);
         }
         u.cap = I + 1;
         u.init();

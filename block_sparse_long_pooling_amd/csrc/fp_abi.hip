@@ -68,9 +68,12 @@ float sigma_of(const fp_params& p) {
     return p.softmax_scale > 0.f ? p.softmax_scale : (float)(1.0 / std::sqrt((double)p.head_dim));
 }
 
-// Validate cu_seqlens_host and fill the request table.  items_per_tile = 1
-// counts query blocks; TI counts tiles of TI query blocks (selection).
-int build_table(const fp_params& p, const int32_t* cu, int32_t batch, int items_per_tile, SeqTable& t) {
+// Validate cu_seqlens_host (query tokens per request) and, for chunked
+// prefill, kv_lens_host (context length per request; NULL: equal to the query
+// count), and fill the request table.  items_per_tile = 1 counts query
+// blocks; TI counts tiles of TI query blocks (selection).
+int build_table(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, int items_per_tile,
+                SeqTable& t) {
     if (!cu) return fail(FP_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
     if (batch < 1) return fail(FP_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
     if (batch > FP_MAX_BATCH) return fail(FP_UNSUPPORTED, "batch %d exceeds %d", batch, FP_MAX_BATCH);
@@ -78,36 +81,49 @@ int build_table(const fp_params& p, const int32_t* cu, int32_t batch, int items_
     const int B = p.block_size;
     std::memset(&t, 0, sizeof t);
     t.batch = batch;
-    int64_t blocks = 0, idx = 0;
+    int64_t blocks = 0, pre = 0, idx = 0;
+    std::vector<int64_t> ctx(batch);
     for (int b = 0; b < batch; ++b) {
         if (cu[b + 1] < cu[b]) return fail(FP_INVALID_ARGUMENT, "cu_seqlens not non-decreasing at %d", b + 1);
-        const int64_t len = (int64_t)cu[b + 1] - cu[b];
+        const int64_t qlen = (int64_t)cu[b + 1] - cu[b];
+        const int64_t len = kv_lens ? (int64_t)kv_lens[b] : qlen;
+        if (len < qlen)
+            return fail(FP_INVALID_ARGUMENT, "request %d: %lld queries exceed its context of %lld tokens", b,
+                        (long long)qlen, (long long)len);
+        if ((len - qlen) % B != 0)
+            return fail(FP_UNSUPPORTED, "request %d: the chunk starts at token %lld, not on a block boundary (%d)", b,
+                        (long long)(len - qlen), B);
         const int64_t nb = (len + B - 1) / B;
+        const int64_t first = (len - qlen) / B;
         if (nb > FP_MAX_BLOCKS / 2)
             return fail(FP_UNSUPPORTED, "request %d has %lld blocks (max %d)", b, (long long)nb, FP_MAX_BLOCKS / 2);
+        ctx[b] = len;
         t.tok_off[b] = cu[b];
         t.blk_off[b] = (int32_t)blocks;
+        t.pre_off[b] = (int32_t)pre;
         t.idx_off[b] = idx;
+        t.tail[b] = (int16_t)(nb > 0 ? len - (nb - 1) * B : 0);
         blocks += nb;
-        idx += (int64_t)p.num_q_heads * tri(nb);
+        pre += first;
+        idx += (int64_t)p.num_q_heads * (tri(nb) - tri(first));
     }
     t.tok_off[batch] = cu[batch];
     t.blk_off[batch] = (int32_t)blocks;
+    t.pre_off[batch] = (int32_t)pre;
     t.idx_off[batch] = idx;
     t.total_tokens = cu[batch];
     t.total_blocks = (int32_t)blocks;
+    t.total_qblocks = (int32_t)(blocks - pre);
     std::vector<int> ord(batch);
     for (int b = 0; b < batch; ++b) ord[b] = b;
-    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) {
-        return (cu[x + 1] - cu[x]) > (cu[y + 1] - cu[y]);
-    });
+    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return ctx[x] > ctx[y]; });
     int64_t items = 0;
     for (int s = 0; s < batch; ++s) {
         const int b = ord[s];
-        const int nb = t.blk_off[b + 1] - t.blk_off[b];
-        t.order[s] = b;
+        const int nq = (t.blk_off[b + 1] - t.blk_off[b]) - (t.pre_off[b + 1] - t.pre_off[b]);
+        t.order[s] = (int16_t)b;
         t.item_off[s] = (int32_t)items;
-        items += (nb + items_per_tile - 1) / items_per_tile;
+        items += (nq + items_per_tile - 1) / items_per_tile;
     }
     t.item_off[batch] = (int32_t)items;
     t.total_items = (int32_t)items;
@@ -123,17 +139,22 @@ int device_status(hipError_t e, const char* what) {
 
 int select_tile(const fp_params& p) { return 32 / (p.num_q_heads / p.num_kv_heads); }
 
-int run_select(const fp_params& p, const int32_t* cu, int32_t batch, const void* q, const void* k, const void* v,
-               const KVLayout& kv, bool paged, float* pq, float* pk, float* pv, uint16_t* pkv16,
-               int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
+// Pooling and selection.  kv_lens: context lengths (chunked prefill) or NULL;
+// pcache: the caller's pooled cache (chunked prefill) or NULL; reuse: read
+// the prefix blocks' means from it instead of pooling them.
+int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const void* q,
+               const void* k, const void* v, const KVLayout& kv, bool paged, float* pq, float* pk, float* pv,
+               uint16_t* pkv16, float* pcache, int reuse, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
     SeqTable t;
-    int rc = build_table(p, cu, batch, 1, t);
+    int rc = build_table(p, cu, kv_lens, batch, 1, t);
     if (rc) return rc;
     PoolArgs pa;
     pa.q = static_cast<const uint16_t*>(q);
     pa.k = static_cast<const uint16_t*>(k);
-    const bool pool_v = pv || pkv16;
+    const bool pool_v = pv || pkv16 || pcache;
     pa.v = pool_v ? static_cast<const uint16_t*>(v) : nullptr;
+    pa.pcache = pcache;
+    pa.reuse = reuse;
     pa.pq = pq;
     pa.pk = pk;
     pa.pv = pv;
@@ -151,7 +172,7 @@ int run_select(const fp_params& p, const int32_t* cu, int32_t batch, const void*
 
     SeqTable ts;
     const int TI = select_tile(p);
-    rc = build_table(p, cu, batch, TI, ts);
+    rc = build_table(p, cu, kv_lens, batch, TI, ts);
     if (rc) return rc;
     SelArgs sa;
     sa.pq = pq;
@@ -185,14 +206,14 @@ FP_EXPORT const char* fp_last_error(void) { return g_last_error.c_str(); }
 
 FP_EXPORT int64_t fp_index_capacity(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
     SeqTable t;
-    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return -1;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, nullptr, batch, 1, t)) return -1;
     return t.idx_off[batch];
 }
 
 FP_EXPORT int64_t fp_count_entries(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
     SeqTable t;
-    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return -1;
-    return (int64_t)params->num_q_heads * t.total_blocks;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, nullptr, batch, 1, t)) return -1;
+    return (int64_t)params->num_q_heads * t.total_qblocks;
 }
 
 namespace {
@@ -200,11 +221,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WsLayout {
     size_t q, k, kv16, total;   // fp32 Q_bar, fp32 K_bar, bf16 K_bar | V_bar
 };
-WsLayout ws_layout(const fp_params& p, int64_t total_blocks) {
+WsLayout ws_layout(const fp_params& p, const SeqTable& t) {
     WsLayout w;
-    const size_t per = (size_t)total_blocks * p.head_dim;
+    const size_t per = (size_t)t.total_blocks * p.head_dim;
     w.q = 0;
-    w.k = align256(per * p.num_q_heads * sizeof(float));
+    w.k = align256((size_t)t.total_qblocks * p.head_dim * p.num_q_heads * sizeof(float));
     w.kv16 = w.k + align256(per * p.num_kv_heads * sizeof(float));
     w.total = w.kv16 + (p.mean_correction ? align256(2 * per * p.num_kv_heads * sizeof(uint16_t)) : 0);
     return w;
@@ -213,8 +234,8 @@ WsLayout ws_layout(const fp_params& p, int64_t total_blocks) {
 
 FP_EXPORT size_t fp_varlen_workspace_bytes(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {
     SeqTable t;
-    if (check_params(params) || build_table(*params, cu_seqlens_host, batch, 1, t)) return 0;
-    return ws_layout(*params, t.total_blocks).total;
+    if (check_params(params) || build_table(*params, cu_seqlens_host, nullptr, batch, 1, t)) return 0;
+    return ws_layout(*params, t).total;
 }
 
 FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const void* k, const void* v, int32_t seqlen,
@@ -236,8 +257,9 @@ FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const voi
     const int32_t cu[2] = {0, seqlen};
     KVLayout kv = {nullptr, 1, 0, 0};
     (void)hipGetLastError();
-    rc = run_select(*params, cu, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v,
-                    static_cast<uint16_t*>(pooled_kv_bf16), kv_idx, kv_cnt, static_cast<hipStream_t>(stream));
+    rc = run_select(*params, cu, nullptr, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v,
+                    static_cast<uint16_t*>(pooled_kv_bf16), nullptr, 0, kv_idx, kv_cnt,
+                    static_cast<hipStream_t>(stream));
     return rc ? rc : ok();
 }
 
@@ -262,7 +284,7 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
         return fail(FP_INVALID_ARGUMENT, "fp8 inputs need q_scale, k_scale and v_scale");
     const int32_t cu[2] = {0, seqlen};
     SeqTable t;
-    rc = build_table(p, cu, 1, 1, t);
+    rc = build_table(p, cu, nullptr, 1, 1, t);
     if (rc) return rc;
     AttnArgs a;
     a.q = q;
@@ -290,24 +312,27 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
     return rc ? rc : ok();
 }
 
-FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q, const void* k_cache,
-                                             const void* v_cache, int32_t page_size, int32_t num_pages,
-                                             const int32_t* block_table, int32_t max_pages_per_seq,
-                                             const int32_t* cu_seqlens_host, int32_t batch,
-                                             int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
-                                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+namespace {
+// The paged entries: pooling, selection and attention of a continuous batch.
+// kv_lens NULL: whole prompts; else context lengths (chunked prefill), with
+// the pooled cache pcache (may be NULL) and its reuse flag.
+int paged_prefill(const fp_params* params, const void* q, const void* k_cache, const void* v_cache, int32_t page_size,
+                  int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_q,
+                  const int32_t* kv_lens, int32_t batch, float* pcache, int32_t reuse, int32_t* kv_idx,
+                  int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
     int rc = check_params(params);
     if (rc) return rc;
     const fp_params& p = *params;
-    if (p.dtype != FP_DTYPE_BF16) return fail(FP_UNSUPPORTED, "the paged entry reads bf16 only");
+    if (p.dtype != FP_DTYPE_BF16) return fail(FP_UNSUPPORTED, "the paged entries read bf16 only");
     SeqTable t;
-    rc = build_table(p, cu_seqlens_host, batch, 1, t);
+    rc = build_table(p, cu_q, kv_lens, batch, 1, t);
     if (rc) return rc;
     if (page_size < 1 || p.block_size % page_size != 0)
         return fail(FP_INVALID_ARGUMENT, "page_size (%d) must divide block_size (%d)", page_size, p.block_size);
     if (num_pages < 1) return fail(FP_INVALID_ARGUMENT, "num_pages must be >= 1");
     for (int b = 0; b < batch; ++b) {
-        const int64_t need = ((int64_t)cu_seqlens_host[b + 1] - cu_seqlens_host[b] + page_size - 1) / page_size;
+        const int64_t len = kv_lens ? (int64_t)kv_lens[b] : (int64_t)cu_q[b + 1] - cu_q[b];
+        const int64_t need = (len + page_size - 1) / page_size;
         if (need > max_pages_per_seq)
             return fail(FP_INVALID_ARGUMENT, "request %d needs %lld pages > max_pages_per_seq %d", b,
                         (long long)need, max_pages_per_seq);
@@ -318,7 +343,8 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     if (!aligned(block_table, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
         return fail(FP_INVALID_ARGUMENT, "block_table, kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
-    const WsLayout ws = ws_layout(p, t.total_blocks);
+    if (pcache && !aligned(pcache, 16)) return fail(FP_INVALID_ARGUMENT, "pooled_cache must be 16-byte aligned");
+    const WsLayout ws = ws_layout(p, t);
     if (!aligned(workspace, 256)) return fail(FP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (workspace_bytes < ws.total)
         return fail(FP_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", workspace_bytes, ws.total);
@@ -329,8 +355,8 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = run_select(p, cu_seqlens_host, batch, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, kv_idx, kv_cnt,
-                    st);
+    rc = run_select(p, cu_q, kv_lens, batch, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, pcache, reuse,
+                    kv_idx, kv_cnt, st);
     if (rc) return rc;
     AttnArgs a;
     a.q = q;
@@ -351,4 +377,46 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     a.correction = p.mean_correction;
     rc = device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, true, st), "attention (paged)");
     return rc ? rc : ok();
+}
+}  // namespace
+
+FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q, const void* k_cache,
+                                             const void* v_cache, int32_t page_size, int32_t num_pages,
+                                             const int32_t* block_table, int32_t max_pages_per_seq,
+                                             const int32_t* cu_seqlens_host, int32_t batch,
+                                             int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+    return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
+                         cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, workspace, workspace_bytes, out,
+                         lse, stream);
+}
+
+FP_EXPORT int fp_chunked_sizes(const fp_params* params, const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                               int32_t batch, int64_t* index_capacity, int64_t* count_entries,
+                               size_t* workspace_bytes) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (!kv_lens_host) return fail(FP_INVALID_ARGUMENT, "kv_lens_host is NULL");
+    SeqTable t;
+    rc = build_table(*params, cu_seqlens_q_host, kv_lens_host, batch, 1, t);
+    if (rc) return rc;
+    if (index_capacity) *index_capacity = t.idx_off[batch];
+    if (count_entries) *count_entries = (int64_t)params->num_q_heads * t.total_qblocks;
+    if (workspace_bytes) *workspace_bytes = ws_layout(*params, t).total;
+    return ok();
+}
+
+FP_EXPORT int fp_sparse_prefill_chunked_paged(const fp_params* params, const void* q, const void* k_cache,
+                                              const void* v_cache, int32_t page_size, int32_t num_pages,
+                                              const int32_t* block_table, int32_t max_pages_per_seq,
+                                              const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                              int32_t batch, float* pooled_cache, int32_t prefix_pooled,
+                                              int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                                              size_t workspace_bytes, void* out, float* lse, void* stream) {
+    if (!kv_lens_host) return fail(FP_INVALID_ARGUMENT, "kv_lens_host is NULL");
+    if (prefix_pooled != 0 && prefix_pooled != 1) return fail(FP_INVALID_ARGUMENT, "prefix_pooled must be 0 or 1");
+    if (prefix_pooled && !pooled_cache) return fail(FP_INVALID_ARGUMENT, "prefix_pooled needs a pooled_cache");
+    return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
+                         cu_seqlens_q_host, kv_lens_host, batch, pooled_cache, prefix_pooled, kv_idx, kv_cnt,
+                         workspace, workspace_bytes, out, lse, stream);
 }

@@ -13,23 +13,48 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 // Requests of one launch and the order in which workgroups visit them.
-// Work items of request b are counted by the launch (query blocks, query
-// block tiles, ...); sorted position s holds request order[s], longest first,
-// and its items start at rank item_off[s].  A single sequence is batch = 1.
+// Request b has a context of kv_len tokens, counted in KV blocks from its
+// start; its queries in this call are the last q_len of them (chunked
+// prefill; q_len = kv_len for a whole prompt) and start on a block boundary,
+// so query blocks are KV blocks first .. nb-1 with first = (kv_len-q_len)/B.
+// Work items of request b are counted by the launch over its query blocks
+// (query blocks, query block tiles, ...); sorted position s holds request
+// order[s], longest context first, and its items start at rank item_off[s].
+// Lists and counts are stored for query blocks only:
+//   kv_idx row (h, I): idx_off[b] + h (tri(nb) - tri(first)) + tri(I) - tri(first)
+//   kv_cnt (h, I):     Hq (blk_off[b] - pre_off[b]) + h (nb - first) + I - first
+// with tri(n) = n (n + 1) / 2.  A single sequence is batch = 1, first = 0.
 struct SeqTable {
     int64_t idx_off[FP_TABLE_MAX + 1];   // start of request b's kv_idx region
-    int32_t tok_off[FP_TABLE_MAX + 1];   // cu_seqlens
-    int32_t blk_off[FP_TABLE_MAX + 1];   // cumulative query blocks
-    int32_t order[FP_TABLE_MAX];
+    int32_t tok_off[FP_TABLE_MAX + 1];   // query token offsets (cu_seqlens of the queries)
+    int32_t blk_off[FP_TABLE_MAX + 1];   // cumulative KV blocks
+    int32_t pre_off[FP_TABLE_MAX + 1];   // cumulative prefix blocks (KV blocks without queries)
     int32_t item_off[FP_TABLE_MAX + 1];
+    int16_t order[FP_TABLE_MAX];
+    int16_t tail[FP_TABLE_MAX];          // tokens in request b's last KV block (1 .. B)
     int32_t batch;
-    int32_t total_tokens;
-    int32_t total_blocks;
+    int32_t total_tokens;                // query tokens
+    int32_t total_blocks;                // KV blocks
+    int32_t total_qblocks;               // query blocks (total_blocks - pre_off[batch])
     int32_t total_items;
 };
 
-__device__ __forceinline__ int seq_len(const SeqTable& t, int b) { return t.tok_off[b + 1] - t.tok_off[b]; }
 __device__ __forceinline__ int seq_blocks(const SeqTable& t, int b) { return t.blk_off[b + 1] - t.blk_off[b]; }
+__device__ __forceinline__ int first_block(const SeqTable& t, int b) { return t.pre_off[b + 1] - t.pre_off[b]; }
+__device__ __forceinline__ int context_len(const SeqTable& t, int b, int B) {
+    const int nb = seq_blocks(t, b);
+    return nb > 0 ? (nb - 1) * B + t.tail[b] : 0;
+}
+__device__ __forceinline__ int64_t tri64(int n) { return (int64_t)n * (n + 1) / 2; }
+// Start of the kv_idx row of (query head h, query block I); capacity I + 1.
+__device__ __forceinline__ int64_t list_row(const SeqTable& t, int b, int h, int I, int nb, int first) {
+    return t.idx_off[b] + (int64_t)h * (tri64(nb) - tri64(first)) + tri64(I) - tri64(first);
+}
+__device__ __forceinline__ int64_t count_index(const SeqTable& t, int Hq, int b, int h, int I, int nb, int first) {
+    return (int64_t)Hq * (t.blk_off[b] - t.pre_off[b]) + (int64_t)h * (nb - first) + (I - first);
+}
+// Row of query block I of request b among all query blocks of the launch.
+__device__ __forceinline__ int qblock_row(const SeqTable& t, int b, int I) { return t.blk_off[b] - t.pre_off[b + 1] + I; }
 
 // Rank (in visiting order) -> (request, item index counted from the request's
 // last item, so that long rows go first).

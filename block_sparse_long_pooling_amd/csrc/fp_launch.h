@@ -9,10 +9,12 @@ struct PoolArgs {
     const uint16_t* q;   // bf16 [T, Hq, d]
     const uint16_t* k;   // bf16 rows (contiguous or paged)
     const uint16_t* v;   // may be null (then not pooled)
-    float* pq;           // [Hq, total_blocks, d]
+    float* pq;           // [Hq, total_qblocks, d]
     float* pk;           // [Hkv, total_blocks, d]
     float* pv;           // [Hkv, total_blocks, d] or null
     uint16_t* pkv16;     // bf16 [2, Hkv, total_blocks, d] (K_bar then V_bar) or null
+    float* pcache;       // fp32 [2, num_pages, Hkv, d] by the page of a block's first token, or null
+    int32_t reuse;       // prefix blocks: read their means from pcache instead of pooling
     KVLayout kv;
     int32_t Hq, Hkv, D, B;
     int32_t q_chunks;    // Hq * d / 8

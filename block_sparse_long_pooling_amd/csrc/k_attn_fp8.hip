@@ -193,16 +193,15 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     const int h = xcd_head(blockIdx.x % a.Hq, a.Hq);
     int b, local;
     item_of(t, rank, b, local);
-    const int nb = seq_blocks(t, b);
+    const int nb = seq_blocks(t, b);                   // whole sequences only: no prefix blocks
     const int I = nb - 1 - local;
     const int tok0 = t.tok_off[b];
-    const int len = t.tok_off[b + 1] - tok0;
+    const int len = context_len(t, b, BLK);
     const int q0 = tok0 + I * BLK;
     const int nI = min(BLK, len - I * BLK);
     const int hk = h / a.g;
-    const int32_t* list = a.kv_idx + t.idx_off[b] + (int64_t)h * ((int64_t)nb * (nb + 1) / 2) +
-                          (int64_t)I * (I + 1) / 2;
-    const int cnt = a.kv_cnt[(int64_t)a.Hq * t.blk_off[b] + (int64_t)h * nb + I];
+    const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, 0);
+    const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, 0)];
     const int qr = 32 * w + col;
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
     const uint8_t* k8 = static_cast<const uint8_t*>(a.k);

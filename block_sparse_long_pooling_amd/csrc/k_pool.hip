@@ -4,7 +4,12 @@
 // K_bar and V_bar are also written rounded to bf16, the form in which the
 // attention kernels consume them.
 //
-// One workgroup covers one query block of one request and 256 column chunks
+// In chunked prefill the prefix blocks have no queries in the call; their
+// K_bar / V_bar are pooled from the cache pages or, when an earlier call
+// pooled them, read from the caller's pooled cache (one fp32 entry per page
+// that starts a block), and every block pooled here is written back to it.
+//
+// One workgroup covers one KV block of one request and 256 column chunks
 // of 8 bf16 (16 bytes) taken from the concatenated row [Q | K | V].  Each
 // thread walks the block's tokens, so a wave reads 1 KiB contiguous per
 // token step; the token loop is unrolled 8 deep so that every thread keeps 8
@@ -30,21 +35,20 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
     if (c >= a.total_chunks) return;
     const int b = request_of_block(t, gb);
     const int I = gb - t.blk_off[b];
-    const int tok0 = t.tok_off[b];
-    const int len = t.tok_off[b + 1] - tok0;
+    const int first = first_block(t, b);
+    const int len = context_len(t, b, a.B);
     const int t0 = I * a.B;
     const int n = min(a.B, len - t0);
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float* dst;
-    uint16_t* dst16 = nullptr;   // bf16 copy (K_bar / V_bar only)
-    int col;
+    float mean[8];
     if (c < a.q_chunks) {
-        // Q: packed rows, never paged.
-        col = c * 8;
-        dst = a.pq;
+        // Q: packed rows of this call's queries, never paged.  Prefix blocks
+        // (chunked prefill) have no queries here.
+        if (I < first) return;
+        const int col = c * 8;
         const int64_t row_elems = (int64_t)a.Hq * a.D;
-        const uint16_t* p = a.q + (int64_t)(tok0 + t0) * row_elems + col;
+        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B) * row_elems + col;
         int r = 0;
         for (; r + kUnroll <= n; r += kUnroll) {
             uint4 x[kUnroll];
@@ -55,19 +59,40 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
             for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
         }
         for (; r < n; ++r) add8(acc, *reinterpret_cast<const uint4*>(p + (int64_t)r * row_elems));
-    } else {
-        int cc = c - a.q_chunks;
-        const uint16_t* base = a.k;
-        dst = a.pk;
-        dst16 = a.pkv16;
-        if (cc >= a.k_chunks) {
-            cc -= a.k_chunks;
-            base = a.v;
-            dst = a.pv;
-            if (dst16) dst16 += (int64_t)a.Hkv * t.total_blocks * a.D;
+        const float fn = (float)n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
+        const int64_t off = ((int64_t)(col / a.D) * t.total_qblocks + qblock_row(t, b, I)) * a.D + col % a.D;
+        reinterpret_cast<float4*>(a.pq + off)[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
+        reinterpret_cast<float4*>(a.pq + off)[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
+        return;
+    }
+    int cc = c - a.q_chunks;
+    const bool isv = cc >= a.k_chunks;
+    if (isv) cc -= a.k_chunks;
+    const int col = cc * 8;
+    const int h = col / a.D;
+    const int dd = col % a.D;
+    // Pooled cache entry of this block: the page holding its first token.
+    float* cache = nullptr;
+    if (PAGED && a.pcache) {
+        const int page = a.kv.block_table[(int64_t)b * a.kv.max_pages + t0 / a.kv.page_size];
+        if ((unsigned)page < (unsigned)a.kv.num_pages)
+            cache = a.pcache + (((int64_t)(isv ? a.kv.num_pages : 0) + page) * a.Hkv + h) * a.D + dd;
+    }
+    if (PAGED && a.reuse && I < first) {
+        // A prefix block pooled by an earlier call.
+        float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+        if (cache) {
+            m0 = reinterpret_cast<const float4*>(cache)[0];
+            m1 = reinterpret_cast<const float4*>(cache)[1];
         }
-        col = cc * 8;
+        mean[0] = m0.x; mean[1] = m0.y; mean[2] = m0.z; mean[3] = m0.w;
+        mean[4] = m1.x; mean[5] = m1.y; mean[6] = m1.z; mean[7] = m1.w;
+    } else {
+        const uint16_t* base = isv ? a.v : a.k;
         const int64_t row_elems = (int64_t)a.Hkv * a.D;
+        const int tok0 = t.tok_off[b];
         int r = 0;
         for (; r + kUnroll <= n; r += kUnroll) {
             uint4 x[kUnroll];
@@ -84,22 +109,26 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
             const int64_t row = kv_row<PAGED>(a.kv, b, tok0, t0 + r);
             if (row >= 0) add8(acc, *reinterpret_cast<const uint4*>(base + row * row_elems + col));
         }
-    }
-    const int h = col / a.D;
-    const int dd = col % a.D;
-    const float fn = (float)n;
-    float mean[8];
+        const float fn = (float)n;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
+        for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
+        if (cache) {
+            reinterpret_cast<float4*>(cache)[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
+            reinterpret_cast<float4*>(cache)[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
+        }
+    }
     const int64_t off = ((int64_t)h * t.total_blocks + gb) * a.D + dd;
+    float* dst = isv ? a.pv : a.pk;
     if (dst) {
         reinterpret_cast<float4*>(dst + off)[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
         reinterpret_cast<float4*>(dst + off)[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
     }
-    if (dst16)   // the same means rounded to bf16 (nearest even): the correction's operands
+    if (a.pkv16) {   // the same means rounded to bf16 (nearest even): the correction's operands
+        uint16_t* dst16 = a.pkv16 + (isv ? (int64_t)a.Hkv * t.total_blocks * a.D : 0);
         *reinterpret_cast<uint4*>(dst16 + off) =
             make_uint4(pack_bf16(mean[0], mean[1]), pack_bf16(mean[2], mean[3]), pack_bf16(mean[4], mean[5]),
                        pack_bf16(mean[6], mean[7]));
+    }
 }
 
 }  // namespace

@@ -88,8 +88,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t
     int b, local;
     item_of(t, rank, b, local);
     const int nb = seq_blocks(t, b);
-    const int ntiles = (nb + a.TI - 1) / a.TI;
-    const int I0 = (ntiles - 1 - local) * a.TI;
+    const int first = first_block(t, b);             // query blocks are first .. nb-1
+    const int ntiles = (nb - first + a.TI - 1) / a.TI;
+    const int I0 = first + (ntiles - 1 - local) * a.TI;
     const int gblk0 = t.blk_off[b];
     const int rows = a.TI * a.g;
     const int rho = lane & 31;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t
         const int h = hk * a.g + rho % a.g;
         const bool valid = rho < rows && I < nb;
         const float4* src = reinterpret_cast<const float4*>(
-            a.pq + ((int64_t)h * t.total_blocks + gblk0 + (valid ? I : 0)) * D + 8 * half);
+            a.pq + ((int64_t)h * t.total_qblocks + qblock_row(t, b, valid ? I : I0)) * D + 8 * half);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             float4 x0 = valid ? src[4 * kk] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -180,8 +181,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t
         const int I = I0 + ii;
         if (rr >= rows || I >= nb) continue;                 // wave-uniform
         const int h = hk * a.g + hi;
-        int32_t* out = a.kv_idx + t.idx_off[b] + (int64_t)h * ((int64_t)nb * (nb + 1) / 2) +
-                       (int64_t)I * (I + 1) / 2;
+        int32_t* out = a.kv_idx + list_row(t, b, h, I, nb, first);
         int base = 0;
         for (int c0 = 0; c0 < ntile; c0 += 64) {
             const int ct = c0 + lane;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t
             }
             base += __shfl(incl, 63);
         }
-        if (lane == 0) a.kv_cnt[(int64_t)a.Hq * gblk0 + (int64_t)h * nb + I] = base;
+        if (lane == 0) a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = base;
     }
 }
 

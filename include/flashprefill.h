@@ -137,6 +137,61 @@ int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
                                    void* workspace, size_t workspace_bytes,
                                    void* out, float* lse, void* stream);
 
+/*
+ * Chunked prefill over a paged KV cache (FlashPrefill V2 abstract and the
+ * authors' post: an attention backend with paged KV and continuous
+ * batching).  Request b brings q_len = cu_seqlens_q_host[b+1] -
+ * cu_seqlens_q_host[b] new queries at the end of a context of
+ * kv_len = kv_lens_host[b] tokens whose keys and values, the new ones
+ * included, are already in the cache.  Blocks are counted from the start of
+ * the context; the chunk must start on a block boundary ((kv_len - q_len) a
+ * multiple of block_size, else FP_UNSUPPORTED), 0 <= q_len <= kv_len.  Query
+ * row r of request b sits at position kv_len - q_len + r and sees every key
+ * at or before it (bottom-right causal alignment); its query block I =
+ * position / block_size is pooled over the chunk's queries in it, scored
+ * against the block means of the whole context and thresholded as in steps
+ * 1-4, and attends as in step 5.  Under these rules a chunk's output equals
+ * the last q_len rows of a prefill of the whole context.
+ *   q [T,Hq,d] bf16, T = cu_seqlens_q_host[batch]: the chunks packed back to back.
+ *   k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq: as
+ *     for fp_sparse_prefill_varlen_paged; block_table covers kv_len tokens.
+ *   kv_lens_host [batch] int32, host memory read during the call.
+ *   pooled_cache: NULL, or fp32 [2, num_pages, Hkv, d] owned by the caller
+ *     and kept between calls: entry [0|1][p][h] holds the K_bar | V_bar of
+ *     head h of the block whose first token lives in page p.  Every block
+ *     pooled in the call is written there.
+ *   prefix_pooled: 1 = the blocks before each chunk were pooled into
+ *     pooled_cache by earlier calls (same pages, same contents): their means
+ *     are read from it instead of from the cache pages; 0 = pool them now.
+ *     1 requires pooled_cache.
+ *   kv_idx, kv_cnt: lists of the chunk's query blocks only: request b's
+ *     region holds, for each head h, the rows I = first .. nb-1 (first =
+ *     (kv_len - q_len) / block_size, nb = ceil(kv_len / block_size)), row I
+ *     with capacity I + 1; kv_cnt is [Hq, nb - first] per request.  Regions
+ *     of consecutive requests are concatenated.  Sizes from fp_chunked_sizes.
+ *   workspace: at least the bytes fp_chunked_sizes gives; contents on return
+ *     are unspecified.
+ *   out [T,Hq,d] bf16, lse [Hq,T] fp32 or NULL (rows of the chunks).
+ * bf16 only.  batch <= FP_MAX_BATCH.
+ */
+int fp_sparse_prefill_chunked_paged(const fp_params* params, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    int32_t page_size, int32_t num_pages,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                    int32_t batch, float* pooled_cache, int32_t prefix_pooled,
+                                    int32_t* kv_idx, int32_t* kv_cnt,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* out, float* lse, void* stream);
+
+/* Sizes for fp_sparse_prefill_chunked_paged (host only): kv_idx entries,
+ * kv_cnt entries and workspace bytes, written where the pointers are not
+ * NULL.  Returns FP_OK or the error the call itself would give for these
+ * lengths. */
+int fp_chunked_sizes(const fp_params* params, const int32_t* cu_seqlens_q_host,
+                     const int32_t* kv_lens_host, int32_t batch,
+                     int64_t* index_capacity, int64_t* count_entries, size_t* workspace_bytes);
+
 /* Sizes (host only, no device work).  A single sequence of length S is
  * cu_seqlens_host = {0, S}, batch = 1.  Return -1 / 0 on invalid arguments. */
 int64_t fp_index_capacity(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch);

@@ -138,3 +138,46 @@ def test_varlen_validation():
     assert _varlen(p, [0] * 130) == fp.FP_UNSUPPORTED                  # batch > 128
     assert _varlen(p, [0, 0, 0]) == fp.FP_OK                            # nothing to do
     assert fp.lib().fp_last_error() == b""
+
+
+def _chunked(p, cu, kv, page_size=64, num_pages=100, max_pages=64, ws=1 << 30, cache=None, reuse=0,
+             kv_lens_null=False):
+    l = fp.lib()
+    c = (ctypes.c_int32 * len(cu))(*cu)
+    k = None if kv_lens_null else (ctypes.c_int32 * len(kv))(*kv)
+    return l.fp_sparse_prefill_chunked_paged(ctypes.byref(p), FAKE, FAKE, FAKE, page_size, num_pages, FAKE,
+                                             max_pages, c, k, len(cu) - 1, cache, reuse, FAKE, FAKE,
+                                             ctypes.c_void_p(1 << 24), ws, FAKE, None, None)
+
+
+def test_chunked_validation():
+    p = _p()
+    assert _chunked(p, [0, 100], [1000]) == fp.FP_UNSUPPORTED          # chunk starts at 900, not a block edge
+    assert "block boundary" in fp.lib().fp_last_error().decode()
+    assert _chunked(p, [0, 300], [200]) == fp.FP_INVALID_ARGUMENT      # more queries than context
+    assert _chunked(p, [0, 128], [256], kv_lens_null=True) == fp.FP_INVALID_ARGUMENT
+    assert _chunked(p, [0, 128], [256], reuse=1) == fp.FP_INVALID_ARGUMENT           # reuse without a cache
+    assert _chunked(p, [0, 128], [256], cache=FAKE, reuse=2) == fp.FP_INVALID_ARGUMENT
+    assert _chunked(p, [0, 128], [4096], max_pages=10) == fp.FP_INVALID_ARGUMENT     # pages cover the context
+    assert _chunked(p, [0, 128], [256], cache=MISALIGNED) == fp.FP_INVALID_ARGUMENT
+    assert _chunked(p, [0, 128], [256], ws=16) == fp.FP_WORKSPACE_TOO_SMALL
+    assert _chunked(_p(dtype=fp.FP_DTYPE_FP8_E4M3FN), [0, 128], [256]) == fp.FP_UNSUPPORTED
+    assert _chunked(p, [0, 0, 0], [256, 512]) == fp.FP_OK                # no queries: nothing to do
+    assert fp.lib().fp_last_error() == b""
+
+
+def test_chunked_sizes():
+    p = _p()                                   # 32/8 heads, d 128, block 128, correction on
+    cap, cnt, ws = fp.fp_chunked_sizes(p, [0, 256], [1024])      # query blocks 6, 7 of 8
+    tri = lambda n: n * (n + 1) // 2
+    assert cap == 32 * (tri(8) - tri(6))
+    assert cnt == 32 * 2
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert ws == a256(2 * 128 * 32 * 4) + a256(8 * 128 * 8 * 4) + a256(2 * 8 * 128 * 8 * 2)
+    # whole prompts: the same sizes as the varlen entry
+    cu = [0, 1000, 1300, 5000]
+    lens = [cu[i + 1] - cu[i] for i in range(3)]
+    assert fp.fp_chunked_sizes(p, cu, lens) == (fp.fp_index_capacity(p, cu), fp.fp_count_entries(p, cu),
+                                                fp.fp_varlen_workspace_bytes(p, cu))
+    with pytest.raises(fp.FlashPrefillError):
+        fp.fp_chunked_sizes(p, [0, 100], [1000])
