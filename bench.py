@@ -298,31 +298,74 @@ def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
     r = fp.fp_sparse_prefill_varlen_paged(p, qd, kc, vc, bt, pb.cu_seqlens)
     tv = timed_ms(lambda: fp.fp_sparse_prefill_varlen_paged(p, qd, kc, vc, bt, pb.cu_seqlens,
                                                             workspace=r.workspace, out=r.out), 5, stream)
-    # every request length is a multiple of the block, so all blocks are full
     cu = [int(x) for x in pb.cu_seqlens]
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
     Bp, dp, Hqp = w.block_size, w.head_dim, w.num_q_heads
-    cnt = r.kv_cnt.to(torch.int64)
-    idx = r.kv_idx.to(torch.int64)
-    kept = skipped = 0
-    ioff = coff = 0
-    for b in range(len(cu) - 1):
-        nb = (cu[b + 1] - cu[b] + Bp - 1) // Bp
-        c = cnt[coff:coff + Hqp * nb].view(Hqp, nb)
-        I = torch.arange(nb, device=dev)
-        tri = nb * (nb + 1) // 2
-        base = ioff + torch.arange(Hqp, device=dev)[:, None] * tri + (I * (I + 1) // 2)[None, :]
-        diag = (idx[base + c - 1] == I[None, :]).to(torch.int64)
-        kept += int(c.sum())
-        skipped += int((I[None, :] - (c - diag)).sum())
-        ioff += Hqp * tri
-        coff += Hqp * nb
-    # kept blocks cost B keys per query row, a skipped past block one pooled entry
+    kept, skipped = list_work(r.kv_idx, r.kv_cnt, lens, [0] * len(lens), Hqp, Bp, dev)
+    # every request length is a multiple of the block, so all blocks are full:
+    # a kept block costs B keys per query row, a skipped past block one pooled entry
     f_v = 4.0 * dp * Bp * (Bp * kept + (skipped if corr else 0))
     res["paged"] = {"workload": w.name, "tokens": cu[-1], "requests": len(cu) - 1, "step_ms": round(tv, 4),
                     "tokens_per_s": round(cu[-1] / (tv * 1e-3), 1), "kept_blocks": kept,
                     "tflops": round(f_v / (tv * 1e-3) / 1e12, 2)}
     log(f"bench: paged {res['paged']}")
+
+    # Chunked prefill on the same contexts: the last CHUNK tokens of each
+    # request are new; the prefix means were pooled into the cache by an
+    # earlier call (untimed), the timed call reads them from it.
+    CHUNK = 4096
+    cut = [max(0, L - CHUNK) for L in lens]
+    num_pages = kc.shape[0]
+    cache = fp.alloc_pooled_cache(p, num_pages, dev)
+    q_pre = torch.cat([qd[cu[b]:cu[b] + cut[b]] for b in range(len(lens))])
+    cu_pre = [0]
+    for c_ in cut:
+        cu_pre.append(cu_pre[-1] + c_)
+    fp.fp_sparse_prefill_chunked_paged(p, q_pre, kc, vc, bt, cu_pre, cut, pooled_cache=cache)
+    q_new = torch.cat([qd[cu[b] + cut[b]:cu[b + 1]] for b in range(len(lens))])
+    cu_new = [0]
+    for b in range(len(lens)):
+        cu_new.append(cu_new[-1] + lens[b] - cut[b])
+    rc = fp.fp_sparse_prefill_chunked_paged(p, q_new, kc, vc, bt, cu_new, lens, pooled_cache=cache,
+                                            prefix_pooled=True)
+    tc = timed_ms(lambda: fp.fp_sparse_prefill_chunked_paged(p, q_new, kc, vc, bt, cu_new, lens,
+                                                             pooled_cache=cache, prefix_pooled=True,
+                                                             workspace=rc.workspace, out=rc.out), 5, stream)
+    kept, skipped = list_work(rc.kv_idx, rc.kv_cnt, lens, cut, Hqp, Bp, dev)
+    f_c = 4.0 * dp * Bp * (Bp * kept + (skipped if corr else 0))
+    res["chunked"] = {"workload": w.name + "_last4096", "new_tokens": cu_new[-1],
+                      "context_tokens": cu[-1], "chunk": CHUNK, "step_ms": round(tc, 4),
+                      "new_tokens_per_s": round(cu_new[-1] / (tc * 1e-3), 1), "kept_blocks": kept,
+                      "tflops": round(f_c / (tc * 1e-3) / 1e12, 2)}
+    log(f"bench: chunked {res['chunked']}")
     return res
+
+
+def list_work(kv_idx, kv_cnt, kv_lens, starts, Hq, B, dev):
+    """(kept, skipped past) block counts over all (head, query block) rows of
+    lists in the paged/chunked layout: per request, rows of query blocks
+    first .. nb-1 (first = start / B), row I with capacity I + 1."""
+    import torch
+    idx = kv_idx.to(torch.int64)
+    cnt = kv_cnt.to(torch.int64)
+    tri = lambda n: n * (n + 1) // 2
+    kept = skipped = 0
+    io = co = 0
+    for L, P0 in zip(kv_lens, starts):
+        nb, first = (L + B - 1) // B, P0 // B
+        nq = nb - first
+        if nq <= 0:
+            continue
+        c = cnt[co:co + Hq * nq].view(Hq, nq)
+        I = torch.arange(first, nb, device=dev)
+        rows = (io + torch.arange(Hq, device=dev)[:, None] * (tri(nb) - tri(first))
+                + (I * (I + 1) // 2 - tri(first))[None, :])
+        diag = (idx[rows + c - 1] == I[None, :]).to(torch.int64)
+        kept += int(c.sum())
+        skipped += int((I[None, :] - (c - diag)).sum())
+        io += Hq * (tri(nb) - tri(first))
+        co += Hq * nq
+    return kept, skipped
 
 
 def cpu_baseline(q, k, v, B, alpha, corr, head, seconds):
