@@ -305,6 +305,64 @@ def attention_probabilities(q, k, v, sel: Selection, correction: bool, h: int, I
     return w / l[:, None]
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """OCP FP8 E4M3 ("fn") codes of fp32 values within [-448, 448].
+
+    Written from the format: sign bit, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds the subnormals m * 2^-9; the
+    largest finite value is 1.75 * 2^8 = 448 (code 0x7e; 0x7f is NaN).  The
+    magnitude is rounded to the nearest representable value, ties to the
+    even mantissa.
+    """
+    y = np.asarray(y, dtype=np.float32).astype(np.float64)     # exact
+    if np.any(np.abs(y) > E4M3_MAX) or np.any(~np.isfinite(y)):
+        raise ValueError("e4m3_encode takes finite values within [-448, 448]")
+    sign = np.signbit(y).astype(np.uint8) << 7
+    a = np.abs(y)
+    _, E = np.frexp(a)                                       # a = m 2^E, m in [0.5, 1)
+    e = np.maximum(E - 1, -6)                                # below 2^-6 the spacing stays 2^-9
+    step = np.ldexp(1.0, e - 3)                              # spacing of representable values
+    v = np.round(a / step) * step                            # exact quotient; round half to even
+    _, E2 = np.frexp(v)
+    normal = v >= 2.0 ** -6
+    ef = np.where(normal, E2 - 1 + 7, 0)
+    mant = np.where(normal, v / np.ldexp(1.0, E2 - 1) - 1.0, v / 2.0 ** -9)
+    mant = np.where(normal, mant * 8.0, mant)
+    return (sign | (ef.astype(np.uint8) << 3) | mant.astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of finite E4M3 codes (fp64)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    ef, m = (c >> 3) & 15, c & 7
+    return s * np.where(ef == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, ef - 7))
+
+
+def quantize_fp8_blockwise(x, block: int):
+    """Codes and scales for fp8 inputs (reading R10): per (head, block) the
+    scale is amax / 448 in fp32 (1 for an all-zero block); the codes are the
+    E4M3 rounding of clamp(x / scale, -448, 448), the division in fp32, so
+    every integer decision is taken in the same precision as on the GPU.
+    x [S, H, d] -> (codes uint8 [S, H, d], scales fp32 [H, nB])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    S, H, d = x32.shape
+    nB = num_blocks(S, block)
+    codes = np.empty((S, H, d), dtype=np.uint8)
+    scales = np.empty((H, nB), dtype=np.float32)
+    for J in range(nB):
+        seg = x32[J * block:min(S, (J + 1) * block)]
+        amax = np.abs(seg).max(axis=(0, 2))
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        scales[:, J] = sc
+        y = np.clip(seg / sc[None, :, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+        codes[J * block:min(S, (J + 1) * block)] = e4m3_encode(y)
+    return codes, scales
+
+
 def dequantize_blockwise(codes_value, scales, block: int) -> np.ndarray:
     """x = x8 * scale[h, t // block] for fp8 values decoded to float ([S, H, d])."""
     x8 = _f64(codes_value)

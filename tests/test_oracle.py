@@ -439,3 +439,70 @@ def test_empty_chunk():
     assert sel.keep.shape == (2, 0, 5)
     o, lse = O.sparse_attention_chunked(q[40:], k, v, sel, True)
     assert o.shape == (0, 2, 4) and lse.shape == (2, 0)
+
+
+# ------------------------------------------------------ e4m3 encoder (fp8)
+
+def _e4m3_table():
+    """Codes 0..126 and their values, from the format definition (bias 7,
+    3 mantissa bits, exponent field 0 = subnormals m/8 * 2^-6)."""
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = np.array([(c & 7) / 8 * 2.0 ** -6 if c >> 3 == 0 else (1 + (c & 7) / 8) * 2.0 ** ((c >> 3) - 7)
+                     for c in range(0x7F)])
+    return codes, vals
+
+
+def test_e4m3_encode_every_finite_value():
+    codes, vals = _e4m3_table()
+    assert vals[-1] == 448.0
+    assert np.array_equal(O.e4m3_encode(vals.astype(np.float32)), codes)
+    assert np.array_equal(O.e4m3_encode(-vals[1:].astype(np.float32)), codes[1:] | 0x80)
+    assert np.array_equal(O.e4m3_decode(codes), vals)
+
+
+def test_e4m3_ties_go_to_even_mantissa():
+    codes, vals = _e4m3_table()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[:-1] + vals[1:]) / 2)   # exact in fp32
+    got = O.e4m3_encode(mids)
+    want = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:])
+    assert np.array_equal(got, want)
+    # just off the midpoint the nearer value wins
+    above = np.nextafter(mids, np.float32(np.inf))
+    assert np.array_equal(O.e4m3_encode(above), codes[1:])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    r = np.random.default_rng(3)
+    y = (r.choice([-1, 1], 20000) * np.exp(r.uniform(np.log(1e-5), np.log(448.0), 20000))).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(y), ref)
+
+
+def test_quantize_blockwise_scale_rule():
+    r = np.random.default_rng(4)
+    x = r.standard_normal((300, 3, 16)).astype(np.float32) * 2
+    x[128:256, 1] = 0.0                                      # an all-zero (head, block)
+    codes, scales = O.quantize_fp8_blockwise(x, 128)
+    assert scales.dtype == np.float32 and scales.shape == (3, 3)
+    assert scales[1, 1] == 1.0 and not codes[128:256, 1].any()
+    for h in range(3):
+        for J in range(3):
+            seg = x[J * 128:(J + 1) * 128, h]
+            if J == 1 and h == 1:
+                continue
+            assert scales[h, J] == np.float32(np.abs(seg).max()) / np.float32(448)
+            i = np.unravel_index(np.abs(seg).argmax(), seg.shape)
+            assert codes[J * 128 + i[0], h, i[1]] & 0x7F == 0x7E         # the amax element maps to 448
+    deq = O.dequantize_blockwise(O.e4m3_decode(codes), scales, 128)
+    big = np.abs(deq) >= 2.0 ** -6 * scales[:, np.arange(300) // 128].T[:, :, None]
+    rel = np.abs(deq - x)[big] / np.abs(x)[big]
+    assert rel.max() <= 2.0 ** -4
+
+
+def test_quantize_blockwise_matches_generator_quantizer():
+    q, k, v = synth.make_sequence(700, 4, 2, 32, seed=9, verticals=True)
+    for x in (q, k, v):
+        c_t, s_t = synth.quantize_fp8_blockwise(x, 128)
+        c_o, s_o = O.quantize_fp8_blockwise(x.float().numpy(), 128)
+        assert np.array_equal(c_o, c_t.numpy()) and np.array_equal(s_o, s_t.numpy())
