@@ -45,6 +45,8 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 EXPORTS = {
     "fp_select_blocks": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, ctypes.c_int32,
                                         _P, _P, _P, _P, _P, _P, _P]),
+    "fp_select_blocks_fp8": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, ctypes.c_int32,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "fp_sparse_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P, _P, _P, _P,
                                              ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "fp_sparse_prefill_varlen_paged": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
@@ -163,6 +165,43 @@ def fp_select_blocks(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: Opt
                                   S, _ptr(sel.pooled_q), _ptr(sel.pooled_k), _ptr(sel.pooled_v),
                                   _ptr(sel.pooled_kv), _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _stream(dev)))
     return sel
+
+
+@dataclass
+class Fp8Inputs:
+    """Outputs of fp_select_blocks_fp8: e4m3 codes (uint8) and fp32 scales per
+    (head, block), ready for fp_sparse_prefill_fwd in fp8 mode."""
+    q8: torch.Tensor
+    k8: torch.Tensor
+    v8: torch.Tensor
+    q_scale: torch.Tensor       # [Hq, nB]
+    k_scale: torch.Tensor       # [Hkv, nB]
+    v_scale: torch.Tensor
+
+
+def fp_select_blocks_fp8(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         sel: Optional[Selection] = None, f8: Optional[Fp8Inputs] = None):
+    """One pass over bf16 q/k/v: fp8 codes and scales, pooled means, then block
+    scores + threshold + lists.  params.dtype must be fp8.  Returns (Selection, Fp8Inputs)."""
+    S = q.shape[0]
+    dev = q.device
+    if sel is None:
+        sel = alloc_selection(params, S, dev, pool_v=bool(params.mean_correction))
+        sel.pooled_v = None
+    if f8 is None:
+        B = params.block_size
+        nB = (S + B - 1) // B
+        f8 = Fp8Inputs(torch.empty(q.shape, dtype=torch.uint8, device=dev),
+                       torch.empty(k.shape, dtype=torch.uint8, device=dev),
+                       torch.empty(v.shape, dtype=torch.uint8, device=dev),
+                       torch.empty((q.shape[1], nB), dtype=torch.float32, device=dev),
+                       torch.empty((k.shape[1], nB), dtype=torch.float32, device=dev),
+                       torch.empty((v.shape[1], nB), dtype=torch.float32, device=dev))
+    _check(lib().fp_select_blocks_fp8(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), S,
+                                      _ptr(f8.q8), _ptr(f8.k8), _ptr(f8.v8), _ptr(f8.q_scale), _ptr(f8.k_scale),
+                                      _ptr(f8.v_scale), _ptr(sel.pooled_q), _ptr(sel.pooled_k), _ptr(sel.pooled_kv),
+                                      _ptr(sel.kv_idx), _ptr(sel.kv_cnt), _stream(dev)))
+    return sel, f8
 
 
 def fp_sparse_prefill_fwd(params: fp_params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

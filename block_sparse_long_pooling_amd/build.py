@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashprefill.so")
-SOURCES = ["fp_abi.hip", "k_pool.hip", "k_select.hip", "k_attn.hip", "k_attn_fp8.hip"]
+SOURCES = ["fp_abi.hip", "k_pool.hip", "k_quant.hip", "k_select.hip", "k_attn.hip", "k_attn_fp8.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -139,6 +139,9 @@ int device_status(hipError_t e, const char* what) {
 
 int select_tile(const fp_params& p) { return 32 / (p.num_q_heads / p.num_kv_heads); }
 
+int run_scores(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const float* pq,
+               const float* pk, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
+
 // Pooling and selection.  kv_lens: context lengths (chunked prefill) or NULL;
 // pcache: the caller's pooled cache (chunked prefill) or NULL; reuse: read
 // the prefix blocks' means from it instead of pooling them.
@@ -169,7 +172,13 @@ int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, in
     pa.total_chunks = pa.q_chunks + pa.k_chunks * (pool_v ? 2 : 1);
     rc = device_status(launch_pool(pa, t, paged, st), "pool");
     if (rc) return rc;
+    return run_scores(p, cu, kv_lens, batch, pq, pk, kv_idx, kv_cnt, st);
+}
 
+// Scores, threshold and lists from pooled means already in place.
+int run_scores(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const float* pq,
+               const float* pk, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
+    int rc;
     SeqTable ts;
     const int TI = select_tile(p);
     rc = build_table(p, cu, kv_lens, batch, TI, ts);
@@ -260,6 +269,61 @@ FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const voi
     rc = run_select(*params, cu, nullptr, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v,
                     static_cast<uint16_t*>(pooled_kv_bf16), nullptr, 0, kv_idx, kv_cnt,
                     static_cast<hipStream_t>(stream));
+    return rc ? rc : ok();
+}
+
+FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const void* k, const void* v,
+                                   int32_t seqlen, void* q8, void* k8, void* v8, float* q_scale, float* k_scale,
+                                   float* v_scale, float* pooled_q, float* pooled_k, void* pooled_kv_bf16,
+                                   int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    const fp_params& p = *params;
+    if (p.dtype != FP_DTYPE_FP8_E4M3FN)
+        return fail(FP_INVALID_ARGUMENT, "fp_select_blocks_fp8 prepares fp8 attention: params->dtype must be fp8");
+    if (seqlen < 0) return fail(FP_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", seqlen);
+    if (seqlen == 0) return ok();
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(FP_INVALID_ARGUMENT, "q, k and v must be non-NULL and 16-byte aligned");
+    if (!aligned(q8, 8) || !aligned(k8, 8) || !aligned(v8, 8))
+        return fail(FP_INVALID_ARGUMENT, "q8, k8 and v8 must be non-NULL and 8-byte aligned");
+    if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+        return fail(FP_INVALID_ARGUMENT, "q_scale, k_scale and v_scale must be non-NULL and 4-byte aligned");
+    if (!aligned(pooled_q, 16) || !aligned(pooled_k, 16))
+        return fail(FP_INVALID_ARGUMENT, "pooled_q and pooled_k must be non-NULL and 16-byte aligned");
+    if (p.mean_correction && !aligned(pooled_kv_bf16, 16))
+        return fail(FP_INVALID_ARGUMENT, "mean_correction needs a 16-byte aligned pooled_kv_bf16");
+    if (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+        return fail(FP_INVALID_ARGUMENT, "kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
+    const int32_t cu[2] = {0, seqlen};
+    SeqTable t;
+    rc = build_table(p, cu, nullptr, 1, 1, t);
+    if (rc) return rc;
+    QuantArgs qa;
+    qa.src[0] = static_cast<const uint16_t*>(q);
+    qa.src[1] = static_cast<const uint16_t*>(k);
+    qa.src[2] = static_cast<const uint16_t*>(v);
+    qa.codes[0] = static_cast<uint8_t*>(q8);
+    qa.codes[1] = static_cast<uint8_t*>(k8);
+    qa.codes[2] = static_cast<uint8_t*>(v8);
+    qa.scale[0] = q_scale;
+    qa.scale[1] = k_scale;
+    qa.scale[2] = v_scale;
+    qa.pq = pooled_q;
+    qa.pk = pooled_k;
+    qa.pkv16 = p.mean_correction ? static_cast<uint16_t*>(pooled_kv_bf16) : nullptr;
+    qa.H[0] = p.num_q_heads;
+    qa.H[1] = qa.H[2] = p.num_kv_heads;
+    qa.groups[0] = qa.groups[1] = qa.groups[2] = 0;
+    qa.S = seqlen;
+    qa.D = p.head_dim;
+    qa.B = p.block_size;
+    qa.nB = t.total_blocks;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    rc = device_status(launch_quant_pool(qa, st), "quantize + pool");
+    if (rc) return rc;
+    rc = run_scores(p, cu, nullptr, 1, pooled_q, pooled_k, kv_idx, kv_cnt, st);
     return rc ? rc : ok();
 }
 

@@ -1,0 +1,177 @@
+// Fused fp8 quantization and block-mean pooling of Q, K and V in one pass
+// over the bf16 data (FlashPrefill V2 abstract: FP8 inference; the fp8
+// recipe is one scale per (head, block) = amax / 448, codes = OCP E4M3 of
+// clamp(x / scale), and the pooled means that drive selection are those of
+// the bf16 data, as in the pooling kernel).
+//
+// A workgroup (8 waves) owns one block of one tensor for a group of heads
+// whose chunks of 8 bf16 make 32 chunks per token row (two heads at d 128,
+// four at d 64), i.e. 512 contiguous bytes.  Lane l of wave w handles chunk
+// l % 32 of tokens 16 s + 2 w + l / 32: a wave reads two full 512-byte rows
+// per load, and each thread keeps its B / 16 chunks in registers.  Block sums
+// and the per-head absolute maximum are reduced across lanes and waves; the
+// means and the scale are written, then the codes are formed from the values
+// still in registers.  HBM sees one read of the bf16 data and one write of
+// the codes.  The scale and x / scale are correctly rounded fp32 divisions,
+// so every code is decided in the same precision as the format's reference.
+// x / scale takes three operations: with y the correctly rounded 1 / scale
+// (one division per head and block), q = x y, the remainder x - q scale
+// (exact with an FMA) and q + remainder * y rounded give the correctly
+// rounded quotient (Markstein's correction step).  Quotients small enough to
+// lose precision as fp32 subnormals lie far below the smallest e4m3 code and
+// encode as zero either way.
+#include "fp_launch.h"
+
+// The quotient steps below are explicit FMAs; nothing else may be fused.
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int kWaves = 8;
+
+template <int D, int B>
+__global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
+    constexpr int CPH = D / 8;             // chunks per head
+    constexpr int HPG = 32 / CPH;          // heads per workgroup
+    constexpr int NS = B / (2 * kWaves);   // tokens per thread
+    __shared__ float psum[kWaves][32][8];
+    __shared__ float pmax[kWaves][HPG];
+    __shared__ float scl[HPG];
+    __shared__ float rcp[HPG];
+
+    const int J = blockIdx.x;
+    int g = blockIdx.y, ts = 0;
+    if (g >= a.groups[0]) {
+        g -= a.groups[0];
+        ts = 1;
+        if (g >= a.groups[1]) {
+            g -= a.groups[1];
+            ts = 2;
+        }
+    }
+    const int H = a.H[ts];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ch = lane & 31, hf = lane >> 5;
+    const int hl = ch / CPH;               // head within the group
+    const int h = g * HPG + hl;
+    const bool hv = h < H;
+    const int t0 = J * B;
+    const int n = min(B, a.S - t0);
+    const int64_t row = (int64_t)H * D;
+    const int64_t col = (int64_t)g * HPG * D + ch * 8;
+    const uint16_t* src = a.src[ts] + (int64_t)t0 * row + col;
+
+    uint4 x[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int tok = 2 * kWaves * s + 2 * w + hf;
+        x[s] = (hv && tok < n) ? *reinterpret_cast<const uint4*>(src + tok * row) : make_uint4(0, 0, 0, 0);
+    }
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float amax = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
+            sum[2 * i] += lo;
+            sum[2 * i + 1] += hi;
+            amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+        }
+    }
+    // Sums: the two token halves of a wave, then the waves (in wave order,
+    // so the sum order is fixed).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum[i] += __shfl_xor(sum[i], 32);
+    // amax: the head's chunks within the wave, both halves.
+#pragma unroll
+    for (int off = 1; off < CPH; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (hf == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) psum[w][ch][i] = sum[i];
+        if (ch % CPH == 0) pmax[w][hl] = amax;
+    }
+    __syncthreads();
+    if (w == 0 && hf == 0 && hv) {
+        float m[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float t = psum[0][ch][i];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) t += psum[w2][ch][i];
+            m[i] = t / (float)n;
+        }
+        const int64_t off = ((int64_t)h * a.nB + J) * D + (ch % CPH) * 8;
+        float* dst = ts == 0 ? a.pq : (ts == 1 ? a.pk : nullptr);
+        if (dst) {
+            reinterpret_cast<float4*>(dst + off)[0] = make_float4(m[0], m[1], m[2], m[3]);
+            reinterpret_cast<float4*>(dst + off)[1] = make_float4(m[4], m[5], m[6], m[7]);
+        }
+        if (ts > 0 && a.pkv16)
+            *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
+                make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
+                           pack_bf16(m[6], m[7]));
+        if (ch % CPH == 0) {
+            float am = pmax[0][hl];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) am = fmaxf(am, pmax[w2][hl]);
+            const float sc = am > 0.f ? __fdiv_rn(am, kE4M3Max) : 1.f;
+            scl[hl] = sc;
+            rcp[hl] = __fdiv_rn(1.f, sc);
+            a.scale[ts][(int64_t)h * a.nB + J] = sc;
+        }
+    }
+    __syncthreads();
+    if (!hv) return;
+    const float sc = scl[hl];
+    const float ry = rcp[hl];
+    auto quot = [&](float xv) {
+        const float q = xv * ry;
+        const float r = fmaf(-q, sc, xv);
+        return fminf(fmaxf(fmaf(r, ry, q), -kE4M3Max), kE4M3Max);
+    };
+    uint8_t* dst = a.codes[ts] + (int64_t)t0 * row + col;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int tok = 2 * kWaves * s + 2 * w + hf;
+        if (tok >= n) continue;
+        const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+        uint32_t out[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float y[4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                y[2 * k] = quot(bf16_lo(wd[2 * i + k]));
+                y[2 * k + 1] = quot(bf16_hi(wd[2 * i + k]));
+            }
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
+            out[i] = (uint32_t)v;
+        }
+        *reinterpret_cast<uint2*>(dst + tok * row) = make_uint2(out[0], out[1]);
+    }
+}
+
+template <int D, int B>
+hipError_t launch_t(const QuantArgs& a, hipStream_t s) {
+    constexpr int HPG = 32 / (D / 8);
+    QuantArgs b = a;
+    for (int i = 0; i < 3; ++i) b.groups[i] = (a.H[i] + HPG - 1) / HPG;
+    hipLaunchKernelGGL((k_quant_pool<D, B>), dim3(a.nB, b.groups[0] + b.groups[1] + b.groups[2]), dim3(64 * kWaves),
+                       0, s, b);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_pool(const QuantArgs& a, hipStream_t s) {
+    if (a.nB == 0) return hipSuccess;
+    if (a.D == 128 && a.B == 128) return launch_t<128, 128>(a, s);
+    if (a.D == 128 && a.B == 64) return launch_t<128, 64>(a, s);
+    if (a.D == 64 && a.B == 128) return launch_t<64, 128>(a, s);
+    if (a.D == 64 && a.B == 64) return launch_t<64, 64>(a, s);
+    return hipErrorInvalidValue;
+}

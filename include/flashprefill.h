@@ -89,6 +89,29 @@ int fp_select_blocks(const fp_params* params,
                      int32_t* kv_idx, int32_t* kv_cnt, void* stream);
 
 /*
+ * fp8 inputs in one pass (FlashPrefill V2 abstract: FP8 inference): reads the
+ * bf16 q, k, v of one sequence once and writes
+ *   - the e4m3 codes and fp32 scales fp_sparse_prefill_fwd takes in fp8 mode:
+ *     per (head, block) scale = amax / 448 of the block's values (1 for an
+ *     all-zero block), code = OCP E4M3 ("fn") value nearest to
+ *     clamp(x / scale, -448, 448), ties to even; both divisions are correctly
+ *     rounded fp32;
+ *   - the block means, and then the lists of steps 1-4 exactly as
+ *     fp_select_blocks would (selection from the bf16 data).
+ *   params: dtype must be FP_DTYPE_FP8_E4M3FN (the attention that follows).
+ *   q [S,Hq,d], k, v [S,Hkv,d] bf16.
+ *   q8 [S,Hq,d], k8, v8 [S,Hkv,d] uint8 codes, 8-byte aligned (written).
+ *   q_scale [Hq,nB], k_scale, v_scale [Hkv,nB] fp32 (written).
+ *   pooled_q, pooled_k, pooled_kv_bf16, kv_idx, kv_cnt: as for fp_select_blocks
+ *     (pooled_kv_bf16 required when params->mean_correction is 1).
+ */
+int fp_select_blocks_fp8(const fp_params* params, const void* q, const void* k, const void* v,
+                         int32_t seqlen, void* q8, void* k8, void* v8,
+                         float* q_scale, float* k_scale, float* v_scale,
+                         float* pooled_q, float* pooled_k, void* pooled_kv_bf16,
+                         int32_t* kv_idx, int32_t* kv_cnt, void* stream);
+
+/*
  * Attention: step 5 for one sequence, over the lists from fp_select_blocks
  * (FlashPrefill 2.C; V2 abstract for the correction, PackGQA and FP8).
  *   q [S,Hq,d], k, v [S,Hkv,d]: bf16, or e4m3fn bytes when params->dtype is

@@ -181,3 +181,20 @@ def test_chunked_sizes():
                                                 fp.fp_varlen_workspace_bytes(p, cu))
     with pytest.raises(fp.FlashPrefillError):
         fp.fp_chunked_sizes(p, [0, 100], [1000])
+
+
+def test_select_blocks_fp8_validation():
+    l = fp.lib()
+    p8 = _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
+
+    def call(p, seqlen=1024, q8=FAKE, pkv=FAKE, scale=FAKE):
+        return l.fp_select_blocks_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, seqlen, q8, FAKE, FAKE, scale, FAKE, FAKE,
+                                      FAKE, FAKE, pkv, FAKE, FAKE, None)
+
+    assert call(_p()) == fp.FP_INVALID_ARGUMENT                     # params must describe fp8 attention
+    assert "fp8" in l.fp_last_error().decode()
+    assert call(p8, q8=ctypes.c_void_p((1 << 20) + 4)) == fp.FP_INVALID_ARGUMENT   # codes 8-byte aligned
+    assert call(p8, pkv=None) == fp.FP_INVALID_ARGUMENT             # correction needs pooled_kv_bf16
+    assert call(p8, scale=None) == fp.FP_INVALID_ARGUMENT
+    assert call(p8, seqlen=-1) == fp.FP_INVALID_ARGUMENT
+    assert call(p8, seqlen=0) == fp.FP_OK

@@ -1,0 +1,80 @@
+"""The one-pass fp8 preparation (fp_select_blocks_fp8): its e4m3 codes and
+scales equal the oracle's quantizer bit for bit, its block means equal the
+oracle's to fp32 rounding, its lists match the oracle's selection outside the
+threshold band, and attention on its outputs matches the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_pooling_amd as fp
+import oracle as O
+from block_sparse_long_pooling_amd import synth
+
+from gpu_util import FP8_TOL, check_lists, compare_mask, dev
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # S, Hq, Hkv, d, B: ragged tails, head counts that leave a workgroup's head group part-empty
+    (1000, 4, 2, 128, 128),
+    (1024, 3, 1, 64, 64),
+    (129, 5, 5, 128, 64),
+    (2048, 32, 8, 128, 128),
+    (77, 6, 2, 64, 128),
+]
+
+
+def _prep(q, k, v, B, alpha, corr):
+    S, Hq, d = q.shape
+    p8 = fp.make_params(Hq, k.shape[1], d, B, alpha, mean_correction=corr, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    sel, f8 = fp.fp_select_blocks_fp8(p8, q.to(dev()), k.to(dev()), v.to(dev()))
+    torch.cuda.synchronize()
+    return p8, sel, f8
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "S%d_h%d-%d_d%d_B%d" % s)
+def test_codes_scales_and_means(shape):
+    S, Hq, Hkv, d, B = shape
+    print(f"fp8 prep {shape}", flush=True)
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, seed=S + Hq, verticals=True)
+    v[: min(S, B), 0] = 0                     # an all-zero (head, block): scale 1, codes 0
+    _, sel, f8 = _prep(q, k, v, B, 0.1, True)
+    nB = (S + B - 1) // B
+    for x, c, s in ((q, f8.q8, f8.q_scale), (k, f8.k8, f8.k_scale), (v, f8.v8, f8.v_scale)):
+        c_ref, s_ref = O.quantize_fp8_blockwise(x.float().numpy(), B)
+        assert np.array_equal(s.cpu().numpy(), s_ref)
+        got = c.cpu().numpy()
+        assert np.array_equal(got, c_ref), int((got != c_ref).sum())
+    assert f8.v_scale[0, 0].item() == 1.0 and not f8.v8[: min(S, B), 0].any()
+    for x, m in ((q, sel.pooled_q), (k, sel.pooled_k)):
+        np.testing.assert_allclose(m.cpu().numpy(), O.block_means(x.float().numpy(), B), rtol=0, atol=2e-6)
+    pkv = sel.pooled_kv.float().cpu().numpy()
+    for i, x in enumerate((k, v)):
+        ref = O.block_means(x.float().numpy(), B)
+        assert np.abs(pkv[i] - ref).max() <= np.abs(ref).max() * 2.0 ** -8 + 1e-6   # bf16 rounding of the means
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.1, 0.5])
+@pytest.mark.parametrize("corr", [True, False])
+@pytest.mark.parametrize("shape", SHAPES[:4], ids=lambda s: "S%d_h%d-%d_d%d_B%d" % s)
+def test_attention_on_prepared_inputs(shape, alpha, corr):
+    S, Hq, Hkv, d, B = shape
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, seed=2 * S + Hq, verticals=True)
+    p8, sel, f8 = _prep(q, k, v, B, alpha, corr)
+    res = fp.fp_sparse_prefill_fwd(p8, f8.q8, f8.k8, f8.v8, sel, q_scale=f8.q_scale, k_scale=f8.k_scale,
+                                   v_scale=f8.v_scale, return_lse=True)
+    torch.cuda.synchronize()
+    nB = (S + B - 1) // B
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    ref = O.select_blocks(qn, kn, vn, B, alpha)
+    outside, inside, band = compare_mask(mask, ref)
+    assert outside == 0, (outside, inside, band)
+    deq = [O.dequantize_blockwise(O.e4m3_decode(c.cpu().numpy()), s.cpu().numpy(), B)
+           for c, s in ((f8.q8, f8.q_scale), (f8.k8, f8.k_scale), (f8.v8, f8.v_scale))]
+    o_ref, lse_ref = O.sparse_attention(deq[0], deq[1], deq[2], ref, corr, keep=mask)
+    out, lse = res
+    err = np.abs(out.float().cpu().numpy() - o_ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lse_ref).max()
+    print(f"  {shape} alpha={alpha} corr={corr}: max|o-ref| {err:.3e} max|lse-ref| {lerr:.3e}", flush=True)
+    assert err <= FP8_TOL and lerr <= 5e-2
