@@ -41,6 +41,11 @@ exactly as in a full prefill, sees blocks J <= I, and row i of the chunk sits
 at position kv_len - q_len + i (bottom-right causal alignment).  Under that
 reading a chunk's result equals the last q_len rows of the full prefill.
 
+Group-shared selection (an option, not in the pages; it serves the
+PackGQA-style head packing the V2 abstract names): the g query heads of a KV
+head share one list, the union of their own lists, so every head of a packed
+group computes on every tile fetched for it.
+
 Pins (tests/test_oracle.py): alpha = 0 reduces to dense causal attention
 computed by an independent routine; masks equal brute-force per-block scoring
 on tiny inputs; every probability row sums to 1; the correction equals dense
@@ -148,11 +153,23 @@ class Selection:
                 for h in range(Hq)]
 
 
+def share_across_group(keep: np.ndarray, band: np.ndarray, g: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-shared selection: the g query heads of a KV head share one mask,
+    the union of their own masks (a block any of them keeps is kept for all).
+    A union entry is flagged near-threshold when any head's entry is."""
+    Hq = keep.shape[0]
+    shp = (Hq // g, g) + keep.shape[1:]
+    ku = keep.reshape(shp).any(axis=1)
+    bu = band.reshape(shp).any(axis=1)
+    return np.repeat(ku, g, axis=0), np.repeat(bu, g, axis=0)
+
+
 def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                  pool_v: bool = True) -> Selection:
+                  pool_v: bool = True, shared: bool = False) -> Selection:
     """Pooling, block scores and thresholding for one sequence.
 
     q [S, Hq, d], k and v [S, Hkv, d] (any float dtype; upcast to fp64).
+    shared: one mask per KV head, the union over its query heads.
     """
     d = q.shape[-1]
     if sigma is None:
@@ -163,6 +180,8 @@ def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = No
     s = block_logits(q_bar, k_bar, sigma)
     score = block_scores(s)
     keep, band = threshold(score, alpha)
+    if shared:
+        keep, band = share_across_group(keep, band, q.shape[1] // k.shape[1])
     return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block)
 
 
@@ -237,7 +256,7 @@ def sparse_attention(q, k, v, sel: Selection, correction: bool, sigma: Optional[
 
 
 def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                          pool_v: bool = True) -> Selection:
+                          pool_v: bool = True, shared: bool = False) -> Selection:
     """Pooling, block scores and thresholding for a chunk of new queries.
 
     q [q_len, Hq, d] are the last q_len tokens of a context whose keys and
@@ -260,6 +279,8 @@ def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[flo
     s = block_logits(q_bar, k_bar, sigma, first)
     score = block_scores(s)
     keep, band = threshold(score, alpha, first)
+    if shared:
+        keep, band = share_across_group(keep, band, q.shape[1] // k.shape[1])
     return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block, first)
 
 

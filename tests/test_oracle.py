@@ -506,3 +506,48 @@ def test_quantize_blockwise_matches_generator_quantizer():
         c_t, s_t = synth.quantize_fp8_blockwise(x, 128)
         c_o, s_o = O.quantize_fp8_blockwise(x.float().numpy(), 128)
         assert np.array_equal(c_o, c_t.numpy()) and np.array_equal(s_o, s_t.numpy())
+
+
+# ------------------------------------------------- group-shared selection
+
+def _brute_force_union(q, k, B, alpha):
+    keep, band = _brute_force_keep(q, k, B, alpha)
+    g = q.shape[1] // k.shape[1]
+    Hkv = k.shape[1]
+    ku = np.zeros_like(keep)
+    for hk in range(Hkv):
+        ku[hk * g:(hk + 1) * g] = keep[hk * g:(hk + 1) * g].any(axis=0)
+    bu = np.zeros_like(band)
+    for hk in range(Hkv):
+        bu[hk * g:(hk + 1) * g] = band[hk * g:(hk + 1) * g].any(axis=0)
+    return ku, bu
+
+
+@pytest.mark.parametrize("alpha", [0.1, 0.5, 1.0])
+def test_shared_selection_is_the_group_union(alpha):
+    q, k, v = synth.make_sequence(320, 8, 2, 16, seed=12, verticals=False)
+    q, k, v = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    own = O.select_blocks(q, k, v, 32, alpha)
+    sh = O.select_blocks(q, k, v, 32, alpha, shared=True)
+    ku, bu = _brute_force_union(q, k, 32, alpha)
+    outside = ~(sh.band | bu)
+    assert np.array_equal(sh.keep[outside], ku[outside])
+    assert (sh.keep | ~own.keep).all()                     # a superset of each head's own mask
+    for hk in range(2):
+        assert (sh.keep[hk * 4:(hk + 1) * 4] == sh.keep[hk * 4]).all()
+    if alpha >= 0.5:
+        assert sh.keep.sum() > own.keep.sum()              # the heads disagree somewhere
+
+
+def test_shared_selection_without_groups_is_per_head():
+    q, k, v = _rand_qkv(200, 3, 3, 8, seed=21, scale=2.0)
+    own = O.select_blocks(q, k, v, 16, 0.4)
+    sh = O.select_blocks(q, k, v, 16, 0.4, shared=True)
+    assert np.array_equal(own.keep, sh.keep) and np.array_equal(own.band, sh.band)
+
+
+def test_shared_selection_chunked_equals_full_rows():
+    q, k, v = _rand_qkv(133, 4, 2, 8, seed=22, scale=1.3)
+    full = O.select_blocks(q, k, v, 32, 0.3, shared=True)
+    ch = O.select_blocks_chunked(q[64:], k, v, 32, 0.3, shared=True)
+    assert np.array_equal(ch.keep, full.keep[:, 2:, :])
