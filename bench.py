@@ -151,8 +151,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(alpha, steps, warmup):
-        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr)
+    def measure(alpha, steps, warmup, shared=False):
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr, shared_selection=shared)
         sel = fp.alloc_selection(p, S, dev)
         fs = lambda: fp.fp_select_blocks(p, qd, kd, vd, sel=sel)
         fa = lambda: fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, out=out)
@@ -190,6 +190,15 @@ def main():
             log(f"bench: sweep {sweep[-1]}")
             del r
         extra["alpha_sweep"] = sweep
+        # group-shared selection (one list per KV head, the union of its query heads')
+        r = measure(args.alpha, max(3, args.steps // 2), 1, shared=True)
+        fa_ = r["f_kept"] + r["f_corr"]
+        extra["shared_selection"] = dict(alpha=args.alpha, ms_per_step=round(r["ms_per_step"], 4),
+                                         select_ms=round(r["select_ms"], 4), attn_ms=round(r["attn_ms"], 4),
+                                         density=round(r["density"], 5),
+                                         attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2))
+        log(f"bench: shared selection {extra['shared_selection']}")
+        del r
         # dense references on the same GPU
         dense = measure(0.0, 2, 1)
         f_dense = 4.0 * d * Hq * (S * (S + 1) / 2)

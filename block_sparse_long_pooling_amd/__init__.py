@@ -29,7 +29,8 @@ class fp_params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-                ("mean_correction", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("mean_correction", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("shared_selection", ctypes.c_int32)]
 
 
 class FlashPrefillError(RuntimeError):
@@ -90,9 +91,10 @@ def _check(status: int):
 
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, alpha, mean_correction=True,
-                softmax_scale=0.0, dtype=FP_DTYPE_BF16) -> fp_params:
+                softmax_scale=0.0, dtype=FP_DTYPE_BF16, shared_selection=False) -> fp_params:
     return fp_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
-                     float(alpha), float(softmax_scale), int(bool(mean_correction)), int(dtype))
+                     float(alpha), float(softmax_scale), int(bool(mean_correction)), int(dtype),
+                     int(bool(shared_selection)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -61,6 +61,8 @@ int check_params(const fp_params* p) {
         return fail(FP_INVALID_ARGUMENT, "mean_correction must be 0 or 1");
     if (p->dtype != FP_DTYPE_BF16 && p->dtype != FP_DTYPE_FP8_E4M3FN)
         return fail(FP_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
+    if (p->shared_selection != 0 && p->shared_selection != 1)
+        return fail(FP_INVALID_ARGUMENT, "shared_selection must be 0 or 1");
     return FP_OK;
 }
 
@@ -195,6 +197,7 @@ int run_scores(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, in
     sa.TI = TI;
     sa.scale = sigma_of(p);
     sa.ln_alpha = p.alpha > 0.f ? (float)std::log((double)p.alpha) : -INFINITY;
+    sa.shared = p.shared_selection;
     return device_status(launch_select(sa, ts, st), "select");
 }
 

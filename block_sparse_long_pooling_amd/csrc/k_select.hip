@@ -185,7 +185,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t
         int base = 0;
         for (int c0 = 0; c0 < ntile; c0 += 64) {
             const int ct = c0 + lane;
-            const uint32_t wbits = ct < ntile ? bits[ct][rr] : 0u;
+            uint32_t wbits = 0u;
+            if (ct < ntile) {
+                if (a.shared) {
+                    // Group-shared selection: the union of the g heads' keep bits
+                    // of this query block (rows ii*g .. ii*g+g-1 of this workgroup).
+                    for (int j = 0; j < a.g; ++j) wbits |= bits[ct][ii * a.g + j];
+                } else {
+                    wbits = bits[ct][rr];
+                }
+            }
             const int n = __popc(wbits);
             int incl = n;
 #pragma unroll

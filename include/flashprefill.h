@@ -68,6 +68,10 @@ typedef struct {
     float   softmax_scale;    /* sigma for scores and attention; <= 0 means 1/sqrt(d) */
     int32_t mean_correction;  /* 1: add the mean-correction entries of skipped blocks */
     int32_t dtype;            /* FP_DTYPE_*: element type of q/k/v in the attention call */
+    int32_t shared_selection; /* 0: one list per query head (steps 1-4 as written);
+                                 1: the g = Hq/Hkv query heads of a KV head share one list,
+                                 the union of their own lists (every head of a group then
+                                 runs on every tile fetched for the group) */
 } fp_params;
 
 /*

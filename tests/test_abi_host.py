@@ -198,3 +198,12 @@ def test_select_blocks_fp8_validation():
     assert call(p8, scale=None) == fp.FP_INVALID_ARGUMENT
     assert call(p8, seqlen=-1) == fp.FP_INVALID_ARGUMENT
     assert call(p8, seqlen=0) == fp.FP_OK
+
+
+def test_shared_selection_flag_validated():
+    p = _p()
+    c = (ctypes.c_int32 * 2)(0, 1024)
+    assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) > 0
+    p.shared_selection = 2
+    assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) == -1
+    assert "shared_selection" in fp.lib().fp_last_error().decode()
