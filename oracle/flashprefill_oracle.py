@@ -46,6 +46,12 @@ PackGQA-style head packing the V2 abstract names): the g query heads of a KV
 head share one list, the union of their own lists, so every head of a packed
 group computes on every tile fetched for it.
 
+Skeleton-query scoring (FlashPrefill, gist.science technical summary,
+section 2.A: attention patterns can be found from a skeleton set of
+uniformly spaced queries): optionally each query block is represented by its
+queries at offsets 0, st, 2 st, ... (st = block / P, P the probe count), whose
+mean replaces q_bar in step 2; P = block is the plain block mean.
+
 Pins (tests/test_oracle.py): alpha = 0 reduces to dense causal attention
 computed by an independent routine; masks equal brute-force per-block scoring
 on tiny inputs; every probability row sums to 1; the correction equals dense
@@ -80,13 +86,17 @@ def block_lengths(seqlen: int, block: int) -> np.ndarray:
     return np.array([min(block, seqlen - J * block) for J in range(nB)], dtype=np.int64)
 
 
-def block_means(x, block: int) -> np.ndarray:
-    """Per-block mean over the valid tokens.  x [S, H, d] -> [H, nB, d] (fp64)."""
+def block_means(x, block: int, stride: int = 1) -> np.ndarray:
+    """Per-block mean over the valid tokens.  x [S, H, d] -> [H, nB, d] (fp64).
+
+    stride > 1 averages only the block's tokens at offsets 0, stride,
+    2 stride, ... (the skeleton queries; a partial block keeps those it has).
+    """
     S, H, d = x.shape
     nB = num_blocks(S, block)
     out = np.empty((H, nB, d), dtype=np.float64)
     for J in range(nB):
-        seg = _f64(x[J * block:min(S, (J + 1) * block)])      # [n_J, H, d]
+        seg = _f64(x[J * block:min(S, (J + 1) * block):stride])   # [n_J / stride, H, d]
         out[:, J, :] = seg.mean(axis=0)
     return out
 
@@ -164,17 +174,28 @@ def share_across_group(keep: np.ndarray, band: np.ndarray, g: int) -> Tuple[np.n
     return np.repeat(ku, g, axis=0), np.repeat(bu, g, axis=0)
 
 
+def probe_stride(block: int, probes: int) -> int:
+    """Token stride of the skeleton queries: block / probes (1 when probes is 0)."""
+    if probes == 0:
+        return 1
+    if probes < 0 or block % probes:
+        raise ValueError("probes must divide the block size")
+    return block // probes
+
+
 def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                  pool_v: bool = True, shared: bool = False) -> Selection:
+                  pool_v: bool = True, shared: bool = False, probes: int = 0) -> Selection:
     """Pooling, block scores and thresholding for one sequence.
 
     q [S, Hq, d], k and v [S, Hkv, d] (any float dtype; upcast to fp64).
     shared: one mask per KV head, the union over its query heads.
+    probes: 0, or P dividing the block: q_bar averages the skeleton queries
+    at every (block / P)-th token of the block instead of all its tokens.
     """
     d = q.shape[-1]
     if sigma is None:
         sigma = 1.0 / math.sqrt(d)
-    q_bar = block_means(q, block)
+    q_bar = block_means(q, block, probe_stride(block, probes))
     k_bar = block_means(k, block)
     v_bar = block_means(v, block) if pool_v else None
     s = block_logits(q_bar, k_bar, sigma)
@@ -256,7 +277,7 @@ def sparse_attention(q, k, v, sel: Selection, correction: bool, sigma: Optional[
 
 
 def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                          pool_v: bool = True, shared: bool = False) -> Selection:
+                          pool_v: bool = True, shared: bool = False, probes: int = 0) -> Selection:
     """Pooling, block scores and thresholding for a chunk of new queries.
 
     q [q_len, Hq, d] are the last q_len tokens of a context whose keys and
@@ -273,7 +294,7 @@ def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[flo
     if sigma is None:
         sigma = 1.0 / math.sqrt(d)
     first = (kv_len - q_len) // block
-    q_bar = block_means(q, block)          # the chunk's blocks are the context's blocks first, first+1, ...
+    q_bar = block_means(q, block, probe_stride(block, probes))   # chunk blocks = context blocks first, ...
     k_bar = block_means(k, block)
     v_bar = block_means(v, block) if pool_v else None
     s = block_logits(q_bar, k_bar, sigma, first)

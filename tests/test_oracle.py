@@ -551,3 +551,38 @@ def test_shared_selection_chunked_equals_full_rows():
     full = O.select_blocks(q, k, v, 32, 0.3, shared=True)
     ch = O.select_blocks_chunked(q[64:], k, v, 32, 0.3, shared=True)
     assert np.array_equal(ch.keep, full.keep[:, 2:, :])
+
+
+# ------------------------------------------------- skeleton-query scoring
+
+def test_skeleton_query_means_brute_force():
+    x = np.random.default_rng(8).standard_normal((45, 3, 5))
+    for P, st in ((16, 1), (4, 4), (2, 8), (1, 16)):
+        m = O.block_means(x, 16, O.probe_stride(16, P))
+        for h in range(3):
+            for J in range(3):
+                toks = range(16 * J, min(45, 16 * J + 16), st)
+                for c in range(5):
+                    assert abs(m[h, J, c] - math.fsum(x[t, h, c] for t in toks) / len(toks)) < 1e-15
+    assert np.array_equal(O.block_means(x, 16, 1), O.block_means(x, 16))
+    with pytest.raises(ValueError):
+        O.probe_stride(16, 3)
+
+
+def test_skeleton_selection_uses_only_the_probes():
+    """Changing non-probe queries leaves the mask alone; with one probe per
+    block the mask equals brute-force scoring of each block's first query."""
+    q, k, v = synth.make_sequence(320, 4, 2, 16, seed=13, verticals=False)
+    q, k, v = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    a = O.select_blocks(q, k, v, 32, 0.3, probes=4)
+    q2 = q.copy()
+    q2[np.arange(320) % 8 != 0] += 5.0
+    b = O.select_blocks(q2, k, v, 32, 0.3, probes=4)
+    assert np.array_equal(a.keep, b.keep) and np.array_equal(a.q_bar, b.q_bar)
+    assert not np.array_equal(O.select_blocks(q2, k, v, 32, 0.3).q_bar, a.q_bar)
+    one = O.select_blocks(q, k, v, 32, 0.3, probes=1)
+    keep_bf, band_bf = _brute_force_keep(q[::32].repeat(32, axis=0)[:320], k, 32, 0.3)
+    outside = ~(one.band | band_bf)
+    assert np.array_equal(one.keep[outside], keep_bf[outside])
+    full = O.select_blocks(q, k, v, 32, 0.3, probes=32)
+    assert np.array_equal(full.keep, O.select_blocks(q, k, v, 32, 0.3).keep)
