@@ -151,8 +151,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(alpha, steps, warmup, shared=False):
-        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr, shared_selection=shared)
+    def measure(alpha, steps, warmup, shared=False, probes=0):
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr, shared_selection=shared,
+                           query_probes=probes)
         sel = fp.alloc_selection(p, S, dev)
         fs = lambda: fp.fp_select_blocks(p, qd, kd, vd, sel=sel)
         fa = lambda: fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, out=out)
@@ -198,6 +199,17 @@ def main():
                                          density=round(r["density"], 5),
                                          attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2))
         log(f"bench: shared selection {extra['shared_selection']}")
+        del r
+        # skeleton-query scoring: q_bar from 16 uniformly spaced queries per block
+        r = measure(args.alpha, max(3, args.steps // 2), 1, probes=16)
+        fa_ = r["f_kept"] + r["f_corr"]
+        jac = mask_agreement(head["sel"], r["sel"], S, Hq, B, dev)
+        extra["skeleton_queries"] = dict(alpha=args.alpha, probes=16, ms_per_step=round(r["ms_per_step"], 4),
+                                         select_ms=round(r["select_ms"], 4), attn_ms=round(r["attn_ms"], 4),
+                                         density=round(r["density"], 5),
+                                         attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2),
+                                         kept_jaccard_vs_full_pooling=round(jac, 4))
+        log(f"bench: skeleton queries {extra['skeleton_queries']}")
         del r
         # dense references on the same GPU
         dense = measure(0.0, 2, 1)
@@ -257,6 +269,28 @@ def main():
     }
     rec.update(extra)
     print(json.dumps(rec), flush=True)
+
+
+def mask_agreement(sel_a, sel_b, S, Hq, B, dev):
+    """|A and B| / |A or B| over the kept (head, query block, KV block) triples
+    of two single-sequence selections."""
+    import torch
+    nB = (S + B - 1) // B
+
+    def mask(sel):
+        cnt = sel.kv_cnt.reshape(-1).to(torch.int64)                          # [Hq * nB], row = h * nB + I
+        rows = torch.arange(Hq * nB, device=dev)
+        h, I = rows // nB, rows % nB
+        base = h * (nB * (nB + 1) // 2) + I * (I + 1) // 2
+        r = torch.repeat_interleave(rows, cnt)
+        j = torch.arange(int(cnt.sum()), device=dev) - torch.repeat_interleave(torch.cumsum(cnt, 0) - cnt, cnt)
+        cols = sel.kv_idx.to(torch.int64)[torch.repeat_interleave(base, cnt) + j]
+        m = torch.zeros(Hq * nB * nB, dtype=torch.bool, device=dev)
+        m[r * nB + cols] = True
+        return m
+
+    a, b = mask(sel_a), mask(sel_b)
+    return float((a & b).sum()) / max(1.0, float((a | b).sum()))
 
 
 def timed_ms(fn, n, stream):

@@ -30,7 +30,7 @@ class fp_params(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("softmax_scale", ctypes.c_float),
                 ("mean_correction", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("shared_selection", ctypes.c_int32)]
+                ("shared_selection", ctypes.c_int32), ("query_probes", ctypes.c_int32)]
 
 
 class FlashPrefillError(RuntimeError):
@@ -91,10 +91,11 @@ def _check(status: int):
 
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, alpha, mean_correction=True,
-                softmax_scale=0.0, dtype=FP_DTYPE_BF16, shared_selection=False) -> fp_params:
+                softmax_scale=0.0, dtype=FP_DTYPE_BF16, shared_selection=False,
+                query_probes=0) -> fp_params:
     return fp_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
                      float(alpha), float(softmax_scale), int(bool(mean_correction)), int(dtype),
-                     int(bool(shared_selection)))
+                     int(bool(shared_selection)), int(query_probes))
 
 
 def _ptr(t: Optional[torch.Tensor]):

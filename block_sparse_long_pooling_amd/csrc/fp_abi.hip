@@ -63,6 +63,9 @@ int check_params(const fp_params* p) {
         return fail(FP_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
     if (p->shared_selection != 0 && p->shared_selection != 1)
         return fail(FP_INVALID_ARGUMENT, "shared_selection must be 0 or 1");
+    if (p->query_probes < 0 || (p->query_probes > 0 && p->block_size % p->query_probes != 0))
+        return fail(FP_INVALID_ARGUMENT, "query_probes (%d) must be 0 or divide block_size (%d)", p->query_probes,
+                    p->block_size);
     return FP_OK;
 }
 
@@ -169,6 +172,7 @@ int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, in
     pa.Hkv = p.num_kv_heads;
     pa.D = p.head_dim;
     pa.B = p.block_size;
+    pa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
     pa.q_chunks = p.num_q_heads * p.head_dim / 8;
     pa.k_chunks = p.num_kv_heads * p.head_dim / 8;
     pa.total_chunks = pa.q_chunks + pa.k_chunks * (pool_v ? 2 : 1);
@@ -322,6 +326,7 @@ FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const
     qa.D = p.head_dim;
     qa.B = p.block_size;
     qa.nB = t.total_blocks;
+    qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     rc = device_status(launch_quant_pool(qa, st), "quantize + pool");

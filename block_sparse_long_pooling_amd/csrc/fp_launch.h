@@ -17,6 +17,7 @@ struct PoolArgs {
     int32_t reuse;       // prefix blocks: read their means from pcache instead of pooling
     KVLayout kv;
     int32_t Hq, Hkv, D, B;
+    int32_t q_stride;    // Q_bar averages the block's tokens 0, q_stride, 2 q_stride, ...
     int32_t q_chunks;    // Hq * d / 8
     int32_t k_chunks;    // Hkv * d / 8
     int32_t total_chunks;
@@ -64,6 +65,7 @@ struct QuantArgs {
     int32_t H[3];                // Hq, Hkv, Hkv
     int32_t groups[3];           // head groups per tensor (set by the launcher)
     int32_t S, D, B, nB;
+    int32_t q_stride;            // Q_bar averages the block's tokens 0, q_stride, 2 q_stride, ...
 };
 
 hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s);

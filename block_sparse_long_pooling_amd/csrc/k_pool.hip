@@ -47,10 +47,12 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
         // (chunked prefill) have no queries here.
         if (I < first) return;
         const int col = c * 8;
-        const int64_t row_elems = (int64_t)a.Hq * a.D;
-        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B) * row_elems + col;
+        // With skeleton queries only every q_stride-th token of the block counts.
+        const int64_t row_elems = (int64_t)a.Hq * a.D * a.q_stride;
+        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B) * a.Hq * a.D + col;
+        const int nq = (n + a.q_stride - 1) / a.q_stride;
         int r = 0;
-        for (; r + kUnroll <= n; r += kUnroll) {
+        for (; r + kUnroll <= nq; r += kUnroll) {
             uint4 x[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
@@ -58,8 +60,8 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
         }
-        for (; r < n; ++r) add8(acc, *reinterpret_cast<const uint4*>(p + (int64_t)r * row_elems));
-        const float fn = (float)n;
+        for (; r < nq; ++r) add8(acc, *reinterpret_cast<const uint4*>(p + (int64_t)r * row_elems));
+        const float fn = (float)nq;
 #pragma unroll
         for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
         const int64_t off = ((int64_t)(col / a.D) * t.total_qblocks + qblock_row(t, b, I)) * a.D + col % a.D;

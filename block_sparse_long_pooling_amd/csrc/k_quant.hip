@@ -69,14 +69,19 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
     }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float amax = 0.f;
+    // Q_bar may average only the skeleton queries (every q_stride-th token).
+    const int stride = ts == 0 ? a.q_stride : 1;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+        const bool counted = (2 * kWaves * s + 2 * w + hf) % stride == 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
-            sum[2 * i] += lo;
-            sum[2 * i + 1] += hi;
+            if (counted) {
+                sum[2 * i] += lo;
+                sum[2 * i + 1] += hi;
+            }
             amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
         }
     }
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
             float t = psum[0][ch][i];
 #pragma unroll
             for (int w2 = 1; w2 < kWaves; ++w2) t += psum[w2][ch][i];
-            m[i] = t / (float)n;
+            m[i] = t / (float)((n + stride - 1) / stride);
         }
         const int64_t off = ((int64_t)h * a.nB + J) * D + (ch % CPH) * 8;
         float* dst = ts == 0 ? a.pq : (ts == 1 ? a.pk : nullptr);

@@ -72,6 +72,10 @@ typedef struct {
                                  1: the g = Hq/Hkv query heads of a KV head share one list,
                                  the union of their own lists (every head of a group then
                                  runs on every tile fetched for the group) */
+    int32_t query_probes;     /* 0: q_bar is the mean of every query of the block (step 1);
+                                 P dividing block_size: the mean of the skeleton queries at
+                                 offsets 0, st, 2 st, ... of the block, st = block_size / P
+                                 (FlashPrefill 2.A); a partial block keeps the probes it has */
 } fp_params;
 
 /*

@@ -207,3 +207,10 @@ def test_shared_selection_flag_validated():
     p.shared_selection = 2
     assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) == -1
     assert "shared_selection" in fp.lib().fp_last_error().decode()
+
+
+def test_query_probes_validated():
+    c = (ctypes.c_int32 * 2)(0, 1024)
+    for probes, ok in ((0, True), (1, True), (16, True), (128, True), (3, False), (-1, False), (256, False)):
+        p = _p(query_probes=probes)
+        assert (fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) > 0) == ok, probes

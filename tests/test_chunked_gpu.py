@@ -157,3 +157,31 @@ def test_pooled_cache_carries_the_prefix_between_calls():
             pg = int(pb.block_table[b, J * B // page])
             np.testing.assert_allclose(cache[0, pg].cpu().numpy(), kbar[:, J], atol=1e-5, rtol=0)
             np.testing.assert_allclose(cache[1, pg].cpu().numpy(), vbar[:, J], atol=1e-5, rtol=0)
+
+
+def test_chunked_with_skeleton_queries_and_shared_lists():
+    """The selection options apply to chunks as to whole prompts: chunk rows
+    stay bit-identical to the whole-prompt entry with the same options."""
+    lengths, starts, Hq, Hkv, d, B, page = CASES[0]
+    pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=61, verticals=True, page_size=page)
+    for shared, probes in ((False, 16), (True, 0), (True, 4)):
+        p = fp.make_params(Hq, Hkv, d, B, 0.2, mean_correction=True, shared_selection=shared,
+                           query_probes=probes)
+        full = fp.fp_sparse_prefill_varlen_paged(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
+                                                 pb.block_table.to(dev()), pb.cu_seqlens, return_lse=True)
+        q, cu, kv_lens = _chunks(pb, starts)
+        res = fp.fp_sparse_prefill_chunked_paged(p, q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
+                                                 pb.block_table.to(dev()), cu, kv_lens, return_lse=True)
+        torch.cuda.synchronize()
+        for b, P0 in enumerate(starts):
+            f0, f1 = int(pb.cu_seqlens[b]) + P0, int(pb.cu_seqlens[b + 1])
+            assert torch.equal(res.out[cu[b]:cu[b + 1]], full.out[f0:f1]), (shared, probes, b)
+        # and the chunk's lists are the oracle's with the same options
+        masks = _masks(res, Hq, kv_lens, starts, B)
+        for b, (L, P0) in enumerate(zip(kv_lens, starts)):
+            if L == P0:
+                continue
+            qb, kb, vb = (t.float().numpy() for t in pb.requests[b])
+            ref = O.select_blocks_chunked(qb[P0:], kb, vb, B, 0.2, shared=shared, probes=probes)
+            outside, inside, band = compare_mask(masks[b], ref)
+            assert outside == 0, (shared, probes, b, outside)

@@ -78,3 +78,18 @@ def test_attention_on_prepared_inputs(shape, alpha, corr):
     lerr = np.abs(lse.cpu().numpy() - lse_ref).max()
     print(f"  {shape} alpha={alpha} corr={corr}: max|o-ref| {err:.3e} max|lse-ref| {lerr:.3e}", flush=True)
     assert err <= FP8_TOL and lerr <= 5e-2
+
+
+def test_prep_with_skeleton_queries():
+    S, Hq, Hkv, d, B = 1000, 4, 2, 128, 128
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, seed=31, verticals=True)
+    p8 = fp.make_params(Hq, Hkv, d, B, 0.2, mean_correction=True, dtype=fp.FP_DTYPE_FP8_E4M3FN, query_probes=16)
+    sel, f8 = fp.fp_select_blocks_fp8(p8, q.to(dev()), k.to(dev()), v.to(dev()))
+    torch.cuda.synchronize()
+    ref = O.select_blocks(q.float().numpy(), k.float().numpy(), v.float().numpy(), B, 0.2, probes=16)
+    np.testing.assert_allclose(sel.pooled_q.cpu().numpy(), ref.q_bar, rtol=0, atol=2e-6)
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, (S + B - 1) // B)
+    outside, inside, band = compare_mask(mask, ref)
+    assert outside == 0
+    c_ref, s_ref = O.quantize_fp8_blockwise(q.float().numpy(), B)       # codes do not depend on the probes
+    assert np.array_equal(f8.q8.cpu().numpy(), c_ref) and np.array_equal(f8.q_scale.cpu().numpy(), s_ref)

@@ -153,3 +153,30 @@ def test_shared_selection(shape, alpha):
     lerr = np.abs(lse.cpu().numpy() - lse_ref).max()
     print(f"  kept {int(mask.sum())} (own {int(own.keep.sum())}) err {err:.3e} lse {lerr:.3e}", flush=True)
     assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("probes", [1, 8, 0])
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[3], SHAPES[6]], ids=lambda s: "S%d_h%d-%d_d%d_B%d" % s[:5])
+def test_skeleton_queries(shape, probes):
+    """q_bar from the skeleton queries (every (B/P)-th query of a block):
+    pooled means, masks and outputs match the oracle with the same probes."""
+    S, Hq, Hkv, d, B, vert = shape
+    print(f"skeleton queries {shape} probes={probes}", flush=True)
+    q, k, v = _case(*shape, seed=9)
+    p = fp.make_params(Hq, Hkv, d, B, 0.2, mean_correction=True, query_probes=probes)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    sel = fp.fp_select_blocks(p, qd, kd, vd)
+    out, lse = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, return_lse=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = oracle_inputs(q, k, v)
+    ref = O.select_blocks(qn, kn, vn, B, 0.2, probes=probes)
+    np.testing.assert_allclose(sel.pooled_q.cpu().numpy(), ref.q_bar, rtol=0, atol=2e-6 * max(1.0, np.abs(ref.q_bar).max()))
+    nB = (S + B - 1) // B
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    outside, inside, band = compare_mask(mask, ref)
+    assert outside == 0, (outside, inside, band)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, ref, True, keep=mask)
+    err = np.abs(out.float().cpu().numpy() - o_ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lse_ref).max()
+    print(f"  kept {int(mask.sum())} err {err:.3e} lse {lerr:.3e}", flush=True)
+    assert err <= BF16_TOL and lerr <= LSE_TOL
