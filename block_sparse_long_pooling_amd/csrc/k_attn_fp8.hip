@@ -16,12 +16,16 @@
 // 32x32 output layout of S^T is directly the byte layout of the PV B operand
 // (position p holds key  32*p[4] + 8*p[3:2] + 4*p[5] + p[1:0]).
 //
-// The mean correction (pooled fp32 K_bar / V_bar) runs on the bf16 pipeline
-// with Q dequantized to bf16.
-#include "fp_attn.h"
+// The mean correction runs on the bf16 pipeline with Q dequantized to bf16:
+// the bf16 pooled K_bar / V_bar rows of 64 past blocks at a time arrive by
+// DMA into one of two LDS buffers (the tile buffers of the kept walk) while
+// the previous 64 are computed, K_bar read row-major and V_bar with the
+// transposing LDS read, as in the bf16 kernel.
+#include "attn_walk.h"
 
 namespace {
 using namespace fp_attn;
+using namespace fp_walk;
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
@@ -180,6 +184,90 @@ __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, fl
     }
 }
 
+// Mean-correction pass over the skipped past blocks J < I of row block I:
+// BLK/2 pooled blocks per step, double-buffered DMA into buf0 / buf1 (each a
+// [BLK][D] bf16 tile buffer: BLK/2 K_bar rows, then BLK/2 V_bar rows, chunks
+// swizzled per row).
+template <int D, int BLK>
+__device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable& t, int b, int I, int hk, int cnt,
+                                               const int32_t* list, const bf16x8* qf, char* buf0, char* buf1,
+                                               uint32_t* kept_bits, int tid, int col, int half, float c, float& m,
+                                               float& l, f32x16* o) {
+    constexpr int NT = 2 * BLK;                          // threads
+    constexpr int HT = BLK / 2;                          // pooled blocks per step
+    constexpr int NS = HT / 32;                          // 32-key subtiles per step
+    constexpr int HALF = HT * D * 2;                     // bytes of K_bar (or V_bar) rows per step
+    const int lane = tid & 63;
+    const int nwords = (I + 31) >> 5;
+    for (int i = tid; i < nwords; i += NT) kept_bits[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += NT) {
+        const int J = list[i];
+        if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    const uint16_t* kfirst = a.pk16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
+    const uint16_t* vfirst = a.pv16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
+    DmaPlan<D, HT, NT> plan;
+    plan.init(tid);
+    const int wave_base = __builtin_amdgcn_readfirstlane(64 * (tid >> 6) * 16);
+    const float log2_blk = __log2f((float)BLK);          // every block J < I is full
+    const int nht = (I + HT - 1) / HT;
+    // Skip bits of step hh: bit j of word sub <=> block HT hh + 32 sub + j is past and not kept.
+    auto skips = [&](int hh, uint32_t* sk) {
+        uint32_t any = 0;
+#pragma unroll
+        for (int sub = 0; sub < NS; ++sub) {
+            const int j0 = HT * hh + 32 * sub;
+            const int nvalid = min(32, max(0, I - j0));
+            const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+            sk[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[j0 >> 5] & valid);
+            any |= sk[sub];
+        }
+        return any != 0;
+    };
+    auto next_step = [&](int hh) {
+        uint32_t sk[NS];
+        for (++hh; hh < nht; ++hh)
+            if (skips(hh, sk)) return hh;
+        return nht;
+    };
+    auto issue = [&](int hh, char* dst) {
+        const int nvalid = I - HT * hh;
+        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
+        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
+    };
+    f32x16 s[NS];
+    uint32_t pk[NS][8];
+    int cur = next_step(-1);
+    if (cur < nht) issue(cur, buf0);
+    auto step = [&](char* bcur, char* bnext) {
+        __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
+        lds_barrier();                                   // ... every thread's; the other buffer is free
+        const int nxt = next_step(cur);
+        if (nxt < nht) issue(nxt, bnext);
+        uint32_t sk[NS];
+        skips(cur, sk);
+        qk<D, BLK, 1, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+#pragma unroll
+        for (int sub = 0; sub < NS; ++sub) {
+            const uint32_t bits = sk[sub] >> (4 * half);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
+        }
+        softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
+        pv<D, BLK, 1, 0, NS>(bcur + HALF, pk, lane, o);
+        cur = nxt;
+    };
+    while (cur < nht) {
+        step(buf0, buf1);
+        if (cur >= nht) break;
+        step(buf1, buf0);
+    }
+    lds_barrier();                                       // buffers free for the output staging
+}
+
 template <int D, int BLK>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t) {
     using T = Tile<D, BLK>;          // bf16 geometry: LDS sized for the correction tiles
@@ -274,8 +362,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
                                         pack_bf16(f2.x * sq, f2.y * sq), pack_bf16(f3.x * sq, f3.y * sq));
             qb[kk] = __builtin_bit_cast(bf16x8, pk);
         }
-        correction_pass<D, BLK>(a, t, b, I, hk, cnt, list, qb, lk, lv, kept_bits, tid, col, half, a.scale_log2,
-                                m, l, o);
+        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, qb, reinterpret_cast<char*>(lk),
+                               reinterpret_cast<char*>(lv), kept_bits, tid, col, half, a.scale_log2, m, l, o);
     }
     store_output<D, BLK>(a, t, h, q0, nI, qr, half, m, l, o, lk, tid);
 }
