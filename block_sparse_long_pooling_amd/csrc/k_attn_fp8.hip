@@ -11,10 +11,11 @@
 // per-tile rescale of the O accumulator: O holds sum P (V8) in units of the
 // current tile's scale.
 //
-// LDS: the K8 tile is [BLK][D] bytes; the V8 tile is stored transposed,
-// [D][BLK] bytes, with keys permuted inside each 64-key step so that the
-// 32x32 output layout of S^T is directly the byte layout of the PV B operand
-// (position p holds key  32*p[4] + 8*p[3:2] + 4*p[5] + p[1:0]).
+// LDS: K8 and V8 tiles are row-major [BLK][D] bytes (16-byte chunks XOR-
+// swizzled per row), DMA'd into one of two buffers while the other is
+// computed on.  The V^T operand is read with ds_read_b64_tr_b8, gathering per
+// lane the keys in the order in which the P registers hold them, so P is the
+// PV operand as it stands.
 //
 // The mean correction runs on the bf16 pipeline with Q dequantized to bf16:
 // the bf16 pooled K_bar / V_bar rows of 64 past blocks at a time arrive by
@@ -31,118 +32,73 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 constexpr int kNeutralScale = 127;   // E8M0 code of 1.0 for the MFMA block scales
 
-__device__ __forceinline__ int key_perm8(int p) {
-    const int q = p & 63;
-    return (p & ~63) | (((q >> 4) & 1) << 5) | (((q >> 2) & 3) << 3) | (((q >> 5) & 1) << 2) | (q & 3);
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ i32x8 cat8(const uint4& x, const uint4& y) {
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-// 4x4 byte transpose: a[u] byte j -> c[j] byte u.
-__device__ __forceinline__ void transpose4b(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t* c) {
-    const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-    const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-    const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-    const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-    c[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-    c[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-    c[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-    c[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
-template <int D, int BLK>
-struct Tile8 {
-    static constexpr int KCH = D / 16;    // 16-byte chunks per K8 row
-    static constexpr int VCH = BLK / 16;  // 16-byte chunks per V8^T row
-    static constexpr int NT = 2 * BLK;
-};
-
-template <int D, int BLK>
-__device__ __forceinline__ void load_kv8_tile(const uint8_t* k8, const uint8_t* v8, int tok0, int len, int J, int Hkv,
-                                              int hk, uint4* lk, uint2* lv2, int tid) {
-    using T = Tile8<D, BLK>;
-    const int64_t rs = (int64_t)Hkv * D;
-    for (int i = tid; i < BLK * T::KCH; i += T::NT) {
-        const int row = i / T::KCH, ch = i % T::KCH;
-        const int tr = J * BLK + row;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (tr < len) val = *reinterpret_cast<const uint4*>(k8 + (tok0 + tr) * rs + (int64_t)hk * D + ch * 16);
-        lk[row * T::KCH + (ch ^ (row % T::KCH))] = val;
-    }
-    // (position group of 8, d group of 8) per thread: 8x8 byte transpose.
-    for (int i = tid; i < (BLK / 8) * (D / 8); i += T::NT) {
-        const int pg = i / (D / 8), dc = i % (D / 8);
-        uint2 x[8];
+// S^T = K8 Q8^T for subtiles SUB0 .. SUB0+NS-1 (64 bytes of d per MFMA).  A
+// operand of lane l: key row 32 sub + l%32, d bytes 32 (l/32) + 64 kk .. +31.
+template <int D, int SUB0, int NS>
+__device__ __forceinline__ void qk8(const uint4* kt, const i32x8* qf, int col, int half, f32x16* s) {
+    constexpr int NCH = D / 16;                  // 16-byte chunks per fp8 row
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int tr = J * BLK + key_perm8(8 * pg + u);
-            x[u] = make_uint2(0, 0);
-            if (tr < len) x[u] = *reinterpret_cast<const uint2*>(v8 + (tok0 + tr) * rs + (int64_t)hk * D + dc * 8);
-        }
-        uint32_t c0[4], c1[4], c2[4], c3[4];
-        transpose4b(x[0].x, x[1].x, x[2].x, x[3].x, c0);   // keys 0-3, d 0-3
-        transpose4b(x[0].y, x[1].y, x[2].y, x[3].y, c1);   // keys 0-3, d 4-7
-        transpose4b(x[4].x, x[5].x, x[6].x, x[7].x, c2);   // keys 4-7, d 0-3
-        transpose4b(x[4].y, x[5].y, x[6].y, x[7].y, c3);   // keys 4-7, d 4-7
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int d = 8 * dc + j;
-            const uint2 y = j < 4 ? make_uint2(c0[j], c2[j]) : make_uint2(c1[j - 4], c3[j - 4]);
-            lv2[2 * (d * T::VCH + ((pg >> 1) ^ (d % T::VCH))) + (pg & 1)] = y;
-        }
-    }
-}
-
-template <int D, int BLK>
-__device__ __forceinline__ i32x8 lds_pair(const uint4* base, int row, int nch, int ch) {
-    const uint4 a = base[row * nch + (ch ^ (row % nch))];
-    const uint4 b = base[row * nch + ((ch + 1) ^ (row % nch))];
-    i32x8 r = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-    return r;
-}
-
-template <int D, int BLK, int NSUB>
-__device__ __forceinline__ void qk8_tile(const uint4* lk, const i32x8* qf, int col, int half, f32x16* s) {
-    using T = Tile8<D, BLK>;
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-        f32x16 acc = {};
+    for (int j = 0; j < NS; ++j) {
+        const int row = 32 * (SUB0 + j) + col;
+        uint4 av[2 * (D / 64)];
 #pragma unroll
         for (int kk = 0; kk < D / 64; ++kk) {
-            const i32x8 a = lds_pair<D, BLK>(lk, 32 * sub + col, T::KCH, 2 * half + 4 * kk);
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[kk], acc, 0, 0, 0, kNeutralScale, 0,
-                                                                  kNeutralScale);
+            av[2 * kk] = kt[row * NCH + ((2 * half + 4 * kk) ^ swz<D / 2>(row))];
+            av[2 * kk + 1] = kt[row * NCH + ((2 * half + 4 * kk + 1) ^ swz<D / 2>(row))];
         }
-        s[sub] = acc;
+        __builtin_amdgcn_sched_barrier(0);       // keep the reads ahead of the MFMA chain
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk)
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(av[2 * kk], av[2 * kk + 1]), qf[kk], acc, 0, 0,
+                                                                  0, kNeutralScale, 0, kNeutralScale);
+        s[j] = acc;
     }
 }
 
-template <int D, int BLK, int NDS>
-__device__ __forceinline__ void pv8_tile(const uint4* lv, const uint32_t (*ph)[4], const uint32_t (*pl)[4], int col,
-                                         int half, f32x16* o) {
-    using T = Tile8<D, BLK>;
+// O^T[ds] += V^T P^T over the 64-key step ST (keys 64 ST ..).  The A operand
+// of lane l (group g = l/16, i = l%16, h = l/32) holds d = 32 ds + 16 (g&1) + i
+// and the 32 keys 64 ST + 4 h + 16 t + {0,1,2,3, 8,9,10,11} (t = 0..3) -- the
+// order in which the P registers of subtiles 2 ST and 2 ST + 1 hold their
+// keys.  ds_read_b64_tr_b8 gives output lane i of a 16-lane group byte i mod 8
+// of the 8-byte reads of source lanes (i div 8) + 2m, m = 0..7; so source lane
+// 2m + p reads key row m of the set at d bytes 32 ds + 16 (g&1) + 8 p.
+template <int D, int ST>
+__device__ __forceinline__ void pv8(const char* vt, const uint32_t (*ph)[4], const uint32_t (*pl)[4], int lane,
+                                    f32x16* o) {
+    const int gl = lane & 15, g = lane >> 4;
+    const int h = g >> 1, m = gl >> 1, p = gl & 1;
+    const int krow = 64 * ST + 4 * h + (m & 3) + 8 * (m >> 2);
+    const i32x8 bh = {(int)ph[0][0], (int)ph[0][1], (int)ph[0][2], (int)ph[0][3],
+                      (int)ph[1][0], (int)ph[1][1], (int)ph[1][2], (int)ph[1][3]};
+    const i32x8 bl = {(int)pl[0][0], (int)pl[0][1], (int)pl[0][2], (int)pl[0][3],
+                      (int)pl[1][0], (int)pl[1][1], (int)pl[1][2], (int)pl[1][3]};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
+    for (int ds = 0; ds < D / 32; ++ds) {
+        const int dbyte = 32 * ds + 16 * (g & 1) + 8 * p;
+        i32x2 part[4];
 #pragma unroll
-        for (int st = 0; st < BLK / 64; ++st) {
-            const i32x8 a = lds_pair<D, BLK>(lv, 32 * ds + col, T::VCH, 4 * st + 2 * half);
-            const uint32_t* h0 = ph[2 * st];
-            const uint32_t* h1 = ph[2 * st + 1];
-            const uint32_t* l0 = pl[2 * st];
-            const uint32_t* l1 = pl[2 * st + 1];
-            const i32x8 bh = {(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3],
-                              (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-            const i32x8 bl = {(int)l0[0], (int)l0[1], (int)l0[2], (int)l0[3],
-                              (int)l1[0], (int)l1[1], (int)l1[2], (int)l1[3]};
-            o[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bh, o[ds], 0, 0, 0, kNeutralScale, 0,
-                                                                    kNeutralScale);
-            o[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bl, o[ds], 0, 0, 0, kNeutralScale, 0,
-                                                                    kNeutralScale);
+        for (int t = 0; t < 4; ++t) {
+            const int key = krow + 16 * t;
+            const char* addr = vt + key * D + (((dbyte >> 4) ^ swz<D / 2>(key)) << 4) + (dbyte & 15);
+            part[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)addr);
         }
+        __builtin_amdgcn_sched_barrier(0);       // keep the reads ahead of the MFMAs
+        const i32x8 av = {part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+        o[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bh, o[ds], 0, 0, 0, kNeutralScale, 0,
+                                                                kNeutralScale);
+        o[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bl, o[ds], 0, 0, 0, kNeutralScale, 0,
+                                                                kNeutralScale);
     }
 }
 
-// Exact online softmax for fp8 tiles.  c = logit scale of this tile (log2
-// units); vr = previous V scale / this tile's V scale.  With e = 2^8 p:
-// ph = e4m3(e), pl = e4m3(e - ph); the row sum takes e itself.
 template <int NSUB, int NDS>
 __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, float& m, float& l, f32x16* o,
                                                 uint32_t (*ph)[4], uint32_t (*pl)[4]) {
@@ -317,12 +273,31 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     float sv_prev = 1.f;
     const float cq = sq * a.scale_log2;
 
-    for (int it = 0; it < cnt; ++it) {
+    // Kept tiles through two DMA buffers (lk for even steps, lv for odd):
+    // K8 rows at the buffer's start, V8 rows after them.
+    constexpr int NTH = 2 * BLK;
+    constexpr int VOFF = BLK * D;                        // bytes of a K8 (or V8) tile
+    DmaPlan<D / 2, BLK, NTH> plan;
+    plan.init(tid);
+    const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
+    const int64_t rs2 = (int64_t)a.Hkv * D / 2;          // row stride in 2-byte units
+    const uint16_t* kfirst = reinterpret_cast<const uint16_t*>(k8 + ((int64_t)tok0 * a.Hkv + hk) * D);
+    const uint16_t* vfirst = reinterpret_cast<const uint16_t*>(v8 + ((int64_t)tok0 * a.Hkv + hk) * D);
+    auto issue8 = [&](int J, char* dst) {
+        issue_tile<D / 2, BLK, NTH, false>(kfirst, nullptr, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk, dst,
+                                           wave_base);
+        issue_tile<D / 2, BLK, NTH, false>(vfirst, nullptr, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk,
+                                           dst + VOFF, wave_base);
+    };
+    char* buf0 = reinterpret_cast<char*>(lk);
+    char* buf1 = reinterpret_cast<char*>(lv);
+    if (cnt > 0) issue8(list[0], buf0);
+    auto step = [&](int it, char* bcur, char* bnext) {
+        __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of tile it is done
+        lds_barrier();                                   // ... every thread's; the other buffer is free
+        if (it + 1 < cnt) issue8(list[it + 1], bnext);
         const int J = list[it];
-        __syncthreads();
-        load_kv8_tile<D, BLK>(k8, v8, tok0, len, J, a.Hkv, hk, lk, reinterpret_cast<uint2*>(lv), tid);
-        __syncthreads();
-        qk8_tile<D, BLK, T::NSUB>(lk, qf, col, half, s);
+        qk8<D, 0, T::NSUB>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
         if (J == I) {
 #pragma unroll
             for (int sub = 0; sub < T::NSUB; ++sub)
@@ -336,8 +311,14 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         const float sv = a.v_scale[(int64_t)hk * t.total_blocks + sblk + J];
         softmax8_update<T::NSUB, T::NDS>(s, cq * sk, sv_prev / sv, m, l, o, ph, pl);
         sv_prev = sv;
-        pv8_tile<D, BLK, T::NDS>(lv, ph, pl, col, half, o);
+        pv8<D, 0>(bcur + VOFF, ph, pl, lane, o);
+        if (BLK == 128) pv8<D, (BLK == 128 ? 1 : 0)>(bcur + VOFF, ph + 2, pl + 2, lane, o);
+    };
+    for (int it = 0; it < cnt; it += 2) {
+        step(it, buf0, buf1);
+        if (it + 1 < cnt) step(it + 1, buf1, buf0);
     }
+    lds_barrier();                                       // all reads of the last tile are done
     // Back to plain units: O * sv / 2^8, l / 2^8.
     {
         const float f = sv_prev * (1.f / 256.f);
