@@ -76,7 +76,7 @@ float sigma_of(const fp_params& p) {
 // Validate cu_seqlens_host (query tokens per request) and, for chunked
 // prefill, kv_lens_host (context length per request; NULL: equal to the query
 // count), and fill the request table.  items_per_tile = 1 counts query
-// blocks; TI counts tiles of TI query blocks (selection).
+// blocks; n > 1 counts tiles of n query blocks (selection workgroups).
 int build_table(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, int items_per_tile,
                 SeqTable& t) {
     if (!cu) return fail(FP_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
@@ -187,7 +187,7 @@ int run_scores(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, in
     int rc;
     SeqTable ts;
     const int TI = select_tile(p);
-    rc = build_table(p, cu, kv_lens, batch, TI, ts);
+    rc = build_table(p, cu, kv_lens, batch, kSelectRowWaves * TI, ts);
     if (rc) return rc;
     SelArgs sa;
     sa.pq = pq;

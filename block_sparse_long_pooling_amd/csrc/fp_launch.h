@@ -23,12 +23,15 @@ struct PoolArgs {
     int32_t total_chunks;
 };
 
+// A selection workgroup holds kSelectRowWaves row waves of 32 score rows, i.e.
+// kSelectRowWaves * TI consecutive query blocks of one KV head.
+constexpr int kSelectRowWaves = 4;
 struct SelArgs {
     const float* pq;
     const float* pk;
     int32_t* kv_idx;
     int32_t* kv_cnt;
-    int32_t Hq, Hkv, g, D, TI;   // TI query blocks x g heads per workgroup (TI * g <= 32)
+    int32_t Hq, Hkv, g, D, TI;   // TI query blocks x g heads per row wave (TI * g <= 32)
     float scale;                 // sigma
     float ln_alpha;              // threshold on s - max s (-inf keeps every causal block)
     int32_t shared;              // 1: the g heads of a query block share the union of their lists

@@ -6,11 +6,16 @@
 // the row's largest, i.e. s[J] - max_J s >= ln(alpha).  Kept blocks are
 // written in ascending J to the (h, I) list, which is never empty.
 //
-// A workgroup owns 32 score rows: TI consecutive query blocks x the g query
-// heads of one KV head, so every k_bar row it loads serves 32 rows.  The
-// (L/B)^2 score matrix is never stored: phase 1 takes each row's max, phase 2
-// recomputes the same scores (same instruction sequence, bit-identical) into
-// a keep bitmap in LDS, phase 3 compacts it in ascending J.  The dot products run on bf16 MFMA with each
+// A workgroup of 8 waves owns up to 128 score rows of one KV head: 4 row
+// waves, each 32 rows = TI consecutive query blocks x the g query heads, and
+// 2 column groups.  The k_bar rows stream through LDS in column tiles of 32
+// blocks, two tiles per step (one per column group), split once per
+// workgroup into bf16 hi + lo parts; every tile then serves all the rows of
+// the workgroup.  The next step's rows are loaded into registers while the
+// current step computes.  The (L/B)^2 score matrix is never stored: phase 1
+// takes each row's max, phase 2 recomputes the same scores (same
+// instruction sequence, bit-identical) into a keep bitmap in LDS, phase 3
+// compacts it in ascending J.  The dot products run on bf16 MFMA with each
 // fp32 operand split into hi + lo bf16 parts (hi*hi + hi*lo + lo*hi), which
 // is within ~2^-17 of the fp32 product sum -- far below the 1e-3 band in
 // which the threshold decision is allowed to differ from an exact one.
@@ -22,6 +27,13 @@
 
 namespace {
 
+constexpr int kRowWaves = kSelectRowWaves;
+constexpr int kColGroups = 2;
+constexpr int kWaves = kRowWaves * kColGroups;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowSlots = 32 * kRowWaves;
+constexpr int kMaxColTiles = FP_MAX_BLOCKS / 2 / 32;   // 32-block column tiles per row
+
 __device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& lo) {
     float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -32,186 +44,284 @@ __device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x
     }
 }
 
-// Three independent MFMA chains (hi*hi, hi*lo, lo*hi) summed in a fixed
-// order: the same instruction sequence gives the same bits in every pass.
+// LDS stage of one column tile: hi and lo bf16 parts of 32 k_bar rows, row
+// J at chunks [J * D/8, (J + 1) * D/8) of 16 bytes, chunk c stored at
+// c ^ (J mod D/8) so that the 32 rows' reads of one chunk spread over the
+// banks.
 template <int D>
-__device__ __forceinline__ f32x16 tile_scores(const bf16x8* qh, const bf16x8* ql, const float4* kb, float scale) {
-    f32x16 a0 = {}, a1 = {}, a2 = {};
+struct TileStage {
+    uint4 part[2][32 * D / 8];
+};
+
+template <int D>
+__device__ __forceinline__ int chunk_slot(int J, int c) {
+    return J * (D / 8) + (c ^ (J & (D / 8 - 1)));
+}
+
+// Staging: thread -> (column group, k_bar row J in the tile, D/8 consecutive
+// floats of that row).
+template <int D>
+struct Stager {
+    static constexpr int F = D / 8;            // floats per thread
+    int cg, J, seg;
+    __device__ __forceinline__ Stager(int tid) : cg(tid / 256), J((tid % 256) / 8), seg(tid % 8) {}
+    // Rows past the workgroup's last column block (ncol - 1) re-read that
+    // block: they are causally masked for every row that scores them, and an
+    // unconditional load keeps the in-flight loads of the other buffer from
+    // being waited for.
+    __device__ __forceinline__ void load(const float* pk, int64_t krow0, int ct, int ncol, float4* x) const {
+        const int blk = min(32 * ct + J, ncol - 1);
+        const float4* src = reinterpret_cast<const float4*>(pk + (krow0 + blk) * D + F * seg);
+#pragma unroll
+        for (int i = 0; i < F / 4; ++i) x[i] = src[i];
+    }
+    __device__ __forceinline__ void store(TileStage<D>* st, const float4* x) const {
+#pragma unroll
+        for (int i = 0; i < F / 8; ++i) {
+            bf16x8 h, l;
+            split8(x[2 * i], x[2 * i + 1], h, l);
+            const int slot = chunk_slot<D>(J, (F / 8) * seg + i);
+            st[cg].part[0][slot] = __builtin_bit_cast(uint4, h);
+            st[cg].part[1][slot] = __builtin_bit_cast(uint4, l);
+        }
+    }
+};
+
+// Transposed scores S^T = K_bar (sigma Q_bar)^T of one column tile: lane
+// (rho, half) holds query row rho and, in register r, column block
+// (r%4) + 8*(r/4) + 4*half of the tile.  One MFMA chain accumulates
+// hi*hi, hi*lo and lo*hi per 16-wide slice of d: the same instruction
+// sequence gives the same bits in every pass.  Lane (rho, half) supplies
+// k_bar row rho and query row rho, d = 16 kk + 8 half .. + 7.
+template <int D>
+__device__ __forceinline__ f32x16 tile_scores(const bf16x8* qh, const bf16x8* ql, const TileStage<D>& st, int rho,
+                                              int half) {
+    // All operand reads go out before the first product.
+    bf16x8 kh[D / 16], kl[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8 kh, kl;
-        split8(kb[2 * kk], kb[2 * kk + 1], kh, kl);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, a1, 0, 0, 0);
-        a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, a2, 0, 0, 0);
+        const int slot = chunk_slot<D>(rho, 2 * kk + half);
+        kh[kk] = __builtin_bit_cast(bf16x8, st.part[0][slot]);
+        kl[kk] = __builtin_bit_cast(bf16x8, st.part[1][slot]);
     }
-    f32x16 acc;
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc = {};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = (a0[r] + (a1[r] + a2[r])) * scale;
+    for (int kk = 0; kk < D / 16; ++kk) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], qh[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], acc, 0, 0, 0);
+    }
     return acc;
 }
 
-template <int D>
-__device__ __forceinline__ void load_kbar(const float* pk, int64_t row0, int J, int nb, int half, float4* kb) {
-    if (J < nb) {
-        const float4* src = reinterpret_cast<const float4*>(pk + (row0 + J) * D + 8 * half);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            kb[2 * kk] = src[4 * kk];       // d = 8*half + 16*kk .. +3
-            kb[2 * kk + 1] = src[4 * kk + 1];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) kb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-}
+// Workgroup barrier over LDS only: the next step's global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int kWaves = 4;
-constexpr int kMaxColTiles = FP_MAX_BLOCKS / 2 / 32;   // 32-block column tiles per row
-
-// One workgroup (4 waves) owns 32 score rows: TI consecutive query blocks x
-// the g query heads of one KV head.  The waves split the 32-block column
-// tiles (wave w takes tiles w, w+4, ...).  Phase 1: row maxima, combined in
-// LDS.  Phase 2: the same scores again, thresholded; each tile's keep bits go
-// to an LDS bitmap [tile][row].  Phase 3: each wave compacts 8 rows in
-// ascending J with a wave-wide prefix sum over the tiles' popcounts.
+// Workgroup = up to 128 score rows (4 row waves x TI query blocks x g heads)
+// of one KV head.  Wave wv: row wave rw = wv % 4, column group cg = wv / 4;
+// step p stages column tiles 2p and 2p + 1, and column group cg scores tile
+// 2p + cg for its row wave's rows.  Phase 1: row maxima, combined over the
+// column groups in LDS.  Phase 2: the same scores again, thresholded; each
+// tile's keep bits go to an LDS bitmap [tile][row slot]; tiles whose phase-1
+// maximum lies below every row's threshold are not scored again.  Phase 3:
+// one lane per row slot writes the row's list in ascending J.
 template <int D>
-__global__ __launch_bounds__(64 * kWaves, 2) void k_select(SelArgs a, SeqTable t) {
-    __shared__ uint32_t bits[kMaxColTiles][32];
-    __shared__ float pmax[kWaves][32];
-    __shared__ float rmax[32];
+__global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
+    __shared__ TileStage<D> stage[2][kColGroups];
+    __shared__ uint32_t bits[kMaxColTiles][kRowSlots];
+    __shared__ float pmax[kColGroups][kRowSlots];
+    __shared__ uint32_t need[kMaxColTiles / 32];     // phase 2: tiles some row may keep from
+    __shared__ int32_t todo[kMaxColTiles];           // ... in ascending order
 
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63;
+    const int rw = wv % kRowWaves, cg = wv / kRowWaves;
     const int rank = blockIdx.x / a.Hkv;
     const int hk = blockIdx.x % a.Hkv;
     int b, local;
     item_of(t, rank, b, local);
     const int nb = seq_blocks(t, b);
     const int first = first_block(t, b);             // query blocks are first .. nb-1
-    const int ntiles = (nb - first + a.TI - 1) / a.TI;
-    const int I0 = first + (ntiles - 1 - local) * a.TI;
+    const int TIW = kRowWaves * a.TI;                // query blocks per workgroup
+    const int ntiles = (nb - first + TIW - 1) / TIW;
+    const int I0 = first + (ntiles - 1 - local) * TIW;
     const int gblk0 = t.blk_off[b];
-    const int rows = a.TI * a.g;
+    const int rows = a.TI * a.g;                     // used row slots per row wave
     const int rho = lane & 31;
     const int half = lane >> 5;
+    const int Iw0 = I0 + rw * a.TI;                  // this row wave's first query block
+    const int Iw_end = min(nb, Iw0 + a.TI);          // and one past its last
+    const int ntile_w = Iw_end > Iw0 ? (Iw_end - 1) / 32 + 1 : 0;   // column tiles it needs
+    const bool rows_full = rows == 32 && Iw0 + a.TI <= nb;
 
-    // A operand: row rho = (query block I0 + rho / g, head hk*g + rho % g).
-    bf16x8 qh[D / 16], ql[D / 16];
-    {
-        const int I = I0 + rho / a.g;
-        const int h = hk * a.g + rho % a.g;
-        const bool valid = rho < rows && I < nb;
-        const float4* src = reinterpret_cast<const float4*>(
-            a.pq + ((int64_t)h * t.total_qblocks + qblock_row(t, b, valid ? I : I0)) * D + 8 * half);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            float4 x0 = valid ? src[4 * kk] : make_float4(0.f, 0.f, 0.f, 0.f);
-            float4 x1 = valid ? src[4 * kk + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-            split8(x0, x1, qh[kk], ql[kk]);
-        }
-    }
-    // Output register r of this lane holds row (r%4) + 8*(r/4) + 4*half.
-    int rowI[16];
-    bool rowOk[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int rr = (r & 3) + 8 * (r >> 2) + 4 * half;
-        rowI[r] = I0 + rr / a.g;
-        rowOk[r] = rr < rows && rowI[r] < nb;
-    }
-    const int ncol = min(nb, I0 + a.TI);
+    const int ncol = min(nb, I0 + TIW);
     const int ntile = (ncol + 31) >> 5;
     const int64_t krow0 = (int64_t)hk * t.total_blocks + gblk0;
+    const Stager<D> sg(tid);
+    if (tid < kMaxColTiles / 32) need[tid] = 0u;
 
-    // Phase 1: partial row maxima over this wave's tiles.
-    float m[16];
+    // This lane's query row rho = (query block Iw0 + rho / g, head hk*g + rho % g);
+    // rows without a query block read the first one and are zeroed.  The
+    // row is scaled by sigma before it is split.
+    const int rowI = Iw0 + rho / a.g;
+    const bool rowOk = rho < rows && rowI < nb;
+    float4 qf[D / 8];
+    {
+        const int h = hk * a.g + rho % a.g;
+        const float4* src = reinterpret_cast<const float4*>(
+            a.pq + ((int64_t)h * t.total_qblocks + qblock_row(t, b, rowOk ? rowI : first)) * D + 8 * half);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m[r] = -INFINITY;
-    float4 kb[D / 8];
-    for (int ct = wv; ct < ntile; ct += kWaves) {
-        load_kbar<D>(a.pk, krow0, 32 * ct + rho, nb, half, kb);
-        const f32x16 s = tile_scores<D>(qh, ql, kb, a.scale);
-        const int J = 32 * ct + rho;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (rowOk[r] && J <= rowI[r]) m[r] = fmaxf(m[r], s[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
-    }
-    if (rho == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pmax[wv][(r & 3) + 8 * (r >> 2) + 4 * half] = m[r];
-    }
-    __syncthreads();
-    if (tid < 32) {
-        float x = pmax[0][tid];
-#pragma unroll
-        for (int w2 = 1; w2 < kWaves; ++w2) x = fmaxf(x, pmax[w2][tid]);
-        rmax[tid] = x;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m[r] = rmax[(r & 3) + 8 * (r >> 2) + 4 * half];
-
-    // Phase 2: keep bits per (tile, row).
-    for (int ct = wv; ct < ntile; ct += kWaves) {
-        load_kbar<D>(a.pk, krow0, 32 * ct + rho, nb, half, kb);
-        const f32x16 s = tile_scores<D>(qh, ql, kb, a.scale);
-        const int J = 32 * ct + rho;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const bool keep = rowOk[r] && J <= rowI[r] && (s[r] - m[r] >= a.ln_alpha);
-            const uint64_t mask = __ballot(keep);
-            if (lane == 0) {
-                const int rr = (r & 3) + 8 * (r >> 2);
-                bits[ct][rr] = (uint32_t)mask;
-                bits[ct][rr + 4] = (uint32_t)(mask >> 32);
-            }
+        for (int kk = 0; kk < D / 16; ++kk) {
+            qf[2 * kk] = src[4 * kk];
+            qf[2 * kk + 1] = src[4 * kk + 1];
         }
     }
-    __syncthreads();
+    // Two register buffers: the rows of step p + 2 load while step p scores.
+    float4 x0[Stager<D>::F / 4], x1[Stager<D>::F / 4];
+    sg.load(a.pk, krow0, sg.cg, ncol, x0);               // phase 1's first two steps
+    sg.load(a.pk, krow0, 2 + sg.cg, ncol, x1);
+    bf16x8 qh[D / 16], ql[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const float sc = rowOk ? a.scale : 0.f;
+        const float4 u = qf[2 * kk], v = qf[2 * kk + 1];
+        split8(make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc), make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc),
+               qh[kk], ql[kk]);
+    }
+    // One pass over column tiles tile_of(0), tile_of(1), ... (a tile index
+    // >= ntile is staged but not scored): step p stages entries 2p and
+    // 2p + 1, and column group cg calls visit(ct, stage) on entry 2p + cg if
+    // its row wave needs that tile.  x0 and x1 hold steps 0 and 1 on entry.
+    auto sweep = [&](int nstep, auto&& tile_of, auto&& visit) {
+        sg.store(stage[0], x0);
+        lds_barrier();
+        auto step = [&](int p, float4* xnext, float4* xfree) {
+            sg.load(a.pk, krow0, tile_of(2 * (p + 2) + sg.cg), ncol, xfree);
+            const int ct = tile_of(2 * p + cg);
+            if (ct < ntile_w) visit(ct, stage[p & 1][cg]);
+            if (p + 1 < nstep) sg.store(stage[(p + 1) & 1], xnext);
+            lds_barrier();
+        };
+        for (int p = 0; p < nstep; p += 2) {
+            step(p, x1, x0);
+            if (p + 1 < nstep) step(p + 1, x0, x1);
+        }
+    };
+    // Tiles wholly below the row wave's first query block with every row
+    // valid need no causal mask.  Column block of register r within a tile:
+    auto masked = [&](int ct) { return !(rows_full && 32 * ct + 31 <= Iw0); };
+    auto colJ = [&](int r) { return (r & 3) + 8 * (r >> 2) + 4 * half; };
+    // Between the phases the bitmap words hold the bits of each (tile, row)'s
+    // score maximum (-inf for rows without a valid entry in the tile).
 
-    // Phase 3: ordered compaction, 8 rows per wave, 64 tiles per step.
-    for (int rr = wv; rr < 32; rr += kWaves) {
-        const int ii = rr / a.g, hi = rr % a.g;
-        const int I = I0 + ii;
-        if (rr >= rows || I >= nb) continue;                 // wave-uniform
-        const int h = hk * a.g + hi;
-        int32_t* out = a.kv_idx + list_row(t, b, h, I, nb, first);
-        int base = 0;
-        for (int c0 = 0; c0 < ntile; c0 += 64) {
-            const int ct = c0 + lane;
-            uint32_t wbits = 0u;
-            if (ct < ntile) {
+    // Phase 1: per tile, this row's max (both halves of the wave), kept in
+    // tmax; then the row max over all tiles and both column groups.
+    float m = -INFINITY;
+    sweep((ntile + 1) >> 1, [](int i) { return i; }, [&](int ct, const TileStage<D>& st) {
+        const f32x16 s = tile_scores<D>(qh, ql, st, rho, half);
+        float tm = -INFINITY;
+        if (masked(ct)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (rowOk && 32 * ct + colJ(r) <= rowI) tm = fmaxf(tm, s[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[r]);
+        }
+        tm = fmaxf(tm, __shfl_xor(tm, 32));
+        if (half == 0) bits[ct][32 * rw + rho] = __float_as_uint(tm);
+        m = fmaxf(m, tm);
+    });
+    if (half == 0) pmax[cg][32 * rw + rho] = m;
+    lds_barrier();
+    m = pmax[0][32 * rw + rho];
+#pragma unroll
+    for (int c2 = 1; c2 < kColGroups; ++c2) m = fmaxf(m, pmax[c2][32 * rw + rho]);
+
+    // Tiles to score again: those where some row's maximum reaches its
+    // threshold (s <= tmax implies s - m <= tmax - m in floating point, so
+    // no other tile keeps anything).  Column group 0 of each row wave marks
+    // them; the list is compacted in ascending order and every other tile's
+    // words are cleared.
+    if (cg == 0) {
+        for (int ct = 0; ct < ntile_w; ++ct) {
+            const float tm = __uint_as_float(bits[ct][32 * rw + rho]);
+            if (__ballot(rowOk && tm - m >= a.ln_alpha) && lane == 0) atomicOr(&need[ct >> 5], 1u << (ct & 31));
+        }
+    }
+    lds_barrier();
+    int nneed = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxColTiles / 32; ++i) nneed += __popc(need[i]);
+    if (tid < ntile) {
+        const uint32_t word = need[tid >> 5], below = word & ((1u << (tid & 31)) - 1u);
+        if ((word >> (tid & 31)) & 1u) {
+            int pos = __popc(below);
+            for (int i = 0; i < (tid >> 5); ++i) pos += __popc(need[i]);
+            todo[pos] = tid;
+        }
+    }
+    for (int e = tid; e < ntile * kRowSlots; e += kThreads) {
+        const int ct = e / kRowSlots;
+        if (!((need[ct >> 5] >> (ct & 31)) & 1u)) bits[ct][e % kRowSlots] = 0u;
+    }
+    lds_barrier();
+    auto todo_tile = [&](int i) { return i < nneed ? todo[i] : ntile; };
+    sg.load(a.pk, krow0, todo_tile(sg.cg), ncol, x0);    // phase 2's first two steps
+    sg.load(a.pk, krow0, todo_tile(2 + sg.cg), ncol, x1);
+
+    // Phase 2: keep bits per listed (tile, row slot); bit j of a word is
+    // column block j of the tile.  Row waves whose rows keep nothing in the
+    // tile skip the scores.  The two halves of the wave hold alternate groups
+    // of 4 columns and are merged before the store.
+    sweep((nneed + 1) >> 1, todo_tile, [&](int ct, const TileStage<D>& st) {
+        const float tm = __uint_as_float(bits[ct][32 * rw + rho]);
+        uint32_t w = 0u;
+        if (__ballot(rowOk && tm - m >= a.ln_alpha)) {
+            const f32x16 s = tile_scores<D>(qh, ql, st, rho, half);
+            const bool mk = masked(ct);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                bool keep = s[r] - m >= a.ln_alpha;
+                if (mk) keep = keep && rowOk && 32 * ct + colJ(r) <= rowI;
+                w |= keep ? (1u << colJ(r)) : 0u;
+            }
+            w |= __shfl_xor(w, 32);
+        }
+        if (half == 0) bits[ct][32 * rw + rho] = w;
+    });
+
+    // Phase 3: ordered compaction, one row slot per lane (lanes 0..15 of
+    // every wave): the row's tiles in ascending order, each tile's bits
+    // lowest first.
+    if (lane < kRowSlots / kWaves) {
+        const int slot = wv * (kRowSlots / kWaves) + lane;
+        const int rw3 = slot / 32, r3 = slot % 32;
+        const int ii = r3 / a.g, hi = r3 % a.g;
+        const int I = I0 + rw3 * a.TI + ii;
+        if (r3 < rows && I < nb) {
+            const int h = hk * a.g + hi;
+            const int nt = I / 32 + 1;                       // tiles holding J <= I
+            int32_t* out = a.kv_idx + list_row(t, b, h, I, nb, first);
+            int pos = 0;
+            for (int ct = 0; ct < nt; ++ct) {
+                uint32_t w;
                 if (a.shared) {
                     // Group-shared selection: the union of the g heads' keep bits
-                    // of this query block (rows ii*g .. ii*g+g-1 of this workgroup).
-                    for (int j = 0; j < a.g; ++j) wbits |= bits[ct][ii * a.g + j];
+                    // of this query block (row slots ii*g .. ii*g+g-1 of this row wave).
+                    w = 0u;
+                    for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
                 } else {
-                    wbits = bits[ct][rr];
+                    w = bits[ct][slot];
+                }
+                while (w) {
+                    out[pos++] = 32 * ct + __ffs(w) - 1;
+                    w &= w - 1;
                 }
             }
-            const int n = __popc(wbits);
-            int incl = n;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
-            }
-            int pos = base + incl - n;
-            uint32_t wb = wbits;
-            while (wb) {
-                const int bit = __ffs(wb) - 1;
-                wb &= wb - 1;
-                out[pos++] = 32 * ct + bit;
-            }
-            base += __shfl(incl, 63);
+            a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = pos;
         }
-        if (lane == 0) a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = base;
     }
 }
 
@@ -221,8 +331,8 @@ hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s) {
     if (t.total_items == 0) return hipSuccess;
     dim3 grid(t.total_items * a.Hkv);
     if (a.D == 64)
-        hipLaunchKernelGGL(k_select<64>, grid, dim3(64 * kWaves), 0, s, a, t);
+        hipLaunchKernelGGL(k_select<64>, grid, dim3(kThreads), 0, s, a, t);
     else
-        hipLaunchKernelGGL(k_select<128>, grid, dim3(64 * kWaves), 0, s, a, t);
+        hipLaunchKernelGGL(k_select<128>, grid, dim3(kThreads), 0, s, a, t);
     return hipGetLastError();
 }
