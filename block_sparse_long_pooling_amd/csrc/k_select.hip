@@ -11,8 +11,8 @@
 // 2 column groups.  The k_bar rows stream through LDS in column tiles of 32
 // blocks, two tiles per step (one per column group), split once per
 // workgroup into bf16 hi + lo parts; every tile then serves all the rows of
-// the workgroup.  The next step's rows are loaded into registers while the
-// current step computes.  The (L/B)^2 score matrix is never stored: phase 1
+// the workgroup.  The rows of the step after next are loaded into registers
+// while the current step computes.  The (L/B)^2 score matrix is never stored: phase 1
 // takes each row's max, phase 2 recomputes the same scores (same
 // instruction sequence, bit-identical) into a keep bitmap in LDS, phase 3
 // compacts it in ascending J.  The dot products run on bf16 MFMA with each
@@ -120,8 +120,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Workgroup = up to 128 score rows (4 row waves x TI query blocks x g heads)
 // of one KV head.  Wave wv: row wave rw = wv % 4, column group cg = wv / 4;
-// step p stages column tiles 2p and 2p + 1, and column group cg scores tile
-// 2p + cg for its row wave's rows.  Phase 1: row maxima, combined over the
+// each step stages two column tiles (phase 1: tiles 2p and 2p + 1 at step
+// p), and column group cg scores the (cg)-th of them for its row wave's
+// rows.  Phase 1: row maxima, combined over the
 // column groups in LDS.  Phase 2: the same scores again, thresholded; each
 // tile's keep bits go to an LDS bitmap [tile][row slot]; tiles whose phase-1
 // maximum lies below every row's threshold are not scored again.  Phase 3:
