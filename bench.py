@@ -11,11 +11,14 @@ Prints one JSON line.  value = effective TFLOP/s of the whole step, counting
 only the algorithmic work of the executed blocks: F_kept = 4 d sum over kept
 (h, I, J) of n_I n_J and F_corr = 4 d sum over (h, I) of n_I * |skipped J < I|.
 The roofline entry is for the attention kernel (MFMA-bound), timed with HIP
-events on the launch stream.  The CPU baseline is the fp64 oracle on a
-bounded sample of the same workload.
+events on the launch stream.  latency_spread gives the median and minimum of
+the per-step selection, attention and step times; hbm_anchor the streaming
+bandwidth of torch's own sum and copy kernels on the same GPU.  The CPU
+baseline is the fp64 oracle on a bounded sample of the same workload.
 """
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -114,9 +117,12 @@ def time_steps(fn_sel, fn_attn, steps, stream):
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
-    attn_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
-    return wall * 1e3 / steps, sel_ms, attn_ms
+    sel = [a.elapsed_time(b) for a, b, _ in ev]
+    attn = [b.elapsed_time(c) for _, b, c in ev]
+    total = [a.elapsed_time(c) for a, _, c in ev]
+    spread = {name: {"median": round(statistics.median(x), 4), "min": round(min(x), 4)}
+              for name, x in (("select_ms", sel), ("attn_ms", attn), ("step_ms", total))}
+    return wall * 1e3 / steps, sum(sel) / steps, sum(attn) / steps, spread
 
 
 def main():
@@ -159,10 +165,10 @@ def main():
         fa = lambda: fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, out=out)
         for _ in range(warmup):
             fs(); fa()
-        step_ms, sel_ms, attn_ms = time_steps(fs, fa, steps, stream)
+        step_ms, sel_ms, attn_ms, spread = time_steps(fs, fa, steps, stream)
         f_kept, f_corr, kept = work_counts(fp, sel, S, Hq, d, B, corr)
         causal = Hq * ((S + B - 1) // B) * ((S + B - 1) // B + 1) // 2
-        return dict(alpha=alpha, ms_per_step=step_ms, select_ms=sel_ms, attn_ms=attn_ms,
+        return dict(alpha=alpha, ms_per_step=step_ms, select_ms=sel_ms, attn_ms=attn_ms, spread=spread,
                     f_kept=f_kept, f_corr=f_corr, kept_blocks=kept, density=kept / causal,
                     sel=sel, p=p)
 
@@ -176,8 +182,10 @@ def main():
         f"attn {head['attn_ms']:.3f}); density {head['density']:.4f}; attn {attn_tflops:.1f} TFLOP/s; "
         f"select {sel_gbps:.0f} GB/s")
 
-    extra = {}
+    extra = {"latency_spread": head["spread"]}
     if not args.quick:
+        extra["hbm_anchor"] = hbm_anchor(stream, dev)
+        log(f"bench: hbm anchor {extra['hbm_anchor']}")
         sweep = []
         for a in w.alphas:
             if a == args.alpha:
@@ -291,6 +299,21 @@ def mask_agreement(sel_a, sel_b, S, Hq, B, dev):
 
     a, b = mask(sel_a), mask(sel_b)
     return float((a & b).sum()) / max(1.0, float((a | b).sum()))
+
+
+def hbm_anchor(stream, dev):
+    """Streaming bandwidth of torch's own kernels on this GPU, as a sanity
+    anchor for the 8 TB/s peak: a 4 GiB fp32 sum (read) and a 2 GiB copy
+    (read + write)."""
+    import torch
+    buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    t_sum = timed_ms(lambda: buf.sum(), 5, stream)
+    src = buf[: 1 << 29]
+    dst = torch.empty_like(src)
+    t_copy = timed_ms(lambda: dst.copy_(src), 5, stream)
+    del buf, src, dst
+    return {"torch_sum_read_gbps": round(4 * (1 << 30) / (t_sum * 1e-3) / 1e9, 1),
+            "torch_copy_gbps": round(2 * 4 * (1 << 29) / (t_copy * 1e-3) / 1e9, 1)}
 
 
 def timed_ms(fn, n, stream):
