@@ -11,7 +11,8 @@
 // per load, and each thread keeps its B / 16 chunks in registers.  Block sums
 // and the per-head absolute maximum are reduced across lanes and waves; the
 // means and the scale are written, then the codes are formed from the values
-// still in registers.  HBM sees one read of the bf16 data and one write of
+// still in registers (every thread derives its head's scale from the
+// waves' maxima itself).  HBM sees one read of the bf16 data and one write of
 // the codes.  The scale and x / scale are correctly rounded fp32 divisions,
 // so every code is decided in the same precision as the format's reference.
 // x / scale takes three operations: with y the correctly rounded 1 / scale
@@ -36,8 +37,6 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
     constexpr int NS = B / (2 * kWaves);   // tokens per thread
     __shared__ float psum[kWaves][32][8];
     __shared__ float pmax[kWaves][HPG];
-    __shared__ float scl[HPG];
-    __shared__ float rcp[HPG];
 
     const int J = blockIdx.x;
     int g = blockIdx.y, ts = 0;
@@ -99,7 +98,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
         if (ch % CPH == 0) pmax[w][hl] = amax;
     }
     __syncthreads();
-    if (w == 0 && hf == 0 && hv) {
+    if (!hv) return;
+    // Every thread forms its head's scale from the waves' maxima itself (the
+    // same operations in the same order, so the same bits), so the codes need
+    // no second barrier.
+    float am = pmax[0][hl];
+#pragma unroll
+    for (int w2 = 1; w2 < kWaves; ++w2) am = fmaxf(am, pmax[w2][hl]);
+    const float sc = am > 0.f ? __fdiv_rn(am, kE4M3Max) : 1.f;
+    const float ry = __fdiv_rn(1.f, sc);
+    if (w == 0 && hf == 0) {
         float m[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -118,20 +126,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
             *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
                 make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
                            pack_bf16(m[6], m[7]));
-        if (ch % CPH == 0) {
-            float am = pmax[0][hl];
-#pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2) am = fmaxf(am, pmax[w2][hl]);
-            const float sc = am > 0.f ? __fdiv_rn(am, kE4M3Max) : 1.f;
-            scl[hl] = sc;
-            rcp[hl] = __fdiv_rn(1.f, sc);
-            a.scale[ts][(int64_t)h * a.nB + J] = sc;
-        }
+        if (ch % CPH == 0) a.scale[ts][(int64_t)h * a.nB + J] = sc;
     }
-    __syncthreads();
-    if (!hv) return;
-    const float sc = scl[hl];
-    const float ry = rcp[hl];
     auto quot = [&](float xv) {
         const float q = xv * ry;
         const float r = fmaf(-q, sc, xv);
