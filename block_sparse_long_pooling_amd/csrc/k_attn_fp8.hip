@@ -1,5 +1,6 @@
 // fp8 (OCP e4m3fn) sparse attention over the kept blocks (FlashPrefill V2
-// abstract: FP8 inference), same work decomposition as the bf16 kernel.
+// abstract: FP8 inference).  One workgroup of BLK/32 waves (32 query rows
+// each) per (query block, query head), at least two workgroups per CU.
 //
 // Inputs carry one fp32 scale per (head, block): x = code * scale.  Scores
 // come from v_mfma_scale_f32_32x32x64_f8f6f4 on the raw codes and are scaled
@@ -18,7 +19,7 @@
 // PV operand as it stands.
 //
 // The mean correction runs on the bf16 pipeline with Q dequantized to bf16:
-// the bf16 pooled K_bar / V_bar rows of 64 past blocks at a time arrive by
+// the bf16 pooled K_bar / V_bar rows of BLK/2 past blocks at a time arrive by
 // DMA into one of two LDS buffers (the tile buffers of the kept walk) while
 // the previous 64 are computed, K_bar read row-major and V_bar with the
 // transposing LDS read, as in the bf16 kernel.
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         l *= (1.f / 256.f);
     }
     if (a.correction && I > 0) {
-        // bf16 Q fragment of the dequantized queries (B operand layout of qk_tile).
+        // bf16 Q fragment of the dequantized queries (the B operand of the bf16 qk product).
         bf16x8 qb[D / 16];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
