@@ -93,3 +93,36 @@ def test_prep_with_skeleton_queries():
     assert outside == 0
     c_ref, s_ref = O.quantize_fp8_blockwise(q.float().numpy(), B)       # codes do not depend on the probes
     assert np.array_equal(f8.q8.cpu().numpy(), c_ref) and np.array_equal(f8.q_scale.cpu().numpy(), s_ref)
+
+
+@pytest.mark.slow
+def test_prep_128k_full_size_sampled():
+    """The one-pass preparation at the 128K layer's full size, in the launch
+    configuration the benchmark times: sampled (tensor, head, block) slices of
+    the codes and scales equal the oracle's quantizer bit for bit, and the
+    sampled block means equal the oracle's to fp32 rounding."""
+    w = synth.WORKLOADS["llama8b_s128k"]
+    S, Hq, Hkv, d, B = w.seqlens[0], w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print("generating llama8b_s128k", flush=True)
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, w.seed, w.verticals)
+    _, sel, f8 = _prep(q, k, v, B, 0.1, True)
+    nB = S // B
+    r = np.random.default_rng(11)
+    got = {"q": (f8.q8.cpu().numpy(), f8.q_scale.cpu().numpy(), sel.pooled_q.cpu().numpy()),
+           "k": (f8.k8.cpu().numpy(), f8.k_scale.cpu().numpy(), sel.pooled_k.cpu().numpy()),
+           "v": (f8.v8.cpu().numpy(), f8.v_scale.cpu().numpy(), None)}
+    src = {"q": q, "k": k, "v": v}
+    n = 0
+    for name, x in src.items():
+        H = x.shape[1]
+        picks = {(0, 0), (H - 1, nB - 1)} | {(int(r.integers(H)), int(r.integers(nB))) for _ in range(10)}
+        for h, J in sorted(picks):
+            seg = x[J * B:(J + 1) * B, h:h + 1].float().numpy()          # [B, 1, d]
+            c_ref, s_ref = O.quantize_fp8_blockwise(seg, B)
+            codes, scales, means = got[name]
+            assert scales[h, J] == s_ref[0, 0], (name, h, J)
+            assert np.array_equal(codes[J * B:(J + 1) * B, h], c_ref[:, 0]), (name, h, J)
+            if means is not None:
+                np.testing.assert_allclose(means[h, J], O.block_means(seg, B)[0, 0], rtol=0, atol=2e-6)
+            n += 1
+    print(f"  {n} sampled (tensor, head, block) slices bit-exact", flush=True)
