@@ -124,3 +124,41 @@ def test_paged_batch8_full_size():
         idx_off += Hq * nb * (nb + 1) // 2
         cnt_off += Hq * nb
     print(f"  overall density {kept_total / causal_total:.4f}", flush=True)
+
+
+def test_paged_batch8_chunked_last4096_full_size():
+    """The chunked entry in the configuration the benchmark times: the 8
+    requests' last 4096 tokens are new, their prefix means come from the
+    pooled cache written by an earlier call over the prefixes.  Every output
+    row and LSE equals the whole-prompt call's (a property of the reading of
+    chunked prefill that holds at any size), and the prefix call's rows equal
+    the whole prompt's first rows."""
+    w = synth.WORKLOADS["paged_batch8"]
+    Hq, Hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print("generating paged_batch8", flush=True)
+    pb = synth.workload_inputs(w)
+    p = fp.make_params(Hq, Hkv, d, B, w.alphas[0], mean_correction=True)
+    qd, kc, vc, bt = (x.to(dev()) for x in (pb.q, pb.k_cache, pb.v_cache, pb.block_table))
+    full = fp.fp_sparse_prefill_varlen_paged(p, qd, kc, vc, bt, pb.cu_seqlens, return_lse=True)
+    cu = [int(x) for x in pb.cu_seqlens]
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    cut = [max(0, L - 4096) for L in lens]
+    cache = fp.alloc_pooled_cache(p, kc.shape[0], dev())
+    q_pre = torch.cat([qd[cu[b]:cu[b] + cut[b]] for b in range(len(lens))])
+    cu_pre = [0]
+    for c_ in cut:
+        cu_pre.append(cu_pre[-1] + c_)
+    pre = fp.fp_sparse_prefill_chunked_paged(p, q_pre, kc, vc, bt, cu_pre, cut, pooled_cache=cache,
+                                             return_lse=True)
+    q_new = torch.cat([qd[cu[b] + cut[b]:cu[b + 1]] for b in range(len(lens))])
+    cu_new = [0]
+    for b in range(len(lens)):
+        cu_new.append(cu_new[-1] + lens[b] - cut[b])
+    res = fp.fp_sparse_prefill_chunked_paged(p, q_new, kc, vc, bt, cu_new, lens, pooled_cache=cache,
+                                             prefix_pooled=True, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        assert torch.equal(res.out[cu_new[b]:cu_new[b + 1]], full.out[cu[b] + cut[b]:cu[b + 1]]), b
+        assert torch.equal(res.lse[:, cu_new[b]:cu_new[b + 1]], full.lse[:, cu[b] + cut[b]:cu[b + 1]]), b
+        assert torch.equal(pre.out[cu_pre[b]:cu_pre[b + 1]], full.out[cu[b]:cu[b] + cut[b]]), b
+    print(f"  {cu_new[-1]} new rows and {cu_pre[-1]} prefix rows equal the whole-prompt rows", flush=True)
