@@ -162,3 +162,33 @@ def test_paged_batch8_chunked_last4096_full_size():
         assert torch.equal(res.lse[:, cu_new[b]:cu_new[b + 1]], full.lse[:, cu[b] + cut[b]:cu[b + 1]]), b
         assert torch.equal(pre.out[cu_pre[b]:cu_pre[b + 1]], full.out[cu[b]:cu[b] + cut[b]]), b
     print(f"  {cu_new[-1]} new rows and {cu_pre[-1]} prefix rows equal the whole-prompt rows", flush=True)
+
+
+@pytest.mark.parametrize("shared,probes", [(True, 0), (False, 16)], ids=["shared_lists", "skeleton16"])
+def test_128k_selection_options_full_size(s128k, shared, probes):
+    """The two selection options the benchmark times beside the headline, at
+    the 128K layer's full size: group-shared lists (the union of a KV head's
+    query heads' masks) and skeleton-query scoring (q_bar from 16 probes per
+    block).  Lists match the oracle's outside the threshold band; sampled
+    outputs match the oracle under the GPU's lists."""
+    seq = s128k
+    S, Hq, Hkv, d, B = seq.S, seq.Hq, seq.Hkv, seq.d, seq.B
+    nB = S // B
+    p = fp.make_params(Hq, Hkv, d, B, 0.1, mean_correction=True, shared_selection=shared, query_probes=probes)
+    qd, kd, vd = seq.gpu
+    sel = fp.fp_select_blocks(p, qd, kd, vd)
+    out = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel)
+    torch.cuda.synchronize()
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    qn, kn, vn = seq.np
+    ref = O.select_blocks(qn, kn, vn, B, 0.1, shared=shared, probes=probes)
+    outside, inside, band = compare_mask(mask, ref)
+    print(f"  shared={shared} probes={probes}: density {mask.sum() / (Hq * nB * (nB + 1) / 2):.4f}, "
+          f"band {band}, in-band mismatches {inside}", flush=True)
+    assert outside == 0
+    pairs = _sample_pairs(Hq, nB, 12, seed=7 + probes)
+    o_ref, _ = O.sparse_attention(qn, kn, vn, ref, True, pairs=pairs, keep=mask)
+    o = out.float().cpu().numpy()
+    worst = max(float(np.abs(o[I * B:(I + 1) * B, h] - o_ref[I * B:(I + 1) * B, h]).max()) for h, I in pairs)
+    print(f"  {len(pairs)} sampled pairs: max|o-ref| {worst:.3e}", flush=True)
+    assert worst <= BF16_TOL
