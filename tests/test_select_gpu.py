@@ -17,7 +17,7 @@ import block_sparse_long_pooling_amd as fp
 from block_sparse_long_pooling_amd import synth
 from oracle import flashprefill_oracle as O
 
-from gpu_util import check_lists, compare_mask, dev, oracle_inputs
+from gpu_util import BF16_TOL, FP8_TOL, check_lists, compare_mask, dev, oracle_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -64,3 +64,46 @@ def test_lists_match_oracle(case, alpha, shared):
         g = Hq // Hkv
         grouped = mask.reshape(Hkv, g, nB, nB)
         assert (grouped == grouped[:, :1]).all()               # one list per KV head
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_maximum_blocks_per_request(fp8):
+    """A request at the largest supported block count (4096 blocks of 64
+    tokens, 262,144 tokens): 128 column tiles per row in the selection
+    kernel, full-length kept-block bitmaps in attention; bf16, and fp8 with
+    the fused preparation.  Lists match the oracle outside the band (fp8
+    selection is on the bf16 data); sampled outputs match the oracle under
+    the GPU's lists (for fp8, on the dequantized codes)."""
+    S, Hq, Hkv, d, B, alpha = 4096 * 64, 2, 1, 64, 64, 0.1
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, seed=77, verticals=True)
+    print(f"case S={S} Hq={Hq} Hkv={Hkv} d={d} B={B} fp8={fp8}", flush=True)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    qn, kn, vn = oracle_inputs(q, k, v)
+    if fp8:
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+        sel, f8 = fp.fp_select_blocks_fp8(p, qd, kd, vd)
+        out = fp.fp_sparse_prefill_fwd(p, f8.q8, f8.k8, f8.v8, sel, q_scale=f8.q_scale, k_scale=f8.k_scale,
+                                       v_scale=f8.v_scale)
+        att = [O.dequantize_blockwise(synth.fp8_codes_to_float(c.cpu()).numpy(), sc.cpu().numpy(), B)
+               for c, sc in ((f8.q8, f8.q_scale), (f8.k8, f8.k_scale), (f8.v8, f8.v_scale))]
+        tol = FP8_TOL
+    else:
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True)
+        sel = fp.fp_select_blocks(p, qd, kd, vd)
+        out = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel)
+        att = [qn, kn, vn]
+        tol = BF16_TOL
+    torch.cuda.synchronize()
+    nB = S // B
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    ref = O.select_blocks(qn, kn, vn, B, alpha)
+    outside, inside, band = compare_mask(mask, ref)
+    print(f"  density {mask.sum() / (Hq * nB * (nB + 1) / 2):.4f}, band {band}, in-band mismatches {inside}",
+          flush=True)
+    assert outside == 0
+    pairs = [(0, 0), (1, nB - 1), (0, nB - 1), (1, 2048), (0, 4000), (1, 63)]
+    o_ref, _ = O.sparse_attention(att[0], att[1], att[2], ref, True, pairs=pairs, keep=mask)
+    o = out.float().cpu().numpy()
+    worst = max(float(np.abs(o[I * B:(I + 1) * B, h] - o_ref[I * B:(I + 1) * B, h]).max()) for h, I in pairs)
+    print(f"  {len(pairs)} sampled pairs: max|o-ref| {worst:.3e}", flush=True)
+    assert worst <= tol
