@@ -61,10 +61,24 @@ struct DmaPlan {
     __device__ __forceinline__ int coff(int i) const { return (chunk0 ^ swz<D>(row(i))) * 8; }
 };
 
+// Page ids of this thread's DMA rows of tile J (paged layout), all loaded
+// before any of the tile's DMAs is issued: the vector-memory counter is in
+// order, so a page id loaded between DMAs could only be waited for together
+// with the DMAs before it.  Rows past the request's end (row >= nvalid) look
+// up its last valid row's page, so the block-table read stays inside the
+// pages that cover the request.
+template <int D, int BLK, int NT>
+__device__ __forceinline__ void load_tile_pages(const int32_t* pages, const KVLayout& L, int J, int nvalid,
+                                                const DmaPlan<D, BLK, NT>& plan, int* pg) {
+#pragma unroll
+    for (int i = 0; i < DmaPlan<D, BLK, NT>::NLOAD; ++i)
+        pg[i] = pages[(J * BLK + min(plan.row(i), nvalid - 1)) / L.page_size];
+}
+
 // DMA one tile: rows J*BLK .. of the request whose first row is `first`
-// (contiguous) or whose pages are listed in `pages` (paged).
+// (contiguous), or of its pages pg from load_tile_pages (paged).
 template <int D, int BLK, int NT, bool PAGED>
-__device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t* pages, const KVLayout& L,
+__device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg, const KVLayout& L,
                                            int64_t rs, int J, int nvalid, const DmaPlan<D, BLK, NT>& plan,
                                            const uint4* zero, char* lds, int wave_base) {
     using P = DmaPlan<D, BLK, NT>;
@@ -90,7 +104,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int32_t*
         for (int i = 0; i < P::NLOAD; ++i) {
             const int row = plan.row(i);
             const int tr = J * BLK + row;
-            const int page = pages[tr / L.page_size];
+            const int page = pg[i];
             // Opaque column offset: keeps the compiler from holding a 64-bit
             // pointer per chunk across the loop (it would spill).
             int co = plan.coff(i);

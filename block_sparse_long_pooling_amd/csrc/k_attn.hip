@@ -96,9 +96,12 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
     auto issue = [&](const It& itm, int code, char* kdst, char* vdst) {
         if (code < kCorr) {
-            issue_tile<D, BLK, G::NT, PAGED>(itm.kfirst, itm.pages, a.kv, rs, code, itm.len - code * BLK, plan, zero,
+            // K and V rows share their pages: one set of page ids for both.
+            int pg[DmaPlan<D, BLK, G::NT>::NLOAD];
+            if (PAGED) load_tile_pages(itm.pages, a.kv, code, itm.len - code * BLK, plan, pg);
+            issue_tile<D, BLK, G::NT, PAGED>(itm.kfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero,
                                           kdst, wave_base);
-            issue_tile<D, BLK, G::NT, PAGED>(itm.vfirst, itm.pages, a.kv, rs, code, itm.len - code * BLK, plan, zero,
+            issue_tile<D, BLK, G::NT, PAGED>(itm.vfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero,
                                           vdst, wave_base);
         } else {
             // Pooled rows of this request's blocks for the KV head (contiguous, row stride D).
