@@ -192,13 +192,6 @@ struct Union {
         const int i = pos[h] + (int)__lane_id();
         win[h] = i < cap ? list[h][i] : INT_MAX;
     }
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int h = 0; h < HP; ++h) {
-            pos[h] = 0;
-            load_window(h);
-        }
-    }
     __device__ __forceinline__ int val(int h) const {
         return pos[h] < cnt[h] ? __builtin_amdgcn_readlane(win[h], pos[h] - wbase[h]) : INT_MAX;
     }
@@ -249,13 +242,25 @@ struct Item {
         hk = h / a.g;
         const int64_t rs = (int64_t)a.Hkv * D;
         const int h0 = h - hs;
+        // The heads' counts and first list windows load together (unconditional
+        // loads, lanes past the capacity re-read the last entry and are masked
+        // after), so setting up an item waits on memory once.
+        int cnt_raw[HP], win_raw[HP];
+        u.cap = I + 1;
 #pragma unroll
         for (int j = 0; j < HP; ++j) {
             u.list[j] = a.kv_idx + list_row(t, b, h0 + j, I, nb, first);
-            u.cnt[j] = __builtin_amdgcn_readfirstlane(a.kv_cnt[count_index(t, a.Hq, b, h0 + j, I, nb, first)]);
+            cnt_raw[j] = a.kv_cnt[count_index(t, a.Hq, b, h0 + j, I, nb, first)];
+            win_raw[j] = u.list[j][min((int)__lane_id(), I)];
         }
-        u.cap = I + 1;
-        u.init();
+        __builtin_amdgcn_sched_barrier(0);               // all four loads before the first use
+#pragma unroll
+        for (int j = 0; j < HP; ++j) {
+            u.cnt[j] = __builtin_amdgcn_readfirstlane(cnt_raw[j]);
+            u.pos[j] = 0;
+            u.wbase[j] = 0;
+            u.win[j] = (int)__lane_id() < u.cap ? win_raw[j] : INT_MAX;
+        }
         nct = (a.correction && I > 0) ? (I + BLK - 1) / BLK : 0;
         ct = -1;
         const int64_t base = (PAGED ? 0 : (int64_t)tok0 * rs) + (int64_t)hk * D;
