@@ -292,12 +292,43 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     };
     char* buf0 = reinterpret_cast<char*>(lk);
     char* buf1 = reinterpret_cast<char*>(lv);
-    if (cnt > 0) issue8(list[0], buf0);
+    // The list and its blocks' K and V scales are read 64 entries at a time,
+    // one per lane, and handed out with readlane.  No global load then sits
+    // between a tile's DMA and its use: the vector-memory counter is in order,
+    // so waiting for such a load would also wait for the DMA issued before it.
+    const int64_t srow = (int64_t)hk * t.total_blocks + sblk;
+    int wbase = 0, wJ = 0;
+    float wsk = 0.f, wsv = 0.f;
+    auto load_window = [&](int base) {
+        wbase = base;
+        const int i = min(base + lane, cnt - 1);
+        wJ = list[i];
+        wsk = a.k_scale[srow + wJ];
+        wsv = a.v_scale[srow + wJ];
+        __builtin_amdgcn_s_waitcnt(0);                   // settled here, not at a later use among DMAs
+    };
+    auto from_window = [&](int it, int& J, float& sk, float& sv) {
+        J = __builtin_amdgcn_readlane(wJ, it - wbase);
+        sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsk), it - wbase));
+        sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsv), it - wbase));
+    };
+    int J = 0;
+    float sk = 1.f, sv = 1.f;
+    if (cnt > 0) {
+        load_window(0);
+        from_window(0, J, sk, sv);
+        issue8(J, buf0);
+    }
     auto step = [&](int it, char* bcur, char* bnext) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of tile it is done
         lds_barrier();                                   // ... every thread's; the other buffer is free
-        if (it + 1 < cnt) issue8(list[it + 1], bnext);
-        const int J = list[it];
+        int Jn = 0;
+        float skn = 1.f, svn = 1.f;
+        if (it + 1 < cnt) {
+            if (it + 1 - wbase == 64) load_window(it + 1);
+            from_window(it + 1, Jn, skn, svn);
+            issue8(Jn, bnext);
+        }
         qk8<D, 0, T::NSUB>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
         if (J == I) {
 #pragma unroll
@@ -308,12 +339,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
                     s[sub][r] = key > qr ? -INFINITY : s[sub][r];
                 }
         }
-        const float sk = a.k_scale[(int64_t)hk * t.total_blocks + sblk + J];
-        const float sv = a.v_scale[(int64_t)hk * t.total_blocks + sblk + J];
         softmax8_update<T::NSUB, T::NDS>(s, cq * sk, sv_prev / sv, m, l, o, ph, pl);
         sv_prev = sv;
         pv8<D, 0>(bcur + VOFF, ph, pl, lane, o);
         if (BLK == 128) pv8<D, (BLK == 128 ? 1 : 0)>(bcur + VOFF, ph + 2, pl + 2, lane, o);
+        J = Jn;
+        sk = skn;
+        sv = svn;
     };
     for (int it = 0; it < cnt; it += 2) {
         step(it, buf0, buf1);
