@@ -43,8 +43,11 @@ reading a chunk's result equals the last q_len rows of the full prefill.
 
 Group-shared selection (an option, not in the pages; it serves the
 PackGQA-style head packing the V2 abstract names): the g query heads of a KV
-head share one list, the union of their own lists, so every head of a packed
-group computes on every tile fetched for it.
+head share one list, so every head of a packed group computes on every tile
+fetched for it.  Two ways to form it: the union of the heads' own lists, or
+one list scored from the group-pooled query (the mean of the g heads' block
+means, i.e. the mean over the group's heads and the block's tokens) against
+the KV head's k_bar, thresholded as in steps 2-4.
 
 Skeleton-query scoring (FlashPrefill, gist.science technical summary,
 section 2.A: attention patterns can be found from a skeleton set of
@@ -174,6 +177,39 @@ def share_across_group(keep: np.ndarray, band: np.ndarray, g: int) -> Tuple[np.n
     return np.repeat(ku, g, axis=0), np.repeat(bu, g, axis=0)
 
 
+def group_pooled_queries(q_bar: np.ndarray, g: int) -> np.ndarray:
+    """[Hq, nq, d] block means -> [Hq / g, nq, d]: each KV head's row is the
+    mean of its g query heads' rows (heads hk*g .. hk*g + g - 1)."""
+    Hq, nq, d = q_bar.shape
+    return q_bar.reshape(Hq // g, g, nq, d).mean(axis=1)
+
+
+def _shared_mode(shared) -> str:
+    """shared: False / None (per head), True or 'union', or 'pooled'."""
+    if shared is False or shared is None:
+        return "none"
+    if shared is True or shared == "union":
+        return "union"
+    if shared == "pooled":
+        return "pooled"
+    raise ValueError(f"unknown group-shared selection {shared!r}")
+
+
+def _select(q_bar, k_bar, sigma, alpha, first, mode):
+    """Steps 2-4 on given means: logits, scores, keep and band per query head."""
+    Hq, Hkv = q_bar.shape[0], k_bar.shape[0]
+    g = Hq // Hkv
+    if mode == "pooled":
+        s = np.repeat(block_logits(group_pooled_queries(q_bar, g), k_bar, sigma, first), g, axis=0)
+    else:
+        s = block_logits(q_bar, k_bar, sigma, first)
+    score = block_scores(s)
+    keep, band = threshold(score, alpha, first)
+    if mode == "union":
+        keep, band = share_across_group(keep, band, g)
+    return s, score, keep, band
+
+
 def probe_stride(block: int, probes: int) -> int:
     """Token stride of the skeleton queries: block / probes (1 when probes is 0)."""
     if probes == 0:
@@ -184,11 +220,14 @@ def probe_stride(block: int, probes: int) -> int:
 
 
 def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                  pool_v: bool = True, shared: bool = False, probes: int = 0) -> Selection:
+                  pool_v: bool = True, shared=False, probes: int = 0) -> Selection:
     """Pooling, block scores and thresholding for one sequence.
 
     q [S, Hq, d], k and v [S, Hkv, d] (any float dtype; upcast to fp64).
-    shared: one mask per KV head, the union over its query heads.
+    shared: False, per query head; True or 'union', one mask per KV head, the
+    union over its query heads; 'pooled', one mask per KV head scored from
+    the group-pooled query (s, score and band are then per KV head, repeated
+    over its query heads).
     probes: 0, or P dividing the block: q_bar averages the skeleton queries
     at every (block / P)-th token of the block instead of all its tokens.
     """
@@ -198,11 +237,7 @@ def select_blocks(q, k, v, block: int, alpha: float, sigma: Optional[float] = No
     q_bar = block_means(q, block, probe_stride(block, probes))
     k_bar = block_means(k, block)
     v_bar = block_means(v, block) if pool_v else None
-    s = block_logits(q_bar, k_bar, sigma)
-    score = block_scores(s)
-    keep, band = threshold(score, alpha)
-    if shared:
-        keep, band = share_across_group(keep, band, q.shape[1] // k.shape[1])
+    s, score, keep, band = _select(q_bar, k_bar, sigma, alpha, 0, _shared_mode(shared))
     return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block)
 
 
@@ -277,7 +312,7 @@ def sparse_attention(q, k, v, sel: Selection, correction: bool, sigma: Optional[
 
 
 def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[float] = None,
-                          pool_v: bool = True, shared: bool = False, probes: int = 0) -> Selection:
+                          pool_v: bool = True, shared=False, probes: int = 0) -> Selection:
     """Pooling, block scores and thresholding for a chunk of new queries.
 
     q [q_len, Hq, d] are the last q_len tokens of a context whose keys and
@@ -297,11 +332,7 @@ def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[flo
     q_bar = block_means(q, block, probe_stride(block, probes))   # chunk blocks = context blocks first, ...
     k_bar = block_means(k, block)
     v_bar = block_means(v, block) if pool_v else None
-    s = block_logits(q_bar, k_bar, sigma, first)
-    score = block_scores(s)
-    keep, band = threshold(score, alpha, first)
-    if shared:
-        keep, band = share_across_group(keep, band, q.shape[1] // k.shape[1])
+    s, score, keep, band = _select(q_bar, k_bar, sigma, alpha, first, _shared_mode(shared))
     return Selection(q_bar, k_bar, v_bar, s, score, keep, band, block, first)
 
 

@@ -553,6 +553,92 @@ def test_shared_selection_chunked_equals_full_rows():
     assert np.array_equal(ch.keep, full.keep[:, 2:, :])
 
 
+def _brute_force_group_pooled(q, k, B, alpha):
+    """One mask per KV head from the mean over its g query heads and the
+    block's tokens, written with Python loops and math.fsum, repeated over
+    the group's query heads."""
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    nB = (S + B - 1) // B
+    sig = 1.0 / math.sqrt(d)
+    keep = np.zeros((Hq, nB, nB), dtype=bool)
+    band = np.zeros((Hq, nB, nB), dtype=bool)
+    for hk in range(Hkv):
+        heads = range(hk * g, (hk + 1) * g)
+
+        def kmean(J):
+            toks = range(J * B, min(S, (J + 1) * B))
+            return [math.fsum(float(k[t, hk, c]) for t in toks) / len(toks) for c in range(d)]
+
+        def qmean(I):
+            toks = range(I * B, min(S, (I + 1) * B))
+            n = len(toks) * g
+            return [math.fsum(float(q[t, h, c]) for t in toks for h in heads) / n for c in range(d)]
+
+        kb = [kmean(J) for J in range(nB)]
+        for I in range(nB):
+            qb = qmean(I)
+            s_ = [sig * math.fsum(a * b for a, b in zip(qb, kb[J])) for J in range(I + 1)]
+            m = max(s_)
+            den = math.fsum(math.exp(x - m) for x in s_)
+            score = [math.exp(x - m) / den for x in s_]
+            thr = alpha * max(score)
+            for J in range(I + 1):
+                for h in heads:
+                    keep[h, I, J] = score[J] >= thr
+                    band[h, I, J] = alpha > 0 and abs(score[J] - thr) <= 1e-3 * thr
+    return keep, band
+
+
+@pytest.mark.parametrize("alpha", [0.1, 0.3, 0.6])
+def test_group_pooled_selection_matches_brute_force(alpha):
+    q, k, v = _rand_qkv(300, 6, 2, 8, seed=31, scale=3.0)     # g = 3, 19 blocks, ragged last block
+    sel = O.select_blocks(q, k, v, 16, alpha, shared="pooled")
+    keep, band = _brute_force_group_pooled(q, k, 16, alpha)
+    outside = ~(sel.band | band)
+    assert np.array_equal(sel.keep[outside], keep[outside])
+    for hk in range(2):
+        assert (sel.keep[hk * 3:(hk + 1) * 3] == sel.keep[hk * 3]).all()
+
+
+def test_group_pooled_logits_are_the_head_mean():
+    """Block logits are linear in q_bar, so the group-pooled logit of a block
+    pair is the mean of the group's per-head logits."""
+    q, k, v = _rand_qkv(256, 8, 2, 16, seed=32)
+    own = O.select_blocks(q, k, v, 32, 0.2)
+    pooled = O.select_blocks(q, k, v, 32, 0.2, shared="pooled")
+    fin = np.isfinite(own.s)
+    mean = own.s.reshape(2, 4, 8, 8).mean(axis=1)
+    ref = np.repeat(mean, 4, axis=0)
+    assert np.allclose(pooled.s[fin], ref[fin], rtol=0, atol=1e-12)
+    assert np.array_equal(np.isfinite(pooled.s), fin)
+
+
+def test_group_pooled_equals_per_head_when_heads_agree():
+    q, k, v = _rand_qkv(200, 3, 3, 8, seed=33, scale=2.0)      # g = 1
+    own = O.select_blocks(q, k, v, 16, 0.4)
+    pooled = O.select_blocks(q, k, v, 16, 0.4, shared="pooled")
+    assert np.array_equal(own.keep, pooled.keep) and np.array_equal(own.band, pooled.band)
+    q1 = np.repeat(q[:, :1], 4, axis=1)                          # g = 4, four equal heads
+    own = O.select_blocks(q1, k[:, :1], v[:, :1], 16, 0.4)
+    pooled = O.select_blocks(q1, k[:, :1], v[:, :1], 16, 0.4, shared="pooled")
+    assert np.array_equal(own.keep, pooled.keep)
+
+
+def test_group_pooled_chunked_equals_full_rows():
+    q, k, v = _rand_qkv(133, 4, 2, 8, seed=34, scale=1.3)
+    full = O.select_blocks(q, k, v, 32, 0.3, shared="pooled")
+    ch = O.select_blocks_chunked(q[64:], k, v, 32, 0.3, shared="pooled")
+    assert np.array_equal(ch.keep, full.keep[:, 2:, :])
+
+
+def test_unknown_group_sharing_rejected():
+    q, k, v = _rand_qkv(64, 2, 1, 8, seed=35)
+    with pytest.raises(ValueError):
+        O.select_blocks(q, k, v, 32, 0.3, shared="mean")
+
+
 # ------------------------------------------------- skeleton-query scoring
 
 def test_skeleton_query_means_brute_force():
