@@ -35,11 +35,15 @@ tokens).  fp8 inputs are judged on their dequantized values.
 Chunked prefill (FlashPrefill V2 abstract and the authors' post: the
 operator serves continuous batching over a paged KV cache): a call brings q_len new queries at the end of a context of kv_len
 tokens whose keys and values are all present.  Blocks are counted from the
-start of the context; the chunk starts on a block boundary (reading), so query
-block I >= first = (kv_len - q_len) / block is pooled over the chunk's tokens
-exactly as in a full prefill, sees blocks J <= I, and row i of the chunk sits
-at position kv_len - q_len + i (bottom-right causal alignment).  Under that
-reading a chunk's result equals the last q_len rows of the full prefill.
+start of the context and row i of the chunk sits at position P0 + i, P0 =
+kv_len - q_len (bottom-right causal alignment).  Query block I >= first =
+floor(P0 / block) holds the chunk's queries in [I block, (I + 1) block) and
+sees blocks J <= I; its q_bar is the mean of the queries it holds, so a block
+the chunk enters part way pools only the chunk's queries (the earlier queries
+of that block belong to an earlier call).  Keys are pooled over whole context
+blocks.  When the chunk starts on a block boundary its result equals the last
+q_len rows of the full prefill; otherwise every row past the first query
+block still does.  Skeleton queries need a chunk that starts on a boundary.
 
 Group-shared selection (an option, not in the pages; it serves the
 PackGQA-style head packing the V2 abstract names): the g query heads of a KV
@@ -107,6 +111,28 @@ def block_means(x, block: int, stride: int = 1) -> np.ndarray:
 def causal_blocks(nq: int, nB: int, first: int = 0) -> np.ndarray:
     """[nq, nB]: query block first + i may see KV blocks J <= first + i."""
     return np.arange(nB)[None, :] <= (first + np.arange(nq))[:, None]
+
+
+def chunk_block_means(q, block: int, P0: int, stride: int = 1) -> np.ndarray:
+    """Query block means of a chunk whose row r is position P0 + r.
+
+    q [q_len, H, d] -> [H, n, d] for query blocks first .. first + n - 1,
+    first = P0 // block: block I averages the chunk's rows at positions
+    [max(I block, P0), min((I + 1) block, P0 + q_len)).  stride > 1 (skeleton
+    queries) requires P0 to be a multiple of the block.
+    """
+    q_len, H, d = q.shape
+    if stride > 1 and P0 % block:
+        raise ValueError("skeleton queries need a chunk that starts on a block boundary")
+    if q_len == 0:
+        return np.empty((H, 0, d), dtype=np.float64)
+    first, last = P0 // block, (P0 + q_len - 1) // block
+    out = np.empty((H, last - first + 1, d), dtype=np.float64)
+    for i, I in enumerate(range(first, last + 1)):
+        r0 = max(I * block, P0) - P0
+        r1 = min((I + 1) * block, P0 + q_len) - P0
+        out[:, i, :] = _f64(q[r0:r1:stride]).mean(axis=0)
+    return out
 
 
 def block_logits(q_bar: np.ndarray, k_bar: np.ndarray, sigma: float, first: int = 0) -> np.ndarray:
@@ -252,7 +278,7 @@ def block_entries(q, k, v, keep_row: np.ndarray, h: int, I: int, block: int, sig
     """
     S = k.shape[0]
     hk = h // g
-    r0, r1 = I * block, min(S, (I + 1) * block)
+    r0, r1 = max(I * block, q_offset), min(S, (I + 1) * block)
     rows = np.arange(r0, r1)
     q_i = _f64(q[r0 - q_offset:r1 - q_offset, h])              # [n_I, d]
     kept = [J for J in range(I + 1) if keep_row[J]]
@@ -316,20 +342,20 @@ def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[flo
     """Pooling, block scores and thresholding for a chunk of new queries.
 
     q [q_len, Hq, d] are the last q_len tokens of a context whose keys and
-    values are k, v [kv_len, Hkv, d].  kv_len - q_len must be a multiple of
-    ``block``.  Row i of the result is query block first + i, first =
-    (kv_len - q_len) / block; keys are pooled over the whole context.
+    values are k, v [kv_len, Hkv, d]; the chunk may start inside a block
+    (not with skeleton queries).  Row i of the result is query block first + i,
+    first = (kv_len - q_len) // block (no rows for an empty chunk); keys are
+    pooled over the whole context.
     """
     q_len, kv_len = q.shape[0], k.shape[0]
     if not 0 <= q_len <= kv_len:
         raise ValueError(f"chunk of {q_len} queries for a context of {kv_len} tokens")
-    if (kv_len - q_len) % block:
-        raise ValueError("the chunk must start on a block boundary")
     d = q.shape[-1]
     if sigma is None:
         sigma = 1.0 / math.sqrt(d)
-    first = (kv_len - q_len) // block
-    q_bar = block_means(q, block, probe_stride(block, probes))   # chunk blocks = context blocks first, ...
+    P0 = kv_len - q_len
+    first = P0 // block if q_len else num_blocks(kv_len, block)
+    q_bar = chunk_block_means(q, block, P0, probe_stride(block, probes))
     k_bar = block_means(k, block)
     v_bar = block_means(v, block) if pool_v else None
     s, score, keep, band = _select(q_bar, k_bar, sigma, alpha, first, _shared_mode(shared))
@@ -359,7 +385,7 @@ def sparse_attention_chunked(q, k, v, sel: Selection, correction: bool, sigma: O
             z, vals = block_entries(q, k, v, keep[h, i], h, I, block, sigma, g, correction,
                                     sel.k_bar, sel.v_bar, q_offset=P0)
             M, w, l = softmax_rows(z)
-            r0, r1 = I * block - P0, min(k.shape[0], (I + 1) * block) - P0
+            r0, r1 = max(I * block, P0) - P0, min(k.shape[0], (I + 1) * block) - P0
             o[r0:r1, h] = (w @ vals) / l[:, None]
             lse[h, r0:r1] = M + np.log(l)
     return o, lse

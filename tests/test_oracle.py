@@ -334,7 +334,8 @@ def _brute_force_chunk(qc, k, v, B, alpha, corr):
     """A chunk of new queries at the end of a context, written from token
     positions with Python loops: query row r is position P0 + r and sees the
     keys at or before it in the kept blocks, plus one pooled entry per skipped
-    past block (n_J copies of its mean key and value)."""
+    past block (n_J copies of its mean key and value).  A query block the
+    chunk enters part way pools the chunk's queries it holds."""
     q_len, Hq, d = qc.shape
     S, Hkv, _ = k.shape
     g = Hq // Hkv
@@ -356,14 +357,14 @@ def _brute_force_chunk(qc, k, v, B, alpha, corr):
         kb = [mean(k, range(J * B, min(S, J * B + B)), hk) for J in range(nB)]
         vb = [mean(v, range(J * B, min(S, J * B + B)), hk) for J in range(nB)]
         for I in range(P0 // B, nB):
-            qb = mean(qc, range(I * B - P0, min(S, I * B + B) - P0), h)
+            qb = mean(qc, range(max(I * B, P0) - P0, min(S, I * B + B) - P0), h)
             s = [sig * dot(qb, kb[J]) for J in range(I + 1)]
             m = max(s)
             den = math.fsum(math.exp(x - m) for x in s)
             score = [math.exp(x - m) / den for x in s]
             keep = [score[J] >= alpha * max(score) for J in range(I + 1)]
             keep_rows[h, I] = keep
-            for p in range(I * B, min(S, I * B + B)):
+            for p in range(max(I * B, P0), min(S, I * B + B)):
                 qr = [float(x) for x in qc[p - P0, h]]
                 z, vals = [], []
                 for J in range(I + 1):
@@ -385,7 +386,7 @@ def _brute_force_chunk(qc, k, v, B, alpha, corr):
     return o, lse, keep_rows
 
 
-@pytest.mark.parametrize("P0", [0, 8, 24])
+@pytest.mark.parametrize("P0", [0, 8, 24, 3, 13, 39])
 @pytest.mark.parametrize("corr", [False, True])
 def test_chunk_matches_brute_force(P0, corr):
     q, k, v = _rand_qkv(45, 2, 1, 4, seed=11 + P0, scale=3.0)
@@ -425,12 +426,54 @@ def test_chunk_equals_last_rows_of_full_prefill(P0, Hq, Hkv):
                for i in range(len(lists[h])))
 
 
-def test_chunk_rejects_unaligned_or_too_long():
+def test_chunk_rejects_unaligned_probes_or_too_long():
     q, k, v = _rand_qkv(40, 2, 1, 4, seed=5)
+    O.select_blocks_chunked(q[3:], k, v, 8, 0.1)                  # a chunk may start inside a block ...
     with pytest.raises(ValueError):
-        O.select_blocks_chunked(q[3:], k, v, 8, 0.1)
+        O.select_blocks_chunked(q[3:], k, v, 8, 0.1, probes=2)    # ... but not with skeleton queries
     with pytest.raises(ValueError):
         O.select_blocks_chunked(np.concatenate([q, q[:8]]), k, v, 8, 0.1)
+
+
+@pytest.mark.parametrize("P0", [5, 31, 33, 100])
+def test_unaligned_chunk_dense_is_bottom_right_causal_attention(P0):
+    """alpha = 0 keeps every causal block, so a chunk starting anywhere is
+    plain causal attention of its queries over the context with bottom-right
+    alignment (torch's routine with an explicit mask)."""
+    S, Hq, Hkv, d, B = 133, 4, 2, 8, 32
+    q, k, v = _rand_qkv(S, Hq, Hkv, d, seed=40 + P0, scale=1.5)
+    sel = O.select_blocks_chunked(q[P0:], k, v, B, 0.0)
+    assert sel.first == P0 // B and sel.keep.shape[1] == (S + B - 1) // B - P0 // B
+    o, lse = O.sparse_attention_chunked(q[P0:], k, v, sel, correction=True)
+    g = Hq // Hkv
+    Q = torch.from_numpy(q[P0:]).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+    V = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+    allowed = torch.arange(S)[None, :] <= (P0 + torch.arange(S - P0))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=allowed)[0].permute(1, 0, 2)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+    z = torch.einsum("hqd,hkd->hqk", Q[0], K[0]) / math.sqrt(d)
+    lse_ref = torch.logsumexp(z.masked_fill(~allowed[None], -math.inf), dim=-1)
+    np.testing.assert_allclose(lse, lse_ref.numpy(), atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("P0", [1, 40, 70])
+def test_unaligned_chunk_later_blocks_equal_full_prefill(P0):
+    """Past the block it enters part way, a chunk's query blocks hold the same
+    queries as in the full prefill, so their masks and rows are the full
+    prefill's; the entered block pools fewer queries."""
+    S, Hq, Hkv, B = 133, 4, 2, 32
+    q, k, v = _rand_qkv(S, Hq, Hkv, 8, seed=50 + P0, scale=2.0)
+    full = O.select_blocks(q, k, v, B, 0.2)
+    o_f, lse_f = O.sparse_attention(q, k, v, full, correction=True)
+    sel = O.select_blocks_chunked(q[P0:], k, v, B, 0.2)
+    o_c, lse_c = O.sparse_attention_chunked(q[P0:], k, v, sel, correction=True)
+    f, r = P0 // B, (P0 // B + 1) * B - P0                        # first query block, its rows in the chunk
+    assert np.array_equal(sel.keep[:, 1:], full.keep[:, f + 1:])
+    np.testing.assert_allclose(o_c[r:], o_f[P0 + r:], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse_c[:, r:], lse_f[:, P0 + r:], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(sel.q_bar[:, 0], q[P0:P0 + r].mean(axis=0), atol=1e-15, rtol=0)
+    assert not np.allclose(sel.q_bar[:, 0], full.q_bar[:, f])
 
 
 def test_empty_chunk():
@@ -439,6 +482,8 @@ def test_empty_chunk():
     assert sel.keep.shape == (2, 0, 5)
     o, lse = O.sparse_attention_chunked(q[40:], k, v, sel, True)
     assert o.shape == (0, 2, 4) and lse.shape == (2, 0)
+    sel = O.select_blocks_chunked(q[37:37], k[:37], v[:37], 8, 0.1)      # ends inside a block: no rows
+    assert sel.keep.shape == (2, 0, 5)
 
 
 # ------------------------------------------------------ e4m3 encoder (fp8)
