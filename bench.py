@@ -199,15 +199,19 @@ def main():
             log(f"bench: sweep {sweep[-1]}")
             del r
         extra["alpha_sweep"] = sweep
-        # group-shared selection (one list per KV head, the union of its query heads')
-        r = measure(args.alpha, max(3, args.steps // 2), 1, shared=True)
-        fa_ = r["f_kept"] + r["f_corr"]
-        extra["shared_selection"] = dict(alpha=args.alpha, ms_per_step=round(r["ms_per_step"], 4),
-                                         select_ms=round(r["select_ms"], 4), attn_ms=round(r["attn_ms"], 4),
-                                         density=round(r["density"], 5),
-                                         attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2))
-        log(f"bench: shared selection {extra['shared_selection']}")
-        del r
+        # group-shared selection: one list per KV head, the union of its query
+        # heads' lists, or the list of the group-pooled query
+        for mode, key in (("union", "shared_selection"), ("pooled", "shared_selection_pooled")):
+            r = measure(args.alpha, max(3, args.steps // 2), 1, shared=mode)
+            fa_ = r["f_kept"] + r["f_corr"]
+            jac = mask_agreement(head["sel"], r["sel"], S, Hq, B, dev)
+            extra[key] = dict(alpha=args.alpha, ms_per_step=round(r["ms_per_step"], 4),
+                              select_ms=round(r["select_ms"], 4), attn_ms=round(r["attn_ms"], 4),
+                              density=round(r["density"], 5),
+                              attn_tflops=round(fa_ / (r["attn_ms"] * 1e-3) / 1e12, 2),
+                              kept_jaccard_vs_per_head=round(jac, 4))
+            log(f"bench: {key} {extra[key]}")
+            del r
         # skeleton-query scoring: q_bar from 16 uniformly spaced queries per block
         r = measure(args.alpha, max(3, args.steps // 2), 1, probes=16)
         fa_ = r["f_kept"] + r["f_corr"]

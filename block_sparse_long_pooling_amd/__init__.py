@@ -90,12 +90,23 @@ def _check(status: int):
         raise FlashPrefillError(status, lib().fp_last_error().decode())
 
 
+def _shared_code(shared) -> int:
+    """shared_selection: False (per head), True or 'union' (1), 'pooled' (2)."""
+    if shared is False or shared is None or shared == 0:
+        return 0
+    if shared is True or shared == "union" or shared == 1:
+        return 1
+    if shared == "pooled" or shared == 2:
+        return 2
+    raise ValueError(f"shared_selection must be False, True/'union' or 'pooled', not {shared!r}")
+
+
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, alpha, mean_correction=True,
                 softmax_scale=0.0, dtype=FP_DTYPE_BF16, shared_selection=False,
                 query_probes=0) -> fp_params:
     return fp_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
                      float(alpha), float(softmax_scale), int(bool(mean_correction)), int(dtype),
-                     int(bool(shared_selection)), int(query_probes))
+                     _shared_code(shared_selection), int(query_probes))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -218,7 +218,7 @@ struct Union {
 // One work item: query block I of one request, HP heads of one KV head.
 template <int D, int BLK, int HP, bool PAGED>
 struct Item {
-    int b, nb, I, tok0, len, q0, nI, hk, h;      // h: this wave's query head
+    int b, nb, I, tok0, len, q0, lo, nI, hk, h;  // h: this wave's query head; rows lo .. nI-1 exist
     int nct;                                      // correction tiles (blocks 0 .. I-1 in tiles of BLK)
     int ct;                                       // next correction tile to examine; -1 while kept blocks remain
     Union<HP> u;
@@ -237,7 +237,11 @@ struct Item {
         I = nb - 1 - local;
         tok0 = t.tok_off[b];
         len = context_len(t, b, BLK);
-        q0 = tok0 + (I - first) * BLK;
+        // Row r of the block is query row q0 + r; a chunk that starts inside
+        // its first block has no rows before lo there.
+        const int ph = chunk_phase(t, b, BLK);
+        q0 = tok0 + (I - first) * BLK - ph;
+        lo = I == first ? ph : 0;
         nI = min(BLK, len - I * BLK);
         hk = h / a.g;
         const int64_t rs = (int64_t)a.Hkv * D;

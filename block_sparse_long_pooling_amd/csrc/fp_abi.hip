@@ -61,8 +61,8 @@ int check_params(const fp_params* p) {
         return fail(FP_INVALID_ARGUMENT, "mean_correction must be 0 or 1");
     if (p->dtype != FP_DTYPE_BF16 && p->dtype != FP_DTYPE_FP8_E4M3FN)
         return fail(FP_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
-    if (p->shared_selection != 0 && p->shared_selection != 1)
-        return fail(FP_INVALID_ARGUMENT, "shared_selection must be 0 or 1");
+    if (p->shared_selection < 0 || p->shared_selection > 2)
+        return fail(FP_INVALID_ARGUMENT, "shared_selection must be 0, 1 or 2");
     if (p->query_probes < 0 || (p->query_probes > 0 && p->block_size % p->query_probes != 0))
         return fail(FP_INVALID_ARGUMENT, "query_probes (%d) must be 0 or divide block_size (%d)", p->query_probes,
                     p->block_size);
@@ -95,11 +95,13 @@ int build_table(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, i
         if (len < qlen)
             return fail(FP_INVALID_ARGUMENT, "request %d: %lld queries exceed its context of %lld tokens", b,
                         (long long)qlen, (long long)len);
-        if ((len - qlen) % B != 0)
-            return fail(FP_UNSUPPORTED, "request %d: the chunk starts at token %lld, not on a block boundary (%d)", b,
-                        (long long)(len - qlen), B);
+        if (p.query_probes > 0 && (len - qlen) % B != 0)
+            return fail(FP_UNSUPPORTED,
+                        "request %d: skeleton queries need a chunk that starts on a block boundary (start %lld, "
+                        "block %d)", b, (long long)(len - qlen), B);
         const int64_t nb = (len + B - 1) / B;
-        const int64_t first = (len - qlen) / B;
+        // Query blocks are first .. nb-1; the chunk may start inside block first.
+        const int64_t first = qlen > 0 ? (len - qlen) / B : nb;
         if (nb > FP_MAX_BLOCKS / 2)
             return fail(FP_UNSUPPORTED, "request %d has %lld blocks (max %d)", b, (long long)nb, FP_MAX_BLOCKS / 2);
         ctx[b] = len;

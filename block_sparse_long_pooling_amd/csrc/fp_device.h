@@ -45,6 +45,12 @@ __device__ __forceinline__ int context_len(const SeqTable& t, int b, int B) {
     const int nb = seq_blocks(t, b);
     return nb > 0 ? (nb - 1) * B + t.tail[b] : 0;
 }
+// Tokens of query block first_block(t, b) that precede the chunk (0 unless a
+// chunk starts inside a block): chunk row 0 is position first * B + phase.
+__device__ __forceinline__ int chunk_phase(const SeqTable& t, int b, int B) {
+    const int qlen = t.tok_off[b + 1] - t.tok_off[b];
+    return qlen > 0 ? context_len(t, b, B) - qlen - first_block(t, b) * B : 0;
+}
 __device__ __forceinline__ int64_t tri64(int n) { return (int64_t)n * (n + 1) / 2; }
 // Start of the kv_idx row of (query head h, query block I); capacity I + 1.
 __device__ __forceinline__ int64_t list_row(const SeqTable& t, int b, int h, int I, int nb, int first) {

@@ -34,7 +34,8 @@ struct SelArgs {
     int32_t Hq, Hkv, g, D, TI;   // TI query blocks x g heads per row wave (TI * g <= 32)
     float scale;                 // sigma
     float ln_alpha;              // threshold on s - max s (-inf keeps every causal block)
-    int32_t shared;              // 1: the g heads of a query block share the union of their lists
+    int32_t shared;              // 1: the g heads of a query block share the union of their lists;
+                                 // 2: they share the list of the mean of their q_bar rows
 };
 
 struct AttnArgs {

@@ -158,13 +158,13 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         for (int i = tphase; i < HP * nwords; i += G::NT) kept_bits[i / nwords][i % nwords] = 0u;
     };
     bf16x8 qf[D / 16];
-    // Rows past the end of a ragged last block re-read the last valid row:
-    // their outputs are never stored, and unconditional loads keep the
-    // compiler from waiting on them (and on DMAs issued before) when the
-    // registers are written.
+    // Rows past the end of a ragged last block (or before the start of a
+    // chunk) re-read the nearest valid row: their outputs are never stored,
+    // and unconditional loads keep the compiler from waiting on them (and on
+    // DMAs issued before) when the registers are written.
     auto load_q = [&](const It& itm) {
         const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                             ((int64_t)(itm.q0 + min(qr, itm.nI - 1)) * a.Hq + itm.h) * D + 8 * half;
+                             ((int64_t)(itm.q0 + min(max(qr, itm.lo), itm.nI - 1)) * a.Hq + itm.h) * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 16 * kk));
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         auto store_rows = [&](const char* buf) {
             const uint4* stage = reinterpret_cast<const uint4*>(buf);
             const int ht = tphase % (64 * G::WPH);       // thread index within this head's waves
-            for (int i = ht; i < cur.nI * G::NCH; i += 64 * G::WPH) {
+            for (int i = cur.lo * G::NCH + ht; i < cur.nI * G::NCH; i += 64 * G::WPH) {
                 const int row = i / G::NCH, ch = i % G::NCH;
                 *reinterpret_cast<uint4*>(a.out + ((int64_t)(cur.q0 + row) * a.Hq + cur.h) * D + ch * 8) =
                     stage[row * G::NCH + (ch ^ swz<D>(row))];
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
             store_rows(vb0);
             asm volatile("; stored head 1");
         }
-        if (a.lse && half == 0 && qr < cur.nI)
+        if (a.lse && half == 0 && qr >= cur.lo && qr < cur.nI)
             a.lse[(int64_t)cur.h * t.total_tokens + cur.q0 + qr] = (m + __log2f(l_tot)) * kLn2;
         if (!has_next) break;
         cur = nxt;

@@ -52,13 +52,17 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
     float mean[8];
     if (c < a.q_chunks) {
         // Q: packed rows of this call's queries, never paged.  Prefix blocks
-        // (chunked prefill) have no queries here.
+        // (chunked prefill) have no queries here, and a chunk that starts
+        // inside its first block holds that block's tokens lo .. n-1 only.
         if (I < first) return;
         const int col = c * 8;
-        // With skeleton queries only every q_stride-th token of the block counts.
+        const int ph = chunk_phase(t, b, a.B);
+        const int lo = I == first ? ph : 0;
+        // With skeleton queries only every q_stride-th token of the block
+        // counts (the host admits them for block-aligned chunks only).
         const int64_t row_elems = (int64_t)a.Hq * a.D * a.q_stride;
-        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B) * a.Hq * a.D + col;
-        const int nq = (n + a.q_stride - 1) / a.q_stride;
+        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B - ph + lo) * a.Hq * a.D + col;
+        const int nq = (n - lo + a.q_stride - 1) / a.q_stride;
         int r = 0;
         for (; r + kUnroll <= nq; r += kUnroll) {
             uint4 x[kUnroll];

@@ -164,18 +164,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
 
     // This lane's query row rho = (query block Iw0 + rho / g, head hk*g + rho % g);
     // rows without a query block read the first one and are zeroed.  The
-    // row is scaled by sigma before it is split.
+    // row is scaled by sigma before it is split.  With group-pooled lists
+    // every row of a query block holds the sum of its g heads' rows, and the
+    // scale takes the 1/g of their mean.
     const int rowI = Iw0 + rho / a.g;
     const bool rowOk = rho < rows && rowI < nb;
+    const bool pooled = a.shared == 2;
     float4 qf[D / 8];
     {
-        const int h = hk * a.g + rho % a.g;
-        const float4* src = reinterpret_cast<const float4*>(
-            a.pq + ((int64_t)h * t.total_qblocks + qblock_row(t, b, rowOk ? rowI : first)) * D + 8 * half);
+        const int64_t qrow = qblock_row(t, b, rowOk ? rowI : first);
+        const int h = hk * a.g + (pooled ? 0 : rho % a.g);
+        const float4* src = reinterpret_cast<const float4*>(a.pq + ((int64_t)h * t.total_qblocks + qrow) * D + 8 * half);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             qf[2 * kk] = src[4 * kk];
             qf[2 * kk + 1] = src[4 * kk + 1];
+        }
+        if (pooled) {
+            for (int j = 1; j < a.g; ++j) {
+                src += (int64_t)t.total_qblocks * D / 4;       // head h + j
+#pragma unroll
+                for (int kk = 0; kk < D / 8; ++kk) {
+                    const float4 x = src[4 * (kk / 2) + (kk & 1)];
+                    qf[kk] = make_float4(qf[kk].x + x.x, qf[kk].y + x.y, qf[kk].z + x.z, qf[kk].w + x.w);
+                }
+            }
         }
     }
     // Two register buffers: the rows of step p + 2 load while step p scores.
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     bf16x8 qh[D / 16], ql[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        const float sc = rowOk ? a.scale : 0.f;
+        const float sc = rowOk ? (pooled ? a.scale / (float)a.g : a.scale) : 0.f;
         const float4 u = qf[2 * kk], v = qf[2 * kk + 1];
         split8(make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc), make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc),
                qh[kk], ql[kk]);
@@ -310,7 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
                 uint32_t w;
                 if (a.shared) {
                     // Group-shared selection: the union of the g heads' keep bits
-                    // of this query block (row slots ii*g .. ii*g+g-1 of this row wave).
+                    // of this query block (row slots ii*g .. ii*g+g-1 of this row
+                    // wave); with group-pooled rows the g rows' bits are equal.
                     w = 0u;
                     for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
                 } else {

@@ -71,7 +71,11 @@ typedef struct {
     int32_t shared_selection; /* 0: one list per query head (steps 1-4 as written);
                                  1: the g = Hq/Hkv query heads of a KV head share one list,
                                  the union of their own lists (every head of a group then
-                                 runs on every tile fetched for the group) */
+                                 runs on every tile fetched for the group);
+                                 2: they share one list scored from the group-pooled query,
+                                 the mean of the g heads' q_bar rows, against the KV head's
+                                 k_bar (steps 2-4 once per KV head).  pooled_q stays per
+                                 query head in every mode. */
     int32_t query_probes;     /* 0: q_bar is the mean of every query of the block (step 1);
                                  P dividing block_size: the mean of the skeleton queries at
                                  offsets 0, st, 2 st, ... of the block, st = block_size / P
@@ -174,15 +178,18 @@ int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
  * batching).  Request b brings q_len = cu_seqlens_q_host[b+1] -
  * cu_seqlens_q_host[b] new queries at the end of a context of
  * kv_len = kv_lens_host[b] tokens whose keys and values, the new ones
- * included, are already in the cache.  Blocks are counted from the start of
- * the context; the chunk must start on a block boundary ((kv_len - q_len) a
- * multiple of block_size, else FP_UNSUPPORTED), 0 <= q_len <= kv_len.  Query
- * row r of request b sits at position kv_len - q_len + r and sees every key
- * at or before it (bottom-right causal alignment); its query block I =
- * position / block_size is pooled over the chunk's queries in it, scored
- * against the block means of the whole context and thresholded as in steps
- * 1-4, and attends as in step 5.  Under these rules a chunk's output equals
- * the last q_len rows of a prefill of the whole context.
+ * included, are already in the cache; 0 <= q_len <= kv_len.  Blocks are
+ * counted from the start of the context.  Query row r of request b sits at
+ * position P0 + r, P0 = kv_len - q_len, and sees every key at or before it
+ * (bottom-right causal alignment); its query block I = position / block_size
+ * is pooled over the chunk's queries in it (a chunk may start inside a
+ * block: that block then pools only the chunk's queries), scored against
+ * the block means of the whole context and thresholded as in steps 1-4, and
+ * attends as in step 5.  When P0 is a multiple of block_size a chunk's
+ * output equals the last q_len rows of a prefill of the whole context;
+ * otherwise every row past its first query block still does.  Skeleton
+ * queries (query_probes > 0) need P0 to be a multiple of block_size, else
+ * FP_UNSUPPORTED.
  *   q [T,Hq,d] bf16, T = cu_seqlens_q_host[batch]: the chunks packed back to back.
  *   k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq: as
  *     for fp_sparse_prefill_varlen_paged; block_table covers kv_len tokens.
@@ -197,7 +204,8 @@ int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
  *     1 requires pooled_cache.
  *   kv_idx, kv_cnt: lists of the chunk's query blocks only: request b's
  *     region holds, for each head h, the rows I = first .. nb-1 (first =
- *     (kv_len - q_len) / block_size, nb = ceil(kv_len / block_size)), row I
+ *     floor(P0 / block_size), or nb for an empty chunk; nb = ceil(kv_len /
+ *     block_size)), row I
  *     with capacity I + 1; kv_cnt is [Hq, nb - first] per request.  Regions
  *     of consecutive requests are concatenated.  Sizes from fp_chunked_sizes.
  *   workspace: at least the bytes fp_chunked_sizes gives; contents on return

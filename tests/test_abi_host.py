@@ -152,7 +152,8 @@ def _chunked(p, cu, kv, page_size=64, num_pages=100, max_pages=64, ws=1 << 30, c
 
 def test_chunked_validation():
     p = _p()
-    assert _chunked(p, [0, 100], [1000]) == fp.FP_UNSUPPORTED          # chunk starts at 900, not a block edge
+    # a chunk that starts at 900, inside block 7, is accepted, but not with skeleton queries
+    assert _chunked(_p(query_probes=16), [0, 100], [1000]) == fp.FP_UNSUPPORTED
     assert "block boundary" in fp.lib().fp_last_error().decode()
     assert _chunked(p, [0, 300], [200]) == fp.FP_INVALID_ARGUMENT      # more queries than context
     assert _chunked(p, [0, 128], [256], kv_lens_null=True) == fp.FP_INVALID_ARGUMENT
@@ -179,8 +180,15 @@ def test_chunked_sizes():
     lens = [cu[i + 1] - cu[i] for i in range(3)]
     assert fp.fp_chunked_sizes(p, cu, lens) == (fp.fp_index_capacity(p, cu), fp.fp_count_entries(p, cu),
                                                 fp.fp_varlen_workspace_bytes(p, cu))
+    # a chunk entering block 7 of 8 part way: query blocks 7 and ... 7
+    cap, cnt, _ = fp.fp_chunked_sizes(p, [0, 100], [1000])
+    assert (cap, cnt) == (32 * (tri(8) - tri(7)), 32)
+    cap, cnt, _ = fp.fp_chunked_sizes(p, [0, 200], [1000])        # from 800, inside block 6
+    assert (cap, cnt) == (32 * (tri(8) - tri(6)), 64)
+    cap, cnt, _ = fp.fp_chunked_sizes(p, [0, 0], [1000])          # empty: no query blocks
+    assert (cap, cnt) == (0, 0)
     with pytest.raises(fp.FlashPrefillError):
-        fp.fp_chunked_sizes(p, [0, 100], [1000])
+        fp.fp_chunked_sizes(_p(query_probes=16), [0, 100], [1000])
 
 
 def test_select_blocks_fp8_validation():
@@ -205,6 +213,8 @@ def test_shared_selection_flag_validated():
     c = (ctypes.c_int32 * 2)(0, 1024)
     assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) > 0
     p.shared_selection = 2
+    assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) > 0
+    p.shared_selection = 3
     assert fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) == -1
     assert "shared_selection" in fp.lib().fp_last_error().decode()
 
@@ -214,3 +224,10 @@ def test_query_probes_validated():
     for probes, ok in ((0, True), (1, True), (16, True), (128, True), (3, False), (-1, False), (256, False)):
         p = _p(query_probes=probes)
         assert (fp.lib().fp_index_capacity(ctypes.byref(p), c, 1) > 0) == ok, probes
+
+
+def test_shared_selection_names():
+    assert [fp.make_params(4, 1, 64, 64, 0.1, shared_selection=x).shared_selection
+            for x in (False, True, "union", "pooled")] == [0, 1, 1, 2]
+    with pytest.raises(ValueError):
+        fp.make_params(4, 1, 64, 64, 0.1, shared_selection="mean")

@@ -20,6 +20,18 @@ CASES = [
     ([640, 129, 255, 64], [256, 64, 192, 64], 4, 1, 64, 64, 16),     # last request: empty chunk
     ([4096, 1000, 2000], [3968, 512, 1024], 32, 8, 128, 128, 64),
 ]
+# Chunks that start inside a block: the first query block holds only the
+# chunk's tail of it (one row, for starts at B - 1 or at the last token).
+UNALIGNED = [
+    ([300, 1024, 777, 2048], [131, 5, 700, 1677], 8, 2, 128, 128, 64),
+    ([640, 129, 255, 100], [250, 63, 1, 100], 4, 1, 64, 64, 16),   # last: empty chunk ending mid-block
+    ([4096, 1000, 2000], [4095, 999, 1030], 32, 8, 128, 128, 64),  # single-token chunks
+]
+
+
+def _case_id(c):
+    aligned = all(P0 % c[5] == 0 for P0 in c[1])
+    return "b%d_d%d_B%d_p%d%s" % (len(c[0]), c[4], c[5], c[6], "" if aligned else "_unaligned")
 
 
 def _tri(n):
@@ -53,7 +65,8 @@ def _masks(res, Hq, kv_lens, starts, B):
     io = co = 0
     masks = []
     for L, P0 in zip(kv_lens, starts):
-        nb, first = (L + B - 1) // B, P0 // B
+        nb = (L + B - 1) // B
+        first = P0 // B if P0 < L else nb
         nq, rowsz = nb - first, _tri(nb) - _tri(first)
         m = np.zeros((Hq, nq, nb), dtype=bool)
         for h in range(Hq):
@@ -74,7 +87,7 @@ def _masks(res, Hq, kv_lens, starts, B):
 
 @pytest.mark.parametrize("alpha", [0.0, 0.1, 0.4])
 @pytest.mark.parametrize("corr", [True, False])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_d%d_B%d_p%d" % (len(c[0]), c[3], c[4], c[5]))
+@pytest.mark.parametrize("case", CASES + UNALIGNED, ids=_case_id)
 def test_chunked_matches_oracle(case, alpha, corr):
     lengths, starts, Hq, Hkv, d, B, page = case
     print(f"chunked {case} alpha={alpha} corr={corr}", flush=True)
@@ -101,10 +114,11 @@ def test_chunked_matches_oracle(case, alpha, corr):
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
-@pytest.mark.parametrize("case", CASES[:2], ids=["B128", "B64"])
+@pytest.mark.parametrize("case", CASES[:2] + UNALIGNED, ids=_case_id)
 def test_chunked_equals_last_rows_of_whole_prompt(case):
-    """Chunks that start on block boundaries give bit-identical rows to the
-    whole-prompt entry: same pooled sums, same lists, same tiles in order."""
+    """Chunks give bit-identical rows to the whole-prompt entry: same pooled
+    sums, same lists, same tiles in order.  A chunk that starts inside a
+    block pools fewer queries there, so that block's rows are left out."""
     lengths, starts, Hq, Hkv, d, B, page = case
     pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=41, verticals=True, page_size=page)
     p = fp.make_params(Hq, Hkv, d, B, 0.2, mean_correction=True)
@@ -113,18 +127,22 @@ def test_chunked_equals_last_rows_of_whole_prompt(case):
     q, cu, kv_lens = _chunks(pb, starts)
     res = _run(pb, q, cu, kv_lens, Hq, Hkv, d, B, 0.2, True)
     for b, P0 in enumerate(starts):
-        f0 = int(pb.cu_seqlens[b]) + P0
+        skip = min(-P0 % B, cu[b + 1] - cu[b])             # rows of a block the chunk enters part way
+        f0 = int(pb.cu_seqlens[b]) + P0 + skip
         f1 = int(pb.cu_seqlens[b + 1])
-        assert torch.equal(res.out[cu[b]:cu[b + 1]], full.out[f0:f1]), b
-        assert torch.equal(res.lse[:, cu[b]:cu[b + 1]], full.lse[:, f0:f1]), b
+        assert torch.equal(res.out[cu[b] + skip:cu[b + 1]], full.out[f0:f1]), b
+        assert torch.equal(res.lse[:, cu[b] + skip:cu[b + 1]], full.lse[:, f0:f1]), b
 
 
-def test_pooled_cache_carries_the_prefix_between_calls():
+@pytest.mark.parametrize("cut", [[1024, 384], [1000, 333]], ids=["aligned", "unaligned"])
+def test_pooled_cache_carries_the_prefix_between_calls(cut):
     """Two calls over the same contexts: the first pools its chunks into the
     cache, the second reads those prefix means from it.  The second equals a
-    call that pools the prefix itself, and the cache is really read."""
+    call that pools the prefix itself, and the cache is really read.  With
+    an unaligned cut the block holding the cut is pooled again, whole, by
+    the second call."""
     lengths, Hq, Hkv, d, B, page = [1500, 700], 8, 2, 128, 128, 32
-    cut = [1024, 384]                                 # first chunk: tokens [0, cut)
+    # first chunk: tokens [0, cut)
     pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=77, verticals=True, page_size=page)
     num_pages = pb.k_cache.shape[0]
     p = fp.make_params(Hq, Hkv, d, B, 0.15, mean_correction=True)
@@ -164,7 +182,7 @@ def test_chunked_with_skeleton_queries_and_shared_lists():
     stay bit-identical to the whole-prompt entry with the same options."""
     lengths, starts, Hq, Hkv, d, B, page = CASES[0]
     pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=61, verticals=True, page_size=page)
-    for shared, probes in ((False, 16), (True, 0), (True, 4)):
+    for shared, probes in ((False, 16), (True, 0), (True, 4), ("pooled", 0), ("pooled", 8)):
         p = fp.make_params(Hq, Hkv, d, B, 0.2, mean_correction=True, shared_selection=shared,
                            query_probes=probes)
         full = fp.fp_sparse_prefill_varlen_paged(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),

@@ -164,11 +164,12 @@ def test_paged_batch8_chunked_last4096_full_size():
     print(f"  {cu_new[-1]} new rows and {cu_pre[-1]} prefix rows equal the whole-prompt rows", flush=True)
 
 
-@pytest.mark.parametrize("shared,probes", [(True, 0), (False, 16)], ids=["shared_lists", "skeleton16"])
+@pytest.mark.parametrize("shared,probes", [(True, 0), ("pooled", 0), (False, 16)],
+                         ids=["shared_lists", "pooled_lists", "skeleton16"])
 def test_128k_selection_options_full_size(s128k, shared, probes):
-    """The two selection options the benchmark times beside the headline, at
-    the 128K layer's full size: group-shared lists (the union of a KV head's
-    query heads' masks) and skeleton-query scoring (q_bar from 16 probes per
+    """The selection options, at the 128K layer's full size: group-shared
+    lists (the union of a KV head's query heads' masks, or the list of the
+    group-pooled query) and skeleton-query scoring (q_bar from 16 probes per
     block).  Lists match the oracle's outside the threshold band; sampled
     outputs match the oracle under the GPU's lists."""
     seq = s128k

@@ -122,17 +122,19 @@ def test_errors_leave_outputs_untouched():
     assert e.value.status == fp.FP_UNSUPPORTED
 
 
+@pytest.mark.parametrize("mode", ["union", "pooled"])
 @pytest.mark.parametrize("alpha", [0.1, 0.4, 0.9])
 @pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[2], SHAPES[6], SHAPES[7]],
                          ids=lambda s: "S%d_h%d-%d_d%d_B%d" % s[:5])
-def test_shared_selection(shape, alpha):
+def test_shared_selection(shape, alpha, mode):
     """Group-shared selection: one list per KV head (the union of its query
-    heads' lists), identical for the g heads, equal to the oracle's union
-    outside the threshold band, and attention on it matches the oracle."""
+    heads' lists, or the list of the group-pooled query), identical for the
+    g heads, equal to the oracle's outside the threshold band, and attention
+    on it matches the oracle."""
     S, Hq, Hkv, d, B, vert = shape
-    print(f"shared selection {shape} alpha={alpha}", flush=True)
+    print(f"shared selection {shape} alpha={alpha} mode={mode}", flush=True)
     q, k, v = _case(*shape, seed=5)
-    p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True, shared_selection=True)
+    p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True, shared_selection=mode)
     qd, kd, vd = (t.to(dev()) for t in (q, k, v))
     sel = fp.fp_select_blocks(p, qd, kd, vd)
     out, lse = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, return_lse=True)
@@ -143,11 +145,12 @@ def test_shared_selection(shape, alpha):
     for hk in range(Hkv):
         assert (mask[hk * g:(hk + 1) * g] == mask[hk * g]).all()
     qn, kn, vn = oracle_inputs(q, k, v)
-    ref = O.select_blocks(qn, kn, vn, B, alpha, shared=True)
+    ref = O.select_blocks(qn, kn, vn, B, alpha, shared=mode)
     own = O.select_blocks(qn, kn, vn, B, alpha)
     outside, inside, band = compare_mask(mask, ref)
     assert outside == 0, (outside, inside, band)
-    assert (mask | ~own.keep | own.band).all()              # covers every head's own mask
+    if mode == "union":
+        assert (mask | ~own.keep | own.band).all()          # covers every head's own mask
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, ref, True, keep=mask)
     err = np.abs(out.float().cpu().numpy() - o_ref).max()
     lerr = np.abs(lse.cpu().numpy() - lse_ref).max()

@@ -5,7 +5,8 @@ step, and scores a tile again only where some row can keep a block in it.
 These cases span several steps, head-group sizes that do not divide 32
 (unused score rows), one and many query heads per KV head, both head
 dimensions and both block sizes, a ragged last block and the dense and
-max-only thresholds.  Every (h, I, J) entry must match the oracle outside
+max-only thresholds, per-head lists and both group-shared forms (union and
+group-pooled query).  Every (h, I, J) entry must match the oracle outside
 the near-threshold band (FlashPrefill, gist.science technical summary,
 sections 2.A-2.C).
 """
@@ -44,7 +45,7 @@ def case(request):
     return request.param, (q, k, v), tuple(t.to(dev()) for t in (q, k, v)), oracle_inputs(q, k, v)
 
 
-@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("shared", [False, True, "pooled"], ids=["own", "union", "pooled"])
 @pytest.mark.parametrize("alpha", [0.0, 0.05, 0.3, 1.0])
 def test_lists_match_oracle(case, alpha, shared):
     (S, Hq, Hkv, d, B), _, (qd, kd, vd), (qn, kn, vn) = case
