@@ -30,8 +30,10 @@ namespace {
 
 constexpr int kWaves = 8;
 
+// Six waves per SIMD (three workgroups per CU): more loads in flight, at
+// the cost of a 16-byte spill.
 template <int D, int B>
-__global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a) {
     constexpr int CPH = D / 8;             // chunks per head
     constexpr int HPG = 32 / CPH;          // heads per workgroup
     constexpr int NS = B / (2 * kWaves);   // tokens per thread
@@ -134,6 +136,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_quant_pool(QuantArgs a) {
         return fminf(fmaxf(fmaf(r, ry, q), -kE4M3Max), kE4M3Max);
     };
     uint8_t* dst = a.codes[ts] + (int64_t)t0 * row + col;
+    // The codes convert the packed words again: the block's values would
+    // otherwise stay unpacked across the barrier (twice the registers).
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(x[s].x), "+v"(x[s].y), "+v"(x[s].z), "+v"(x[s].w));
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int tok = 2 * kWaves * s + 2 * w + hf;
