@@ -390,6 +390,21 @@ def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
                     "tflops": round(f_v / (tv * 1e-3) / 1e12, 2)}
     log(f"bench: paged {res['paged']}")
 
+    # The same batch in fp8: one pass writes the e4m3 paged cache, the Q codes
+    # and the means; selection on the bf16 means; fp8 attention on the pages.
+    p8 = fp.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, head["alpha"],
+                        mean_correction=corr, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    r8, c8 = fp.fp_sparse_prefill_varlen_paged_fp8(p8, qd, kc, vc, bt, pb.cu_seqlens)
+    t8 = timed_ms(lambda: fp.fp_sparse_prefill_varlen_paged_fp8(p8, qd, kc, vc, bt, pb.cu_seqlens, cache=c8,
+                                                                workspace=r8.workspace, out=r8.out), 5, stream)
+    kept8, skipped8 = list_work(r8.kv_idx, r8.kv_cnt, lens, [0] * len(lens), Hqp, Bp, dev)
+    f_8 = 4.0 * dp * Bp * (Bp * kept8 + (skipped8 if corr else 0))
+    res["paged_fp8"] = {"workload": w.name + "_fp8", "dtype": "fp8_e4m3", "tokens": cu[-1],
+                        "step_ms": round(t8, 4), "tokens_per_s": round(cu[-1] / (t8 * 1e-3), 1),
+                        "kept_blocks": kept8, "tflops": round(f_8 / (t8 * 1e-3) / 1e12, 2)}
+    log(f"bench: paged fp8 {res['paged_fp8']}")
+    del r8, c8
+
     # Chunked prefill on the same contexts: the last CHUNK tokens of each
     # request are new; the prefix means were pooled into the cache by an
     # earlier call (untimed), the timed call reads them from it.

@@ -54,6 +54,10 @@ EXPORTS = {
                                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                       _I32P, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P, _P, _P]),
+    "fp_sparse_prefill_varlen_paged_fp8": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
+                                                          ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                          _I32P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                                          ctypes.c_size_t, _P, _P, _P]),
     "fp_sparse_prefill_chunked_paged": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
                                                        ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                        _I32P, _I32P, ctypes.c_int32, _P, ctypes.c_int32,
@@ -275,6 +279,58 @@ def fp_sparse_prefill_varlen_paged(params: fp_params, q: torch.Tensor, k_cache: 
         _ptr(block_table), block_table.shape[1], cu, batch, _ptr(kv_idx), _ptr(kv_cnt),
         _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
     return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
+
+
+@dataclass
+class Fp8Cache:
+    """The fp8 paged cache: e4m3 pages shaped like the bf16 ones and fp32
+    scales [num_pages, Hkv], one per (page holding a block's first token, head)."""
+    k8: torch.Tensor
+    v8: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+
+
+def alloc_fp8_cache(k_cache: torch.Tensor) -> Fp8Cache:
+    num_pages, _, Hkv, _ = k_cache.shape
+    dev = k_cache.device
+    return Fp8Cache(torch.empty(k_cache.shape, dtype=torch.uint8, device=dev),
+                    torch.empty(k_cache.shape, dtype=torch.uint8, device=dev),
+                    torch.empty((num_pages, Hkv), dtype=torch.float32, device=dev),
+                    torch.empty((num_pages, Hkv), dtype=torch.float32, device=dev))
+
+
+def fp_sparse_prefill_varlen_paged_fp8(params: fp_params, q: torch.Tensor, k_cache: torch.Tensor,
+                                       v_cache: torch.Tensor, block_table: torch.Tensor, cu_seqlens,
+                                       return_lse: bool = False, cache: Optional[Fp8Cache] = None,
+                                       workspace: Optional[torch.Tensor] = None,
+                                       out: Optional[torch.Tensor] = None):
+    """fp8 inference over a paged batch (bf16 inputs): quantize + pool in one
+    pass (codes into the fp8 paged cache), selection, fp8 attention reading the
+    e4m3 pages.  Returns (VarlenResult, Fp8Cache)."""
+    T, Hq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    dev = q.device
+    cu = _cu_host(cu_seqlens)
+    batch = len(cu) - 1
+    cap = fp_index_capacity(params, list(cu))
+    ncnt = fp_count_entries(params, list(cu))
+    wsb = fp_varlen_workspace_bytes(params, list(cu))
+    kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty(max(ncnt, 1), dtype=torch.int32, device=dev)
+    if cache is None:
+        cache = alloc_fp8_cache(k_cache)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().fp_sparse_prefill_varlen_paged_fp8(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
+        _ptr(block_table), block_table.shape[1], cu, batch, _ptr(cache.k8), _ptr(cache.v8),
+        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(kv_idx), _ptr(kv_cnt),
+        _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return VarlenResult(out, lse, kv_idx, kv_cnt, workspace), cache
 
 
 def fp_chunked_sizes(params: fp_params, cu_seqlens_q: Sequence[int], kv_lens: Sequence[int]):

@@ -237,7 +237,9 @@ FP_EXPORT int64_t fp_count_entries(const fp_params* params, const int32_t* cu_se
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WsLayout {
-    size_t q, k, kv16, total;   // fp32 Q_bar, fp32 K_bar, bf16 K_bar | V_bar
+    size_t q, k, kv16;          // fp32 Q_bar, fp32 K_bar, bf16 K_bar | V_bar
+    size_t q8, qs;              // fp8 only: e4m3 Q codes [T, Hq, d], fp32 Q scales [Hq, blocks]
+    size_t total;
 };
 WsLayout ws_layout(const fp_params& p, const SeqTable& t) {
     WsLayout w;
@@ -245,7 +247,13 @@ WsLayout ws_layout(const fp_params& p, const SeqTable& t) {
     w.q = 0;
     w.k = align256((size_t)t.total_qblocks * p.head_dim * p.num_q_heads * sizeof(float));
     w.kv16 = w.k + align256(per * p.num_kv_heads * sizeof(float));
-    w.total = w.kv16 + (p.mean_correction ? align256(2 * per * p.num_kv_heads * sizeof(uint16_t)) : 0);
+    w.q8 = w.kv16 + (p.mean_correction ? align256(2 * per * p.num_kv_heads * sizeof(uint16_t)) : 0);
+    w.qs = w.q8;
+    w.total = w.q8;
+    if (p.dtype == FP_DTYPE_FP8_E4M3FN) {
+        w.qs = w.q8 + align256((size_t)t.total_tokens * p.num_q_heads * p.head_dim);
+        w.total = w.qs + align256((size_t)t.total_qblocks * p.num_q_heads * sizeof(float));
+    }
     return w;
 }
 }  // namespace
@@ -324,14 +332,14 @@ FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const
     qa.H[0] = p.num_q_heads;
     qa.H[1] = qa.H[2] = p.num_kv_heads;
     qa.groups[0] = qa.groups[1] = qa.groups[2] = 0;
-    qa.S = seqlen;
+    qa.kv = KVLayout{nullptr, 1, 0, 0};
     qa.D = p.head_dim;
     qa.B = p.block_size;
     qa.nB = t.total_blocks;
     qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = device_status(launch_quant_pool(qa, st), "quantize + pool");
+    rc = device_status(launch_quant_pool(qa, t, false, st), "quantize + pool");
     if (rc) return rc;
     rc = run_scores(p, cu, nullptr, 1, pooled_q, pooled_k, kv_idx, kv_cnt, st);
     return rc ? rc : ok();
@@ -381,7 +389,7 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
     a.correction = p.mean_correction;
     (void)hipGetLastError();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    rc = fp8 ? device_status(launch_attn_fp8(a, t, p.head_dim, p.block_size, st), "attention (fp8)")
+    rc = fp8 ? device_status(launch_attn_fp8(a, t, p.head_dim, p.block_size, false, st), "attention (fp8)")
              : device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, false, st), "attention");
     return rc ? rc : ok();
 }
@@ -463,6 +471,103 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
                          cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, workspace, workspace_bytes, out,
                          lse, stream);
+}
+
+FP_EXPORT int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const void* q, const void* k_cache,
+                                                 const void* v_cache, int32_t page_size, int32_t num_pages,
+                                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                                 const int32_t* cu_seqlens_host, int32_t batch, void* k8_cache,
+                                                 void* v8_cache, float* k_scale_cache, float* v_scale_cache,
+                                                 int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                                                 size_t workspace_bytes, void* out, float* lse, void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    const fp_params& p = *params;
+    if (p.dtype != FP_DTYPE_FP8_E4M3FN)
+        return fail(FP_INVALID_ARGUMENT, "fp_sparse_prefill_varlen_paged_fp8: params->dtype must be fp8");
+    SeqTable t;
+    rc = build_table(p, cu_seqlens_host, nullptr, batch, 1, t);
+    if (rc) return rc;
+    if (page_size < 1 || p.block_size % page_size != 0)
+        return fail(FP_INVALID_ARGUMENT, "page_size (%d) must divide block_size (%d)", page_size, p.block_size);
+    if (num_pages < 1) return fail(FP_INVALID_ARGUMENT, "num_pages must be >= 1");
+    for (int b = 0; b < batch; ++b) {
+        const int64_t len = (int64_t)cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+        if ((len + page_size - 1) / page_size > max_pages_per_seq)
+            return fail(FP_INVALID_ARGUMENT, "request %d needs %lld pages > max_pages_per_seq %d", b,
+                        (long long)((len + page_size - 1) / page_size), max_pages_per_seq);
+    }
+    if (t.total_tokens == 0) return ok();
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(FP_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be non-NULL and 16-byte aligned");
+    if (!aligned(k8_cache, 16) || !aligned(v8_cache, 16))
+        return fail(FP_INVALID_ARGUMENT, "k8_cache and v8_cache must be non-NULL and 16-byte aligned");
+    if (!aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4))
+        return fail(FP_INVALID_ARGUMENT, "k_scale_cache and v_scale_cache must be non-NULL and 4-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+        return fail(FP_INVALID_ARGUMENT, "block_table, kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    const WsLayout ws = ws_layout(p, t);
+    if (!aligned(workspace, 256)) return fail(FP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < ws.total)
+        return fail(FP_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", workspace_bytes, ws.total);
+    char* wsb = static_cast<char*>(workspace);
+    float* pq = reinterpret_cast<float*>(wsb + ws.q);
+    float* pk = reinterpret_cast<float*>(wsb + ws.k);
+    uint16_t* pkv16 = p.mean_correction ? reinterpret_cast<uint16_t*>(wsb + ws.kv16) : nullptr;
+    uint8_t* q8 = reinterpret_cast<uint8_t*>(wsb + ws.q8);
+    float* qs = reinterpret_cast<float*>(wsb + ws.qs);
+    const KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
+    // One pass over the bf16 data: Q codes and scales into the workspace, K
+    // and V codes into the e4m3 pages with their scales, the block means.
+    QuantArgs qa;
+    qa.src[0] = static_cast<const uint16_t*>(q);
+    qa.src[1] = static_cast<const uint16_t*>(k_cache);
+    qa.src[2] = static_cast<const uint16_t*>(v_cache);
+    qa.codes[0] = q8;
+    qa.codes[1] = static_cast<uint8_t*>(k8_cache);
+    qa.codes[2] = static_cast<uint8_t*>(v8_cache);
+    qa.scale[0] = qs;
+    qa.scale[1] = k_scale_cache;
+    qa.scale[2] = v_scale_cache;
+    qa.pq = pq;
+    qa.pk = pk;
+    qa.pkv16 = pkv16;
+    qa.kv = kv;
+    qa.H[0] = p.num_q_heads;
+    qa.H[1] = qa.H[2] = p.num_kv_heads;
+    qa.groups[0] = qa.groups[1] = qa.groups[2] = 0;
+    qa.D = p.head_dim;
+    qa.B = p.block_size;
+    qa.nB = t.total_blocks;
+    qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    rc = device_status(launch_quant_pool(qa, t, true, st), "quantize + pool (paged)");
+    if (rc) return rc;
+    rc = run_scores(p, cu_seqlens_host, nullptr, batch, pq, pk, kv_idx, kv_cnt, st);
+    if (rc) return rc;
+    AttnArgs a;
+    a.q = q8;
+    a.k = k8_cache;
+    a.v = v8_cache;
+    a.q_scale = qs;
+    a.k_scale = k_scale_cache;
+    a.v_scale = v_scale_cache;
+    a.kv_idx = kv_idx;
+    a.kv_cnt = kv_cnt;
+    a.pk16 = pkv16;
+    a.pv16 = pkv16 ? pkv16 + (int64_t)p.num_kv_heads * t.total_blocks * p.head_dim : nullptr;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.kv = kv;
+    a.Hq = p.num_q_heads;
+    a.Hkv = p.num_kv_heads;
+    a.g = p.num_q_heads / p.num_kv_heads;
+    a.scale_log2 = (float)(sigma_of(p) * 1.4426950408889634);
+    a.correction = p.mean_correction;
+    rc = device_status(launch_attn_fp8(a, t, p.head_dim, p.block_size, true, st), "attention (fp8, paged)");
+    return rc ? rc : ok();
 }
 
 FP_EXPORT int fp_chunked_sizes(const fp_params* params, const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,

@@ -60,20 +60,21 @@ struct AttnArgs {
 // Fused fp8 quantization + pooling of one sequence (tensors 0, 1, 2 = Q, K, V).
 constexpr float kE4M3Max = 448.f;
 struct QuantArgs {
-    const uint16_t* src[3];      // bf16 [S, H, d]
-    uint8_t* codes[3];           // e4m3 codes [S, H, d]
-    float* scale[3];             // fp32 [H, nB]
+    const uint16_t* src[3];      // bf16 [T, H, d] packed rows; K and V may be pages [num_pages, page, Hkv, d]
+    uint8_t* codes[3];           // e4m3 codes in the layout of src
+    float* scale[3];             // fp32 [H, nB]; paged K and V: [num_pages, Hkv], entry of a block's first page
     float* pq;                   // fp32 Q_bar [Hq, nB, d]
     float* pk;                   // fp32 K_bar [Hkv, nB, d]
     uint16_t* pkv16;             // bf16 [2, Hkv, nB, d] (K_bar then V_bar) or null
+    KVLayout kv;                 // pages of K and V (used when paged)
     int32_t H[3];                // Hq, Hkv, Hkv
     int32_t groups[3];           // head groups per tensor (set by the launcher)
-    int32_t S, D, B, nB;
+    int32_t D, B, nB;            // nB: blocks of all requests
     int32_t q_stride;            // Q_bar averages the block's tokens 0, q_stride, 2 q_stride, ...
 };
 
 hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s);
-hipError_t launch_quant_pool(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s);
 hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);
-hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);

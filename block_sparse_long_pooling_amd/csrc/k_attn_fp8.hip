@@ -225,7 +225,7 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
     lds_barrier();                                       // buffers free for the output staging
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool PAGED>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t) {
     using T = Tile<D, BLK>;          // bf16 geometry: LDS sized for the correction tiles
     __shared__ uint4 lk[BLK * T::KCH];
@@ -282,12 +282,17 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     plan.init(tid);
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
     const int64_t rs2 = (int64_t)a.Hkv * D / 2;          // row stride in 2-byte units
-    const uint16_t* kfirst = reinterpret_cast<const uint16_t*>(k8 + ((int64_t)tok0 * a.Hkv + hk) * D);
-    const uint16_t* vfirst = reinterpret_cast<const uint16_t*>(v8 + ((int64_t)tok0 * a.Hkv + hk) * D);
+    // Contiguous: the request's rows; paged: the pools (page ids per tile).
+    const int64_t kvbase = ((PAGED ? 0 : (int64_t)tok0 * a.Hkv) + hk) * D;
+    const uint16_t* kfirst = reinterpret_cast<const uint16_t*>(k8 + kvbase);
+    const uint16_t* vfirst = reinterpret_cast<const uint16_t*>(v8 + kvbase);
+    const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
     auto issue8 = [&](int J, char* dst) {
-        issue_tile<D / 2, BLK, NTH, false>(kfirst, nullptr, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk, dst,
+        int pg[DmaPlan<D / 2, BLK, NTH>::NLOAD];
+        if (PAGED) load_tile_pages(pages, a.kv, J, len - J * BLK, plan, pg);
+        issue_tile<D / 2, BLK, NTH, PAGED>(kfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk, dst,
                                            wave_base);
-        issue_tile<D / 2, BLK, NTH, false>(vfirst, nullptr, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk,
+        issue_tile<D / 2, BLK, NTH, PAGED>(vfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk,
                                            dst + VOFF, wave_base);
     };
     char* buf0 = reinterpret_cast<char*>(lk);
@@ -303,8 +308,17 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         wbase = base;
         const int i = min(base + lane, cnt - 1);
         wJ = list[i];
-        wsk = a.k_scale[srow + wJ];
-        wsv = a.v_scale[srow + wJ];
+        if (PAGED) {
+            // Paged scales: [num_pages, Hkv], the entry of the block's first page.
+            const int page = pages[wJ * BLK / a.kv.page_size];
+            const bool ok = (unsigned)page < (unsigned)a.kv.num_pages;
+            const int64_t e = (int64_t)(ok ? page : 0) * a.Hkv + hk;
+            wsk = ok ? a.k_scale[e] : 0.f;
+            wsv = ok ? a.v_scale[e] : 0.f;
+        } else {
+            wsk = a.k_scale[srow + wJ];
+            wsv = a.v_scale[srow + wJ];
+        }
         __builtin_amdgcn_s_waitcnt(0);                   // settled here, not at a later use among DMAs
     };
     auto from_window = [&](int it, int& J, float& sk, float& sv) {
@@ -383,19 +397,22 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
 }
 
 template <int D, int BLK>
-hipError_t launch_fp8_t(const AttnArgs& a, const SeqTable& t, hipStream_t s) {
+hipError_t launch_fp8_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     dim3 grid((unsigned)t.total_items * a.Hq);
-    hipLaunchKernelGGL((k_attn_fp8<D, BLK>), grid, dim3(2 * BLK), 0, s, a, t);
+    if (paged)
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, true>), grid, dim3(2 * BLK), 0, s, a, t);
+    else
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, false>), grid, dim3(2 * BLK), 0, s, a, t);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, hipStream_t s) {
+hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s) {
     if (t.total_items == 0) return hipSuccess;
-    if (D == 128 && B == 128) return launch_fp8_t<128, 128>(a, t, s);
-    if (D == 128 && B == 64) return launch_fp8_t<128, 64>(a, t, s);
-    if (D == 64 && B == 128) return launch_fp8_t<64, 128>(a, t, s);
-    if (D == 64 && B == 64) return launch_fp8_t<64, 64>(a, t, s);
+    if (D == 128 && B == 128) return launch_fp8_t<128, 128>(a, t, paged, s);
+    if (D == 128 && B == 64) return launch_fp8_t<128, 64>(a, t, paged, s);
+    if (D == 64 && B == 128) return launch_fp8_t<64, 128>(a, t, paged, s);
+    if (D == 64 && B == 64) return launch_fp8_t<64, 64>(a, t, paged, s);
     return hipErrorInvalidValue;
 }

@@ -4,6 +4,9 @@
 // clamp(x / scale), and the pooled means that drive selection are those of
 // the bf16 data, as in the pooling kernel).
 //
+// Blocks are those of a request table (one sequence, or a batch whose K and
+// V rows may live in a paged cache: codes then go to the same place in an
+// e4m3 page pool, and each block's scale to the entry of its first page).
 // A workgroup (8 waves) owns one block of one tensor for a group of heads
 // whose chunks of 8 bf16 make 32 chunks per token row (two heads at d 128,
 // four at d 64), i.e. 512 contiguous bytes.  Lane l of wave w handles chunk
@@ -32,15 +35,15 @@ constexpr int kWaves = 8;
 
 // Six waves per SIMD (three workgroups per CU): more loads in flight, at
 // the cost of a 16-byte spill.
-template <int D, int B>
-__global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a) {
+template <int D, int B, bool PAGED>
+__global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqTable t) {
     constexpr int CPH = D / 8;             // chunks per head
     constexpr int HPG = 32 / CPH;          // heads per workgroup
     constexpr int NS = B / (2 * kWaves);   // tokens per thread
     __shared__ float psum[kWaves][32][8];
     __shared__ float pmax[kWaves][HPG];
 
-    const int J = blockIdx.x;
+    const int J = blockIdx.x;                       // block of all requests
     int g = blockIdx.y, ts = 0;
     if (g >= a.groups[0]) {
         g -= a.groups[0];
@@ -56,17 +59,26 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a) {
     const int hl = ch / CPH;               // head within the group
     const int h = g * HPG + hl;
     const bool hv = h < H;
-    const int t0 = J * B;
-    const int n = min(B, a.S - t0);
+    const int b = request_of_block(t, J);
+    const int I = J - t.blk_off[b];                 // block of request b
+    const int t0 = I * B;
+    const int n = min(B, context_len(t, b, B) - t0);
+    const bool pg = PAGED && ts > 0;                // K and V rows live in pages
+    const int64_t row0 = (int64_t)t.tok_off[b] + t0;   // packed rows of the block
+    const KVLayout kv = a.kv;
+    // Row of token tok of this block (-1: a page id out of range, read as
+    // zeros and not written).
+    auto row_of = [=](int tok) -> int64_t { return pg ? kv_row<true>(kv, b, 0, t0 + tok) : row0 + tok; };
     const int64_t row = (int64_t)H * D;
     const int64_t col = (int64_t)g * HPG * D + ch * 8;
-    const uint16_t* src = a.src[ts] + (int64_t)t0 * row + col;
+    const uint16_t* src = a.src[ts] + col;
 
     uint4 x[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int tok = 2 * kWaves * s + 2 * w + hf;
-        x[s] = (hv && tok < n) ? *reinterpret_cast<const uint4*>(src + tok * row) : make_uint4(0, 0, 0, 0);
+        const int64_t r = row_of(min(tok, n - 1));
+        x[s] = (hv && tok < n && r >= 0) ? *reinterpret_cast<const uint4*>(src + r * row) : make_uint4(0, 0, 0, 0);
     }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float amax = 0.f;
@@ -128,14 +140,22 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a) {
             *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
                 make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
                            pack_bf16(m[6], m[7]));
-        if (ch % CPH == 0) a.scale[ts][(int64_t)h * a.nB + J] = sc;
+        if (ch % CPH == 0) {
+            if (pg) {
+                // Paged K and V: the scale goes with the page of the block's first token.
+                const int page = a.kv.block_table[(int64_t)b * a.kv.max_pages + t0 / a.kv.page_size];
+                if ((unsigned)page < (unsigned)a.kv.num_pages) a.scale[ts][(int64_t)page * H + h] = sc;
+            } else {
+                a.scale[ts][(int64_t)h * a.nB + J] = sc;
+            }
+        }
     }
     auto quot = [&](float xv) {
         const float q = xv * ry;
         const float r = fmaf(-q, sc, xv);
         return fminf(fmaxf(fmaf(r, ry, q), -kE4M3Max), kE4M3Max);
     };
-    uint8_t* dst = a.codes[ts] + (int64_t)t0 * row + col;
+    uint8_t* dst = a.codes[ts] + col;
     // The codes convert the packed words again: the block's values would
     // otherwise stay unpacked across the barrier (twice the registers).
 #pragma unroll
@@ -158,27 +178,31 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a) {
             v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
             out[i] = (uint32_t)v;
         }
-        *reinterpret_cast<uint2*>(dst + tok * row) = make_uint2(out[0], out[1]);
+        const int64_t r = row_of(tok);
+        if (r >= 0) *reinterpret_cast<uint2*>(dst + r * row) = make_uint2(out[0], out[1]);
     }
 }
 
 template <int D, int B>
-hipError_t launch_t(const QuantArgs& a, hipStream_t s) {
+hipError_t launch_t(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     constexpr int HPG = 32 / (D / 8);
     QuantArgs b = a;
     for (int i = 0; i < 3; ++i) b.groups[i] = (a.H[i] + HPG - 1) / HPG;
-    hipLaunchKernelGGL((k_quant_pool<D, B>), dim3(a.nB, b.groups[0] + b.groups[1] + b.groups[2]), dim3(64 * kWaves),
-                       0, s, b);
+    const dim3 grid(a.nB, b.groups[0] + b.groups[1] + b.groups[2]);
+    if (paged)
+        hipLaunchKernelGGL((k_quant_pool<D, B, true>), grid, dim3(64 * kWaves), 0, s, b, t);
+    else
+        hipLaunchKernelGGL((k_quant_pool<D, B, false>), grid, dim3(64 * kWaves), 0, s, b, t);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_quant_pool(const QuantArgs& a, hipStream_t s) {
+hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     if (a.nB == 0) return hipSuccess;
-    if (a.D == 128 && a.B == 128) return launch_t<128, 128>(a, s);
-    if (a.D == 128 && a.B == 64) return launch_t<128, 64>(a, s);
-    if (a.D == 64 && a.B == 128) return launch_t<64, 128>(a, s);
-    if (a.D == 64 && a.B == 64) return launch_t<64, 64>(a, s);
+    if (a.D == 128 && a.B == 128) return launch_t<128, 128>(a, t, paged, s);
+    if (a.D == 128 && a.B == 64) return launch_t<128, 64>(a, t, paged, s);
+    if (a.D == 64 && a.B == 128) return launch_t<64, 128>(a, t, paged, s);
+    if (a.D == 64 && a.B == 64) return launch_t<64, 64>(a, t, paged, s);
     return hipErrorInvalidValue;
 }

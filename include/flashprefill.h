@@ -161,7 +161,8 @@ int fp_sparse_prefill_fwd(const fp_params* params,
  *   workspace: device scratch of at least fp_varlen_workspace_bytes() bytes
  *     (pooled means); contents on return are unspecified.
  *   out [T,Hq,d] bf16, lse [Hq,T] fp32 or NULL.
- * bf16 only (FP_UNSUPPORTED for fp8).  batch <= FP_MAX_BATCH.
+ * bf16 only (FP_UNSUPPORTED for fp8; see fp_sparse_prefill_varlen_paged_fp8).
+ * batch <= FP_MAX_BATCH.
  */
 #define FP_MAX_BATCH 128
 int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
@@ -171,6 +172,41 @@ int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
                                    const int32_t* cu_seqlens_host, int32_t batch, int32_t* kv_idx, int32_t* kv_cnt,
                                    void* workspace, size_t workspace_bytes,
                                    void* out, float* lse, void* stream);
+
+/*
+ * fp8 inference over a paged batch (FlashPrefill V2 abstract: FP8 inference,
+ * paged KV cache and continuous batching): the requests of
+ * fp_sparse_prefill_varlen_paged, with params->dtype = FP_DTYPE_FP8_E4M3FN.
+ * One pass over the bf16 data writes the e4m3 codes with one scale per
+ * (head, block) (the recipe of fp_select_blocks_fp8) and the block means;
+ * selection runs on the means of the bf16 data; attention runs on the codes,
+ * reading K and V from the e4m3 pages.
+ *   q, k_cache, v_cache, page_size, num_pages, block_table,
+ *     max_pages_per_seq, cu_seqlens_host, batch: as for
+ *     fp_sparse_prefill_varlen_paged (bf16 inputs).
+ *   k8_cache, v8_cache [num_pages, page_size, Hkv, d] uint8 e4m3 codes, 16-byte
+ *     aligned (written): the fp8 paged cache.  Each token's codes go to the
+ *     place its bf16 values have in k_cache / v_cache; pages no request
+ *     names are left untouched.
+ *   k_scale_cache, v_scale_cache [num_pages, Hkv] fp32 (written): the scale of
+ *     head h of a block sits at the entry [p][h] of the page p that holds the
+ *     block's first token.
+ *   kv_idx, kv_cnt: list outputs, as for fp_sparse_prefill_varlen_paged.
+ *   workspace: at least fp_varlen_workspace_bytes() bytes for these params
+ *     (with dtype fp8 it includes the Q codes and scales).
+ *   out [T,Hq,d] bf16, lse [Hq,T] fp32 or NULL.
+ * FP_INVALID_ARGUMENT when params->dtype is not fp8.
+ */
+int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       int32_t page_size, int32_t num_pages,
+                                       const int32_t* block_table, int32_t max_pages_per_seq,
+                                       const int32_t* cu_seqlens_host, int32_t batch,
+                                       void* k8_cache, void* v8_cache,
+                                       float* k_scale_cache, float* v_scale_cache,
+                                       int32_t* kv_idx, int32_t* kv_cnt,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* out, float* lse, void* stream);
 
 /*
  * Chunked prefill over a paged KV cache (FlashPrefill V2 abstract and the

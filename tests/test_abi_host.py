@@ -231,3 +231,24 @@ def test_shared_selection_names():
             for x in (False, True, "union", "pooled")] == [0, 1, 1, 2]
     with pytest.raises(ValueError):
         fp.make_params(4, 1, 64, 64, 0.1, shared_selection="mean")
+
+
+def test_fp8_paged_validation_and_workspace():
+    l = fp.lib()
+    cu = (ctypes.c_int32 * 3)(0, 1000, 1300)
+    p16, p8 = _p(), _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    ws16 = l.fp_varlen_workspace_bytes(ctypes.byref(p16), cu, 2)
+    ws8 = l.fp_varlen_workspace_bytes(ctypes.byref(p8), cu, 2)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert ws8 == ws16 + a256(1300 * 32 * 128) + a256(11 * 32 * 4)     # Q codes + Q scales (11 blocks)
+
+    def call(p, k8=FAKE, ks=FAKE, ws=1 << 30):
+        return l.fp_sparse_prefill_varlen_paged_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, 64, 100, FAKE, 64, cu, 2,
+                                                    k8, FAKE, ks, FAKE, FAKE, FAKE, ctypes.c_void_p(1 << 24), ws,
+                                                    FAKE, None, None)
+    assert call(p16) == fp.FP_INVALID_ARGUMENT                          # bf16 params
+    assert "fp8" in l.fp_last_error().decode()
+    assert call(p8, k8=None) == fp.FP_INVALID_ARGUMENT                  # no fp8 pages
+    assert call(p8, k8=MISALIGNED) == fp.FP_INVALID_ARGUMENT
+    assert call(p8, ks=None) == fp.FP_INVALID_ARGUMENT                  # no scale cache
+    assert call(p8, ws=ws16) == fp.FP_WORKSPACE_TOO_SMALL               # the bf16 size is not enough
