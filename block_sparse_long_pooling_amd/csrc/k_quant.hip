@@ -64,14 +64,16 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     const int t0 = I * B;
     const int n = min(B, context_len(t, b, B) - t0);
     const bool pg = PAGED && ts > 0;                // K and V rows live in pages
-    const int64_t row0 = (int64_t)t.tok_off[b] + t0;   // packed rows of the block
-    const KVLayout kv = a.kv;
-    // Row of token tok of this block (-1: a page id out of range, read as
-    // zeros and not written).
-    auto row_of = [=](int tok) -> int64_t { return pg ? kv_row<true>(kv, b, 0, t0 + tok) : row0 + tok; };
     const int64_t row = (int64_t)H * D;
     const int64_t col = (int64_t)g * HPG * D + ch * 8;
-    const uint16_t* src = a.src[ts] + col;
+    // Packed rows: offsets from the block's first row; paged rows: from the
+    // pool's start.
+    const int64_t base = pg ? col : ((int64_t)t.tok_off[b] + t0) * row + col;
+    const KVLayout kv = a.kv;
+    // Row of token tok of this block relative to the base (-1: a page id out
+    // of range, read as zeros and not written).
+    auto row_of = [=](int tok) -> int64_t { return pg ? kv_row<true>(kv, b, 0, t0 + tok) : tok; };
+    const uint16_t* src = a.src[ts] + base;
 
     uint4 x[NS];
 #pragma unroll
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
         const float r = fmaf(-q, sc, xv);
         return fminf(fmaxf(fmaf(r, ry, q), -kE4M3Max), kE4M3Max);
     };
-    uint8_t* dst = a.codes[ts] + col;
+    uint8_t* dst = a.codes[ts] + base;
     // The codes convert the packed words again: the block's values would
     // otherwise stay unpacked across the barrier (twice the registers).
 #pragma unroll
