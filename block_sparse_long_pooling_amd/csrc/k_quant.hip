@@ -152,10 +152,12 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
             }
         }
     }
+    // The correction step turns a quotient of -0 into +0 (-0 + +0 rounds to
+    // +0); the sign of x restores it, so -0 inputs encode as -0 like x / scale.
     auto quot = [&](float xv) {
         const float q = xv * ry;
         const float r = fmaf(-q, sc, xv);
-        return fminf(fmaxf(fmaf(r, ry, q), -kE4M3Max), kE4M3Max);
+        return fminf(fmaxf(copysignf(fmaf(r, ry, q), xv), -kE4M3Max), kE4M3Max);
     };
     uint8_t* dst = a.codes[ts] + base;
     // The codes convert the packed words again: the block's values would

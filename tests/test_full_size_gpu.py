@@ -11,7 +11,7 @@ import block_sparse_long_pooling_amd as fp
 import oracle as O
 from block_sparse_long_pooling_amd import synth
 
-from gpu_util import BF16_TOL, LSE_TOL, check_lists, compare_mask, dev
+from gpu_util import BF16_TOL, FP8_TOL, LSE_TOL, check_lists, compare_mask, dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -124,6 +124,52 @@ def test_paged_batch8_full_size():
         idx_off += Hq * nb * (nb + 1) // 2
         cnt_off += Hq * nb
     print(f"  overall density {kept_total / causal_total:.4f}", flush=True)
+
+
+def test_paged_batch8_fp8_full_size():
+    """The fp8 paged entry in the configuration the benchmark times (8
+    requests, 307,200 tokens): the e4m3 pages and their page-keyed scales
+    equal the oracle's quantizer per request bit for bit, the lists match the
+    oracle outside the band, and sampled outputs match the oracle's attention
+    on the dequantized codes under the GPU's lists."""
+    w = synth.WORKLOADS["paged_batch8"]
+    Hq, Hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print("generating paged_batch8 (fp8)", flush=True)
+    pb = synth.workload_inputs(w)
+    page = pb.k_cache.shape[1]
+    p = fp.make_params(Hq, Hkv, d, B, w.alphas[0], mean_correction=True, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    res, cache = fp.fp_sparse_prefill_varlen_paged_fp8(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
+                                                       pb.block_table.to(dev()), pb.cu_seqlens)
+    torch.cuda.synchronize()
+    out = res.out.float().cpu().numpy()
+    assert np.isfinite(out).all()
+    k8, v8 = cache.k8.cpu(), cache.v8.cpu()
+    ks, vs = cache.k_scale.cpu().numpy(), cache.v_scale.cpu().numpy()
+    idx_off, cnt_off = 0, 0
+    for b, L in enumerate(pb.seqlens):
+        nb = (L + B - 1) // B
+        qb, kb, vb = (t.float().numpy() for t in pb.requests[b])
+        pages = pb.block_table[b, :(L + page - 1) // page].tolist()
+        deq = []
+        for x, pool, sc in ((qb, None, None), (kb, k8, ks), (vb, v8, vs)):
+            c_ref, s_ref = O.quantize_fp8_blockwise(x, B)
+            if pool is not None:
+                assert np.array_equal(pool[pages].reshape(-1, Hkv, d)[:L].numpy(), c_ref), b
+                assert np.array_equal(np.stack([sc[pages[J * B // page]] for J in range(nb)], axis=1), s_ref), b
+            deq.append(O.dequantize_blockwise(synth.fp8_codes_to_float(torch.from_numpy(c_ref)).numpy(), s_ref, B))
+        mask = check_lists(res.kv_idx, res.kv_cnt, Hq, nb, offset=idx_off, cnt_offset=cnt_off)
+        ref = O.select_blocks(qb, kb, vb, B, w.alphas[0])
+        outside, inside, band = compare_mask(mask, ref)
+        assert outside == 0, (b, outside)
+        pairs = _sample_pairs(Hq, nb, 6, seed=50 + b)
+        o_ref, _ = O.sparse_attention(deq[0], deq[1], deq[2], ref, True, pairs=pairs, keep=mask)
+        t0 = int(pb.cu_seqlens[b])
+        worst = max(float(np.abs(out[t0 + I * B:t0 + min(L, (I + 1) * B), h] - o_ref[I * B:min(L, (I + 1) * B), h]).max())
+                    for h, I in pairs)
+        print(f"  request {b} L={L}: kept {int(mask.sum())}, sampled max|o-ref| {worst:.3e}", flush=True)
+        assert worst <= FP8_TOL, (b, worst)
+        idx_off += Hq * nb * (nb + 1) // 2
+        cnt_off += Hq * nb
 
 
 def test_paged_batch8_chunked_last4096_full_size():
