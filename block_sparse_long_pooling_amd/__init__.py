@@ -68,6 +68,8 @@ EXPORTS = {
     "fp_index_capacity": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
     "fp_count_entries": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
     "fp_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32]),
+    "fp_attention_workgroups": (ctypes.c_int64, [ctypes.POINTER(fp_params), _I32P, ctypes.c_int32,
+                                                 ctypes.c_int32]),
     "fp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp_last_error": (ctypes.c_char_p, []),
 }
@@ -139,6 +141,14 @@ def fp_count_entries(params: fp_params, cu_seqlens: Sequence[int]) -> int:
 def fp_varlen_workspace_bytes(params: fp_params, cu_seqlens: Sequence[int]) -> int:
     cu = _cu_host(cu_seqlens)
     return int(lib().fp_varlen_workspace_bytes(ctypes.byref(params), cu, len(cu) - 1))
+
+
+def fp_attention_workgroups(params: fp_params, cu_seqlens: Sequence[int], paged: bool = False) -> int:
+    """Workgroups the attention launch uses for these lengths on the current
+    device (bf16: the persistent grid of this kernel variant; fp8: one per
+    query block and head); -1 for invalid arguments."""
+    cu = _cu_host(cu_seqlens)
+    return int(lib().fp_attention_workgroups(ctypes.byref(params), cu, len(cu) - 1, int(bool(paged))))
 
 
 @dataclass

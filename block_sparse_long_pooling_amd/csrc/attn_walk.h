@@ -5,7 +5,7 @@
 // means that form the correction (FlashPrefill, gist.science technical
 // summary, section 2.C; FlashPrefill V2 abstract).
 #pragma once
-#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fp_attn.h"
@@ -279,24 +279,38 @@ struct Item {
 constexpr int kCorr = FP_MAX_BLOCKS;
 
 // Persistent grid: as many workgroups as the device holds at once (a multiple
-// of the 8 XCDs), at most one per item.  The resident count is computed once
-// per kernel and device.
+// of the 8 XCDs), at most one per item.  The resident count depends on the
+// kernel (its registers and LDS) and the block size, so it is computed once
+// per (kernel, block size, device) and cached under that key: every
+// instantiation of a kernel template has the same function type, so a cache
+// keyed by type alone would let the first variant launched size all others.
+inline int resident_workgroups(const void* kernel, int block) {
+    struct Entry {
+        const void* fn;
+        int block, dev, n;
+    };
+    constexpr int kMaxEntries = 256;
+    static std::mutex mu;
+    static Entry cache[kMaxEntries];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == kernel && cache[i].block == block && cache[i].dev == dev) return cache[i].n;
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
+        return 0;
+    const int n = max(8, (ncu * max(per_cu, 1)) / 8 * 8);
+    if (used < kMaxEntries) cache[used++] = Entry{kernel, block, dev, n};
+    return n;
+}
+
 template <typename K>
 int persistent_grid(K kernel, int block, int nitems) {
-    constexpr int kMaxDev = 64;
-    static std::atomic<int> resident[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nitems;
-    int n = resident[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        int ncu = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
-            return nitems;
-        n = max(8, (ncu * max(per_cu, 1)) / 8 * 8);
-        resident[dev].store(n, std::memory_order_relaxed);
-    }
-    return max(1, min(nitems, n));
+    const int n = resident_workgroups(reinterpret_cast<const void*>(kernel), block);
+    return n > 0 ? max(1, min(nitems, n)) : nitems;
 }
 
 }  // namespace fp_walk

@@ -336,22 +336,32 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
 }
 
 template <int D, int BLK, int HP>
-hipError_t launch_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+int grid_t(const AttnArgs& a, const SeqTable& t, bool paged) {
     const int nitems = t.total_items * (a.Hq / HP);
     const int block = 64 * HP * (BLK / 32);
-    if (paged) {
-        auto k = k_attn_bf16<D, BLK, HP, true>;
-        hipLaunchKernelGGL(k, dim3(persistent_grid(k, block, nitems)), dim3(block), 0, s, a, t);
-    } else {
-        auto k = k_attn_bf16<D, BLK, HP, false>;
-        hipLaunchKernelGGL(k, dim3(persistent_grid(k, block, nitems)), dim3(block), 0, s, a, t);
-    }
+    return paged ? persistent_grid(k_attn_bf16<D, BLK, HP, true>, block, nitems)
+                 : persistent_grid(k_attn_bf16<D, BLK, HP, false>, block, nitems);
+}
+
+template <int D, int BLK, int HP>
+hipError_t launch_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+    const int block = 64 * HP * (BLK / 32);
+    const dim3 grid(grid_t<D, BLK, HP>(a, t, paged));
+    if (paged)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, true>), grid, dim3(block), 0, s, a, t);
+    else
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, HP, false>), grid, dim3(block), 0, s, a, t);
     return hipGetLastError();
 }
 
 template <int D, int BLK>
 hipError_t launch_db(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     return (a.g % 2 == 0) ? launch_t<D, BLK, 2>(a, t, paged, s) : launch_t<D, BLK, 1>(a, t, paged, s);
+}
+
+template <int D, int BLK>
+int grid_db(const AttnArgs& a, const SeqTable& t, bool paged) {
+    return (a.g % 2 == 0) ? grid_t<D, BLK, 2>(a, t, paged) : grid_t<D, BLK, 1>(a, t, paged);
 }
 
 }  // namespace
@@ -363,4 +373,13 @@ hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, 
     if (D == 64 && B == 128) return launch_db<64, 128>(a, t, paged, s);
     if (D == 64 && B == 64) return launch_db<64, 64>(a, t, paged, s);
     return hipErrorInvalidValue;
+}
+
+int attn_bf16_grid(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged) {
+    if (t.total_items == 0) return 0;
+    if (D == 128 && B == 128) return grid_db<128, 128>(a, t, paged);
+    if (D == 128 && B == 64) return grid_db<128, 64>(a, t, paged);
+    if (D == 64 && B == 128) return grid_db<64, 128>(a, t, paged);
+    if (D == 64 && B == 64) return grid_db<64, 64>(a, t, paged);
+    return -1;
 }

@@ -60,6 +60,19 @@ def test_sizes():
     assert fp.fp_index_capacity(p, [1, S]) == -1
 
 
+def test_attention_workgroups_host():
+    """fp8 attention launches one workgroup per (query block, head); bad
+    arguments give -1 (the bf16 persistent grid needs a device and is checked
+    by the GPU tests)."""
+    p8 = _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    assert fp.fp_attention_workgroups(p8, [0, 1000]) == 32 * 8
+    assert fp.fp_attention_workgroups(p8, [0, 100, 300, 300, 1000]) == 32 * (1 + 2 + 0 + 6)
+    assert fp.fp_attention_workgroups(_p(head_dim=96), [0, 1000]) == -1
+    assert fp.fp_attention_workgroups(_p(), [1, 1000]) == -1
+    cu = (ctypes.c_int32 * 2)(0, 1000)
+    assert fp.lib().fp_attention_workgroups(ctypes.byref(_p()), cu, 1, 2) == -1
+
+
 BAD_PARAMS = [
     (dict(num_q_heads=30, num_kv_heads=8), fp.FP_INVALID_ARGUMENT),
     (dict(num_kv_heads=0), fp.FP_INVALID_ARGUMENT),
@@ -252,3 +265,4 @@ def test_fp8_paged_validation_and_workspace():
     assert call(p8, k8=MISALIGNED) == fp.FP_INVALID_ARGUMENT
     assert call(p8, ks=None) == fp.FP_INVALID_ARGUMENT                  # no scale cache
     assert call(p8, ws=ws16) == fp.FP_WORKSPACE_TOO_SMALL               # the bf16 size is not enough
+
