@@ -312,9 +312,11 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
             // Paged scales: [num_pages, Hkv], the entry of the block's first page.
             const int page = pages[wJ * BLK / a.kv.page_size];
             const bool ok = (unsigned)page < (unsigned)a.kv.num_pages;
+            // A page id outside the pool reads as zero codes (the DMA's zero
+            // chunk) with scale 1, i.e. as a page of zeros.
             const int64_t e = (int64_t)(ok ? page : 0) * a.Hkv + hk;
-            wsk = ok ? a.k_scale[e] : 0.f;
-            wsv = ok ? a.v_scale[e] : 0.f;
+            wsk = ok ? a.k_scale[e] : 1.f;
+            wsv = ok ? a.v_scale[e] : 1.f;
         } else {
             wsk = a.k_scale[srow + wJ];
             wsv = a.v_scale[srow + wJ];

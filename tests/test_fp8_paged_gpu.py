@@ -111,3 +111,26 @@ def test_fp8_paged_rejects_bf16_params():
         fp.fp_sparse_prefill_varlen_paged_fp8(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
                                               pb.block_table.to(dev()), pb.cu_seqlens)
     assert e.value.status == fp.FP_INVALID_ARGUMENT
+
+
+def test_fp8_out_of_range_page_reads_zero():
+    """A block-table entry outside the pool reads as zeros (codes 0, scale 1)
+    instead of faulting or giving NaN rows: the result equals a cache whose
+    page holds zeros.  With page = block, the bad page is the first page of
+    its block, so its scale lookup is the one that falls outside the pool."""
+    lengths, Hq, Hkv, d, B, page = [320], 4, 1, 64, 64, 64
+    pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=6, verticals=False, page_size=page)
+    bad = pb.block_table.clone()
+    victim = int(bad[0, 2])
+    bad[0, 2] = 10 ** 6
+    zeroed_k, zeroed_v = pb.k_cache.clone(), pb.v_cache.clone()
+    zeroed_k[victim] = 0
+    zeroed_v[victim] = 0
+    p = fp.make_params(Hq, Hkv, d, B, 0.0, mean_correction=True, dtype=FP8)
+    r1, _ = fp.fp_sparse_prefill_varlen_paged_fp8(p, pb.q.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev()),
+                                                  bad.to(dev()), pb.cu_seqlens, return_lse=True)
+    r2, _ = fp.fp_sparse_prefill_varlen_paged_fp8(p, pb.q.to(dev()), zeroed_k.to(dev()), zeroed_v.to(dev()),
+                                                  pb.block_table.to(dev()), pb.cu_seqlens, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(r1.out.float()).all() and torch.isfinite(r1.lse).all()
+    assert torch.equal(r1.out, r2.out) and torch.equal(r1.lse, r2.lse)
