@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libflashprefill.so")
 FP_OK, FP_INVALID_ARGUMENT, FP_UNSUPPORTED, FP_WORKSPACE_TOO_SMALL, FP_DEVICE_ERROR = range(5)
 FP_DTYPE_BF16, FP_DTYPE_FP8_E4M3FN = 0, 1
 FP_MAX_BATCH = 128
+FP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class fp_params(ctypes.Structure):
@@ -54,6 +55,9 @@ EXPORTS = {
                                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                       _I32P, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P, _P, _P]),
+    "fp_sparse_prefill_varlen_paged_noalloc": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
+                                                              ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                              _I32P, ctypes.c_int32, _P, _P, _P, _P, _P]),
     "fp_sparse_prefill_varlen_paged_fp8": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
                                                           ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                           _I32P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
@@ -289,6 +293,20 @@ def fp_sparse_prefill_varlen_paged(params: fp_params, q: torch.Tensor, k_cache: 
         _ptr(block_table), block_table.shape[1], cu, batch, _ptr(kv_idx), _ptr(kv_cnt),
         _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
     return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
+
+
+def fp_sparse_prefill_varlen_paged_noalloc(params: fp_params, q: torch.Tensor, k_cache: torch.Tensor,
+                                           v_cache: torch.Tensor, block_table: torch.Tensor, cu_seqlens,
+                                           out: torch.Tensor, kv_idx: torch.Tensor, kv_cnt: torch.Tensor,
+                                           lse: Optional[torch.Tensor] = None) -> None:
+    """fp_sparse_prefill_varlen_paged with the library's own scratch: the
+    caller passes every output buffer, and the call allocates nothing."""
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    cu = _cu_host(cu_seqlens)
+    _check(lib().fp_sparse_prefill_varlen_paged_noalloc(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
+        _ptr(block_table), block_table.shape[1], cu, len(cu) - 1, _ptr(kv_idx), _ptr(kv_cnt),
+        _ptr(out), _ptr(lse), _stream(q.device)))
 
 
 @dataclass

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -487,6 +488,63 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
     return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
                          cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, workspace, workspace_bytes, out,
                          lse, stream);
+}
+
+// Scratch of the allocation-free paged entry: one copy per GPU, in the
+// library's code object, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it names a stand-in, not device
+// memory): the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[FP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (looked up on the first call
+// with that device current), or an FP_* error.
+int scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FP_DEVICE_ERROR, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FP_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FP_DEVICE_ERROR, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FP_OK;
+}
+}  // namespace
+
+FP_EXPORT int fp_sparse_prefill_varlen_paged_noalloc(const fp_params* params, const void* q, const void* k_cache,
+                                                     const void* v_cache, int32_t page_size, int32_t num_pages,
+                                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                                     const int32_t* cu_seqlens_host, int32_t batch,
+                                                     int32_t* kv_idx, int32_t* kv_cnt, void* out, float* lse,
+                                                     void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    SeqTable t;
+    rc = build_table(*params, cu_seqlens_host, nullptr, batch, 1, t);
+    if (rc) return rc;
+    const size_t need = ws_layout(*params, t).total;
+    if (need > FP_NOALLOC_SCRATCH_BYTES)
+        return fail(FP_WORKSPACE_TOO_SMALL,
+                    "the batch needs %zu bytes of pooled-mean scratch; the allocation-free entry holds %zu "
+                    "(use fp_sparse_prefill_varlen_paged with a workspace)",
+                    need, (size_t)FP_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc) return rc;
+    return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
+                         cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, ws,
+                         (size_t)FP_NOALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
 FP_EXPORT int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const void* q, const void* k_cache,

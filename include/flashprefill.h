@@ -174,6 +174,33 @@ int fp_sparse_prefill_varlen_paged(const fp_params* params, const void* q,
                                    void* out, float* lse, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as fp_sparse_prefill_varlen_paged, with the workspace taken
+ * from a library-owned device array of FP_NOALLOC_SCRATCH_BYTES per GPU
+ * instead of a caller's buffer.  The array lives in the library's code object
+ * on every GPU the library runs on, until the process ends.  The call
+ * allocates nothing, frees nothing and calls no allocating routine; the
+ * caller still passes (and owns) every input and output.
+ *   All arguments: as for fp_sparse_prefill_varlen_paged, without workspace.
+ *   FP_WORKSPACE_TOO_SMALL when the batch needs more pooled-mean scratch than
+ *     FP_NOALLOC_SCRATCH_BYTES (fp_varlen_workspace_bytes gives the need);
+ *     nothing is launched then.
+ * Every call on one GPU shares that GPU's array and overwrites it (it holds
+ * the last call's pooled means; nothing in it needs to start at zero).  Calls
+ * that overlap on one GPU (other streams, other threads) race on it: the
+ * caller orders them, e.g. by issuing them on one stream.
+ */
+#define FP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fp_sparse_prefill_varlen_paged_noalloc(const fp_params* params, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           int32_t page_size, int32_t num_pages,
+                                           const int32_t* block_table, int32_t max_pages_per_seq,
+                                           const int32_t* cu_seqlens_host, int32_t batch,
+                                           int32_t* kv_idx, int32_t* kv_cnt,
+                                           void* out, float* lse, void* stream);
+
+/*
  * fp8 inference over a paged batch (FlashPrefill V2 abstract: FP8 inference,
  * paged KV cache and continuous batching): the requests of
  * fp_sparse_prefill_varlen_paged, with params->dtype = FP_DTYPE_FP8_E4M3FN.

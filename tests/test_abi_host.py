@@ -266,3 +266,17 @@ def test_fp8_paged_validation_and_workspace():
     assert call(p8, ks=None) == fp.FP_INVALID_ARGUMENT                  # no scale cache
     assert call(p8, ws=ws16) == fp.FP_WORKSPACE_TOO_SMALL               # the bf16 size is not enough
 
+
+def test_noalloc_entry_rejects_batches_beyond_its_scratch():
+    """The allocation-free entry checks the pooled-mean scratch it needs
+    against its fixed array on the host, before any device work."""
+    l = fp.lib()
+    p = _p()
+    cu = (ctypes.c_int32 * 3)(0, 1 << 19, 1 << 20)     # 2 x 512K tokens: about 200 MB of means
+    need = l.fp_varlen_workspace_bytes(ctypes.byref(p), cu, 2)
+    assert need > fp.FP_NOALLOC_SCRATCH_BYTES
+    d = ctypes.c_void_p(256)
+    rc = l.fp_sparse_prefill_varlen_paged_noalloc(ctypes.byref(p), d, d, d, 64, 100000, d, 8192, cu, 2,
+                                                  d, d, d, None, None)
+    assert rc == fp.FP_WORKSPACE_TOO_SMALL
+    assert b"scratch" in l.fp_last_error()
