@@ -15,6 +15,13 @@ events on the launch stream.  latency_spread gives the median and minimum of
 the per-step selection, attention and step times; hbm_anchor the streaming
 bandwidth of torch's own sum and copy kernels on the same GPU.  The CPU
 baseline is the fp64 oracle on a bounded sample of the same workload.
+
+Beside the headline: the fp8 layer, the paged batch (bf16 and fp8) and its
+chunked variant; the tiny (1K) and 32K workloads with their own latency,
+effective TFLOP/s and alpha = 0 dense reference (`configs`); and, outside every
+timed region, a parity summary of all five workloads against the oracle
+(`parity`: mask mismatches inside and outside the threshold band, band size,
+max-abs output error).
 """
 import argparse
 import json
@@ -67,6 +74,10 @@ def parse():
     ap.add_argument("--layouts", action="store_true",
                     help="with --quick: still time the fp8 layer and the paged batch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--configs", action="store_true",
+                    help="with --quick: still time the tiny (1K) and 32K workloads")
+    ap.add_argument("--parity", action="store_true", help="with --quick: still run the parity summary")
+    ap.add_argument("--no-parity", action="store_true", help="skip the parity summary")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -257,10 +268,19 @@ def main():
     if not args.quick or args.layouts:
         extra.update(other_layouts(fp, synth, q, k, v, head, stream, dev, corr))
 
+    if not args.quick or args.configs:
+        extra["configs"] = [small_config(fp, synth, name, corr, args.steps, args.warmup, stream, dev)
+                            for name in ("tiny_s1k_gqa4_d64", "llama8b_s32k")]
+
     cpu = None
+    oracle128 = []
     if not args.quick:
-        cpu = cpu_baseline(q, k, v, B, args.alpha, corr, head, args.cpu_seconds)
+        cpu = cpu_baseline(q, k, v, B, args.alpha, corr, head, args.cpu_seconds, oracle128)
         log(f"bench: cpu {cpu}")
+    if (not args.quick and not args.no_parity) or args.parity:
+        del head["sel"]
+        torch.cuda.empty_cache()
+        extra["parity"] = parity_summary(fp, synth, dev, corr, q, k, v, oracle128[0] if oracle128 else None)
 
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -463,10 +483,189 @@ def list_work(kv_idx, kv_cnt, kv_lens, starts, Hq, B, dev):
     return kept, skipped
 
 
-def cpu_baseline(q, k, v, B, alpha, corr, head, seconds):
+def small_config(fp, synth, name, corr, steps, warmup, stream, dev):
+    """One single-sequence workload at its threshold ratio: selection,
+    attention and step latency, effective TFLOP/s (F_kept + F_corr over the
+    attention and step times), density; our alpha = 0 kernel (every causal
+    block) as the dense reference on the same GPU."""
+    import torch
+    w = synth.WORKLOADS[name]
+    S, Hq, Hkv, d, B = w.seqlens[0], w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    q, k, v = synth.make_sequence(S, Hq, Hkv, d, w.seed, w.verticals)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    nB = (S + B - 1) // B
+    res = {"workload": name, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "block": B}
+    for alpha in (w.alphas[0], 0.0):
+        p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr)
+        sel = fp.alloc_selection(p, S, dev)
+        fs = lambda: fp.fp_select_blocks(p, qd, kd, vd, sel=sel)
+        fa = lambda: fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel, out=out)
+        for _ in range(warmup):
+            fs()
+            fa()
+        step_ms, sel_ms, attn_ms, spread = time_steps(fs, fa, steps if alpha > 0 else max(3, steps // 4), stream)
+        f_kept, f_corr, kept = work_counts(fp, sel, S, Hq, d, B, corr)
+        f = f_kept + f_corr
+        if alpha > 0:
+            res.update({"alpha": alpha, "select_ms": round(sel_ms, 4), "attn_ms": round(attn_ms, 4),
+                        "step_ms": round(step_ms, 4), "latency_spread": spread,
+                        "density": round(kept / (Hq * nB * (nB + 1) // 2), 5),
+                        "attn_tflops": round(f / (attn_ms * 1e-3) / 1e12, 2),
+                        "step_tflops": round(f / (step_ms * 1e-3) / 1e12, 2),
+                        "attn_frac_bf16_peak": round(f / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "flops": {"kept": f_kept, "corr": f_corr}})
+        else:
+            res["dense_ref"] = {"ours_alpha0_attn_ms": round(attn_ms, 4),
+                                "ours_alpha0_tflops": round(f / (attn_ms * 1e-3) / 1e12, 2),
+                                "speedup_step_vs_alpha0_attn": round(attn_ms / res["step_ms"], 2)}
+    log(f"bench: {name} {res}")
+    return res
+
+
+def _mask_stats(mask, ref_keep, ref_band):
+    diff = mask != ref_keep
+    return {"kept": int(mask.sum()), "band": int(ref_band.sum()),
+            "mismatch_in_band": int((diff & ref_band).sum()),
+            "mismatch_outside_band": int((diff & ~ref_band).sum())}
+
+
+def _sampled_error(O, q, k, v, sel, keep, corr, out, pairs, B):
+    """max |o_gpu - o_oracle| over the rows of the sampled (head, query block)
+    pairs, the oracle run under the GPU's mask."""
+    import numpy as np
+    o_ref, _ = O.sparse_attention(q, k, v, sel, corr, pairs=pairs, keep=keep)
+    err = 0.0
+    S = q.shape[0]
+    for h, I in pairs:
+        r0, r1 = I * B, min(S, (I + 1) * B)
+        err = max(err, float(np.abs(out[r0:r1, h] - o_ref[r0:r1, h]).max()))
+    return err
+
+
+def parity_summary(fp, synth, dev, corr, q128, k128, v128, oracle128=None):
+    """Parity of every configuration against the CPU oracle, outside the timed
+    regions: mask mismatches inside and outside the 1e-3 band around each
+    threshold (outside must be 0), band size, and the max-abs output error
+    against the oracle under the GPU's mask (whole output for the tiny
+    workload, sampled (head, query block) pairs for the others; fp8 against
+    the oracle on the oracle's own dequantized codes)."""
+    import numpy as np
+    import torch
+    import oracle as O
+    rng = np.random.default_rng(7)
+    res = {}
+
+    def single(name, alphas, q, k, v, full_error, npairs, sel_ref=None):
+        S, Hq, d = q.shape
+        Hkv = k.shape[1]
+        B = synth.WORKLOADS[name].block_size
+        nB = (S + B - 1) // B
+        qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        ref = sel_ref if sel_ref is not None else O.select_blocks(qn, kn, vn, B, alphas[0])
+        out_cfg = {}
+        for alpha in alphas:
+            p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=corr)
+            sel = fp.fp_select_blocks(p, qd, kd, vd)
+            mask = fp.lists_to_mask(sel.kv_idx, sel.kv_cnt, Hq, nB)
+            keep, band = O.threshold(ref.score, alpha)
+            st = _mask_stats(mask, keep, band)
+            if alpha == alphas[0]:
+                o = fp.fp_sparse_prefill_fwd(p, qd, kd, vd, sel).float().cpu().numpy()
+                if full_error:
+                    o_ref, _ = O.sparse_attention(qn, kn, vn, ref, corr, keep=mask)
+                    st["max_abs_err"] = float(np.abs(o - o_ref).max())
+                    st["err_rows"] = "all"
+                else:
+                    pairs = [divmod(int(x), nB) for x in rng.choice(Hq * nB, npairs, replace=False)]
+                    st["max_abs_err"] = _sampled_error(O, qn, kn, vn, ref, mask, corr, o, pairs, B)
+                    st["err_rows"] = f"{npairs} random (head, query block) pairs"
+            out_cfg[str(alpha)] = st
+        return out_cfg, ref
+
+    t0 = time.perf_counter()
+    w = synth.WORKLOADS["tiny_s1k_gqa4_d64"]
+    q, k, v = synth.make_sequence(w.seqlens[0], w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed, w.verticals)
+    res[w.name], _ = single(w.name, (0.1, 0.3, 0.5, 0.9), q, k, v, True, 0)
+    w = synth.WORKLOADS["llama8b_s32k"]
+    q, k, v = synth.make_sequence(w.seqlens[0], w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed, w.verticals)
+    res[w.name], _ = single(w.name, (0.1,), q, k, v, False, 16)
+    del q, k, v
+    res["llama8b_s128k"], ref128 = single("llama8b_s128k", (0.1, 0.05, 0.2), q128, k128, v128, False, 16,
+                                          oracle128)
+    # fp8: lists from the fused fp8 preparation (selection on the bf16 data),
+    # output against the oracle on the oracle's own codes of KV head 0's group
+    Hq, Hkv = q128.shape[1], k128.shape[1]
+    g = Hq // Hkv
+    S, d = q128.shape[0], q128.shape[2]
+    B = 128
+    nB = S // B
+    p8 = fp.make_params(Hq, Hkv, d, B, 0.1, mean_correction=corr, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    sel8, f8 = fp.fp_select_blocks_fp8(p8, q128.to(dev), k128.to(dev), v128.to(dev))
+    o8 = fp.fp_sparse_prefill_fwd(p8, f8.q8, f8.k8, f8.v8, sel8, q_scale=f8.q_scale, k_scale=f8.k_scale,
+                                  v_scale=f8.v_scale).float().cpu().numpy()
+    mask8 = fp.lists_to_mask(sel8.kv_idx, sel8.kv_cnt, Hq, nB)
+    keep, band = O.threshold(ref128.score, 0.1)
+    st = _mask_stats(mask8, keep, band)
+    del sel8, f8
+    deq = []
+    for x in (q128[:, :g], k128[:, :1], v128[:, :1]):
+        c, sc = O.quantize_fp8_blockwise(x.float().numpy(), B)
+        deq.append(O.dequantize_blockwise(synth.fp8_codes_to_float(torch.from_numpy(c)).numpy(), sc, B))
+    sub = O.Selection(None, ref128.k_bar[:1], ref128.v_bar[:1], None, None, None, None, B)
+    pairs = [(int(h), int(I)) for h, I in zip(rng.integers(0, g, 12), rng.integers(0, nB, 12))]
+    st["max_abs_err"] = _sampled_error(O, deq[0], deq[1], deq[2], sub, mask8[:g], corr, o8[:, :g], pairs, B)
+    st["err_rows"] = "12 random (head, query block) pairs of KV head 0's query heads, oracle on its own e4m3 codes"
+    res["llama8b_s128k_fp8"] = {"0.1": st}
+    del deq, o8
+    # paged batch: each request against the oracle run on it alone
+    w = synth.WORKLOADS["paged_batch8"]
+    pb = synth.workload_inputs(w, keep_requests=True)
+    p = fp.make_params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, 0.1, mean_correction=corr)
+    r = fp.fp_sparse_prefill_varlen_paged(p, pb.q.to(dev), pb.k_cache.to(dev), pb.v_cache.to(dev),
+                                          pb.block_table.to(dev), pb.cu_seqlens)
+    out = r.out.float().cpu().numpy()
+    tot = {"kept": 0, "band": 0, "mismatch_in_band": 0, "mismatch_outside_band": 0, "max_abs_err": 0.0}
+    io = co = 0
+    Bp, Hqp = w.block_size, w.num_q_heads
+    for b, (qb, kb, vb) in enumerate(pb.requests):
+        L = qb.shape[0]
+        nb = (L + Bp - 1) // Bp
+        mask = fp.lists_to_mask(r.kv_idx, r.kv_cnt, Hqp, nb, offset=io, cnt_offset=co)
+        qn, kn, vn = qb.float().numpy(), kb.float().numpy(), vb.float().numpy()
+        ref = O.select_blocks(qn, kn, vn, Bp, 0.1)
+        st_b = _mask_stats(mask, ref.keep, ref.band)
+        for key in ("kept", "band", "mismatch_in_band", "mismatch_outside_band"):
+            tot[key] += st_b[key]
+        t0b = int(pb.cu_seqlens[b])
+        pairs = [(int(h), int(I)) for h, I in zip(rng.integers(0, Hqp, 2), rng.integers(0, nb, 2))]
+        tot["max_abs_err"] = max(tot["max_abs_err"],
+                                 _sampled_error(O, qn, kn, vn, ref, mask, corr, out[t0b:t0b + L], pairs, Bp))
+        io += Hqp * nb * (nb + 1) // 2
+        co += Hqp * nb
+    tot["err_rows"] = "2 random (head, query block) pairs per request"
+    res["paged_batch8"] = {"0.1": tot}
+    res["seconds"] = round(time.perf_counter() - t0, 1)
+    res["tolerance"] = {"bf16": 2e-2, "fp8": 6e-2}
+    log(f"bench: parity {res}")
+    return res
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return None
+
+
+def cpu_baseline(q, k, v, B, alpha, corr, head, seconds, oracle_sel=None):
     """The fp64 oracle on the host: full selection, then attention for a
-    sample of (head, query block) pairs under the GPU's mask until about
-    `seconds` have passed; the rate is scaled to the whole workload."""
+    random sample of (head, query block) pairs under the GPU's mask, in
+    batched calls that fill about `seconds`; the rate is scaled by FLOP to the
+    whole workload.  cores: the CPUs this process may run on; blas_threads:
+    the BLAS pool the oracle's products use."""
     import numpy as np
     import oracle as O
     import block_sparse_long_pooling_amd as fp
@@ -477,36 +676,47 @@ def cpu_baseline(q, k, v, B, alpha, corr, head, seconds):
     sel = O.select_blocks(qn, kn, vn, B, alpha)
     t_sel = time.perf_counter() - t0
     mask = fp.lists_to_mask(head["sel"].kv_idx, head["sel"].kv_cnt, Hq, nB)
-    rng = np.random.default_rng(0)
-    order = rng.permutation(Hq * nB)
-    t1 = time.perf_counter()
-    f_s = 0.0
-    done = 0
+    order = [divmod(int(x), nB) for x in np.random.default_rng(0).permutation(Hq * nB)]
     n_full = np.full(nB, B)
     n_full[-1] = S - (nB - 1) * B
-    for idx in order:
-        h, I = divmod(int(idx), nB)
-        O.sparse_attention(qn, kn, vn, sel, corr, pairs=[(h, I)], keep=mask)
-        kept = mask[h, I, :I + 1]
-        f_s += 4.0 * d * n_full[I] * float(n_full[:I + 1][kept].sum())
-        if corr:
-            f_s += 4.0 * d * n_full[I] * float((~kept[:I]).sum())
-        done += 1
-        if time.perf_counter() - t1 > seconds:
+
+    def work(pairs):
+        f = 0.0
+        for h, I in pairs:
+            kept = mask[h, I, :I + 1]
+            f += 4.0 * d * n_full[I] * float(n_full[:I + 1][kept].sum())
+            if corr:
+                f += 4.0 * d * n_full[I] * float((~kept[:I]).sum())
+        return f
+
+    # Batched calls of growing size (each call fills an [S, Hq, d] output, so
+    # one pair per call would mostly time that fill), the last one sized by
+    # the rate measured so far to end near the time budget.
+    done, t_att, f_s, n = 0, 0.0, 0.0, 8
+    while done < len(order):
+        batch = order[done:done + n]
+        t1 = time.perf_counter()
+        O.sparse_attention(qn, kn, vn, sel, corr, pairs=batch, keep=mask)
+        t_att += time.perf_counter() - t1
+        f_s += work(batch)
+        done += len(batch)
+        left = seconds - t_att
+        if left <= 0:
             break
-    t_att = time.perf_counter() - t1
+        per_pair = t_att / done
+        n = int(min(4 * n, max(8, left / per_pair)))
     f_total = head["f_kept"] + head["f_corr"]
     est_total_s = t_sel + t_att * f_total / max(f_s, 1.0)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
-    return {"value": round(f_total / est_total_s / 1e12, 6), "unit": "TFLOP/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"full fp64 selection ({t_sel:.1f}s) + attention for {done} of {Hq * nB} random "
-                      f"(head, query block) pairs ({t_att:.1f}s), scaled by FLOP to the whole workload",
-            "est_seconds_full": round(est_total_s, 1)}
+    cores = len(os.sched_getaffinity(0))
+    res = {"value": round(float(f_total / est_total_s / 1e12), 6), "unit": "TFLOP/s",
+           "cores": cores, "blas_threads": _blas_threads(), "numpy": np.__version__, "kind": "oracle",
+           "sample": f"full fp64 selection ({t_sel:.1f}s) + attention for {done} of {Hq * nB} random "
+                     f"(head, query block) pairs in batched calls ({t_att:.1f}s), scaled by FLOP to the "
+                     f"whole workload",
+           "est_seconds_full": round(float(est_total_s), 1)}
+    if oracle_sel is not None:
+        oracle_sel.append(sel)
+    return res
 
 
 if __name__ == "__main__":
