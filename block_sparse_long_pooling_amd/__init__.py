@@ -18,7 +18,9 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libflashprefill.so")
+# FLASHPREFILL_LIB selects another build of the same library (the host-side
+# address-sanitizer build the CPU tests use); by default, the in-tree one.
+LIB_PATH = os.environ.get("FLASHPREFILL_LIB") or os.path.join(_HERE, "libflashprefill.so")
 
 FP_OK, FP_INVALID_ARGUMENT, FP_UNSUPPORTED, FP_WORKSPACE_TOO_SMALL, FP_DEVICE_ERROR = range(5)
 FP_DTYPE_BF16, FP_DTYPE_FP8_E4M3FN = 0, 1

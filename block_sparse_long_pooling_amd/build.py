@@ -56,5 +56,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(PKG, "_build", "asan")
+
+
+def asan_runtime() -> str:
+    """The compiler's shared address-sanitizer runtime (to preload), or ''."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    for c in (clang, "/opt/rocm/llvm/bin/clang"):
+        if os.path.exists(c):
+            r = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                               text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return ""
+
+
+def build_host_asan() -> str:
+    """A copy of the library whose host code (the C ABI: validation, sizes,
+    request tables) is built with the address sanitizer; the kernels are the
+    regular objects.  Device code is never instrumented.  Load it with the
+    runtime from asan_runtime() preloaded and FLASHPREFILL_LIB pointing at it."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ, src.replace(".hip", ".o")) for src in SOURCES if src != "fp_abi.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    abi = os.path.join(ASAN_DIR, "fp_abi.o")
+    flags = [f for f in CFLAGS if f != "-O3"]
+    _run([HIPCC, "-O1", "-g", *flags, "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+          "-c", os.path.join(CSRC, "fp_abi.hip"), "-o", abi])
+    lib = os.path.join(ASAN_DIR, "libflashprefill.so")
+    clangxx = "/opt/rocm/llvm/bin/clang++"
+    _run([clangxx, "-shared", "-fsanitize=address", "-shared-libasan", "-o", lib, abi, *objs,
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
