@@ -108,9 +108,11 @@ def test_fp8_128k_full_size():
     assert outside == 0
     deq = [O.dequantize_blockwise(synth.fp8_codes_to_float(inp[n + "8"]).numpy(), inp[n + "_scale"].numpy(), B)
            for n in ("q", "k", "v")]
+    # every query head (each XCD's heads) and query blocks across the whole
+    # sequence: 64 pairs, plus the first and last blocks
     r = np.random.default_rng(4)
     pairs = sorted({(0, 0), (Hq - 1, nB - 1), (5, nB // 2)} |
-                   {(int(r.integers(Hq)), int(r.integers(nB))) for _ in range(40)})
+                   {(k % Hq, int(r.integers(k * nB // 64, (k + 1) * nB // 64))) for k in range(64)})
     o_ref, lse_ref = O.sparse_attention(deq[0], deq[1], deq[2], ref, True, pairs=pairs, keep=mask)
     o = out.float().cpu().numpy()
     worst = max(float(np.abs(o[I * B:(I + 1) * B, h] - o_ref[I * B:(I + 1) * B, h]).max()) for h, I in pairs)

@@ -1,8 +1,10 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times: every block list against the oracle's selection (bit-exact
 outside the threshold band), and outputs of a sample of (head, query block)
-pairs -- always including the first and last query blocks -- against the
-oracle evaluated under the GPU's mask."""
+pairs -- always including the first and last query blocks, at 32K and 128K
+one pair in every band of the persistent attention grid and every XCD slot,
+and 16 pairs per request of the paged batch -- against the oracle evaluated
+under the GPU's mask."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +24,27 @@ def _sample_pairs(Hq, nB, n, seed):
     while len(pairs) < n:
         pairs.add((int(r.integers(Hq)), int(r.integers(nB))))
     return sorted(pairs)
+
+
+def _band_pairs(Hq, nB, grid, HP=2):
+    """One (head, query block) pair per band of `grid` consecutive work items
+    of the persistent attention kernel (items: query blocks longest first,
+    times the Hq / HP head pairs, heads of one KV head on one XCD), taking
+    XCD slot k mod 8 in band k, so every band and every XCD slot is sampled."""
+    npairs = Hq // HP
+    nitems = nB * npairs
+
+    def xcd_head(slot):
+        return (slot % 8) * (npairs // 8) + slot // 8 if npairs % 8 == 0 else slot
+
+    pairs = set()
+    for k in range((nitems + grid - 1) // grid):
+        idx = k * grid + k % 8 + 8 * ((5 * k) % max(1, grid // 8))
+        if idx >= nitems:
+            idx = min(nitems - 1, k * grid + k % 8)
+        rank, slot = divmod(idx, npairs)
+        pairs.add((HP * xcd_head(slot) + k % HP, nB - 1 - rank))
+    return pairs
 
 
 class _Seq:
@@ -65,7 +88,10 @@ def _check_full(seq, alpha, n_pairs, seed):
     assert outside == 0
     # pooled means against the oracle's
     np.testing.assert_allclose(sel.pooled_k.cpu().numpy(), ref.k_bar, rtol=0, atol=1e-5)
-    pairs = _sample_pairs(Hq, nB, n_pairs, seed)
+    grid = fp.fp_attention_workgroups(p, [0, S])
+    bands = _band_pairs(Hq, nB, grid)
+    pairs = sorted(set(_sample_pairs(Hq, nB, n_pairs, seed)) | bands)
+    print(f"  grid {grid}: {len(bands)} pairs over the persistent bands", flush=True)
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, ref, True, pairs=pairs, keep=mask)
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
@@ -109,7 +135,7 @@ def test_paged_batch8_full_size():
         ref = O.select_blocks(qb, kb, vb, B, w.alphas[0])
         outside, inside, band = compare_mask(mask, ref)
         assert outside == 0, (b, outside)
-        pairs = _sample_pairs(Hq, nb, 8, seed=b)
+        pairs = _sample_pairs(Hq, nb, 16, seed=b)
         o_ref, lse_ref = O.sparse_attention(qb, kb, vb, ref, True, pairs=pairs, keep=mask)
         t0 = int(pb.cu_seqlens[b])
         for h, I in pairs:
@@ -161,7 +187,7 @@ def test_paged_batch8_fp8_full_size():
         ref = O.select_blocks(qb, kb, vb, B, w.alphas[0])
         outside, inside, band = compare_mask(mask, ref)
         assert outside == 0, (b, outside)
-        pairs = _sample_pairs(Hq, nb, 6, seed=50 + b)
+        pairs = _sample_pairs(Hq, nb, 16, seed=50 + b)
         o_ref, _ = O.sparse_attention(deq[0], deq[1], deq[2], ref, True, pairs=pairs, keep=mask)
         t0 = int(pb.cu_seqlens[b])
         worst = max(float(np.abs(out[t0 + I * B:t0 + min(L, (I + 1) * B), h] - o_ref[I * B:min(L, (I + 1) * B), h]).max())
