@@ -8,7 +8,10 @@
 //
 // A workgroup of 8 waves owns up to 128 score rows of one KV head: 4 row
 // waves, each 32 rows = TI consecutive query blocks x the g query heads, and
-// 2 column groups.  The k_bar rows stream through LDS in column tiles of 32
+// 2 column groups.  A row wave's cost grows with its last query block, so the
+// row waves are dealt to workgroups in a snake (the longest with the
+// shortest, two middle ones together) and every workgroup gets about the
+// same number of (row, column tile) products.  The k_bar rows stream through LDS in column tiles of 32
 // blocks, two tiles per step (one per column group), split once per
 // workgroup into bf16 hi + lo parts; every tile then serves all the rows of
 // the workgroup.  The rows of the step after next are loaded into registers
@@ -119,7 +122,7 @@ __device__ __forceinline__ f32x16 tile_scores(const bf16x8* qh, const bf16x8* ql
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Workgroup = up to 128 score rows (4 row waves x TI query blocks x g heads)
-// of one KV head.  Wave wv: row wave rw = wv % 4, column group cg = wv / 4;
+// of one KV head.  Wave wv: row wave rw = wv / 2, column group cg = wv % 2;
 // each step stages two column tiles (phase 1: tiles 2p and 2p + 1 at step
 // p), and column group cg scores the (cg)-th of them for its row wave's
 // rows.  Phase 1: row maxima, combined over the
@@ -137,7 +140,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
 
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63;
-    const int rw = wv % kRowWaves, cg = wv / kRowWaves;
+    // Column groups of a row wave on different SIMDs (waves are dealt to the
+    // 4 SIMDs in turn): row waves 0 and 2 on SIMDs 0-1, 1 and 3 on SIMDs 2-3.
+    const int rw = wv >> 1, cg = wv & 1;
     const int rank = blockIdx.x / a.Hkv;
     const int hk = blockIdx.x % a.Hkv;
     int b, local;
@@ -146,17 +151,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     const int first = first_block(t, b);             // query blocks are first .. nb-1
     const int TIW = kRowWaves * a.TI;                // query blocks per workgroup
     const int ntiles = (nb - first + TIW - 1) / TIW;
-    const int I0 = first + (ntiles - 1 - local) * TIW;
+    // Row waves are dealt to workgroups so that every workgroup gets about
+    // the same number of column tiles, and each SIMD pair too: with the
+    // request's nrw row waves counted from the longest (i = 0), workgroup
+    // `local` of K takes i = local (row wave 0), 2K-1-local (1), 4K-1-local
+    // (2, the shortest, beside the longest) and 2K+local (3).
+    const int nrw = (nb - first + a.TI - 1) / a.TI;
+    auto rw_first = [&](int r) {
+        const int K = ntiles;
+        const int i = r == 0 ? local : r == 1 ? 2 * K - 1 - local : r == 2 ? 4 * K - 1 - local : 2 * K + local;
+        return i < nrw ? first + (nrw - 1 - i) * a.TI : nb;     // nb: no rows
+    };
     const int gblk0 = t.blk_off[b];
     const int rows = a.TI * a.g;                     // used row slots per row wave
     const int rho = lane & 31;
     const int half = lane >> 5;
-    const int Iw0 = I0 + rw * a.TI;                  // this row wave's first query block
+    const int Iw0 = rw_first(rw);                    // this row wave's first query block
     const int Iw_end = min(nb, Iw0 + a.TI);          // and one past its last
     const int ntile_w = Iw_end > Iw0 ? (Iw_end - 1) / 32 + 1 : 0;   // column tiles it needs
     const bool rows_full = rows == 32 && Iw0 + a.TI <= nb;
 
-    const int ncol = min(nb, I0 + TIW);
+    const int ncol = min(nb, rw_first(0) + a.TI);    // row wave 0 holds the workgroup's last rows
     const int ntile = (ncol + 31) >> 5;
     const int64_t krow0 = (int64_t)hk * t.total_blocks + gblk0;
     const Stager<D> sg(tid);
@@ -313,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
         const int slot = wv * (kRowSlots / kWaves) + lane;
         const int rw3 = slot / 32, r3 = slot % 32;
         const int ii = r3 / a.g, hi = r3 % a.g;
-        const int I = I0 + rw3 * a.TI + ii;
+        const int I = rw_first(rw3) + ii;
         if (r3 < rows && I < nb) {
             const int h = hk * a.g + hi;
             const int nt = I / 32 + 1;                       // tiles holding J <= I
