@@ -8,7 +8,9 @@
 // maximum 1 is exact) goes to the PV product as two e4m3 terms,
 // P_hi = e4m3(p) and P_lo = e4m3(p - P_hi), both on fp8 MFMA into the same
 // accumulator: one e4m3 term alone carries up to 2^-4 relative error per
-// weight, the pair about 2^-8.  Each tile's V scale is folded into the
+// weight, the pair about 2^-8.  The row sum l is taken from the same two
+// rounded terms (a product of P against a block of ones), so numerator and
+// denominator weigh every key alike.  Each tile's V scale is folded into the
 // per-tile rescale of the O accumulator: O holds sum P (V8) in units of the
 // current tile's scale.
 //
@@ -73,7 +75,7 @@ __device__ __forceinline__ void qk8(const uint4* kt, const i32x8* qf, int col, i
 // 2m + p reads key row m of the set at d bytes 32 ds + 16 (g&1) + 8 p.
 template <int D, int ST>
 __device__ __forceinline__ void pv8(const char* vt, const uint32_t (*ph)[4], const uint32_t (*pl)[4], int lane,
-                                    f32x16* o) {
+                                    f32x16* o, f32x16& lsum) {
     const int gl = lane & 15, g = lane >> 4;
     const int h = g >> 1, m = gl >> 1, p = gl & 1;
     const int krow = 64 * ST + 4 * h + (m & 3) + 8 * (m >> 2);
@@ -98,6 +100,13 @@ __device__ __forceinline__ void pv8(const char* vt, const uint32_t (*ph)[4], con
         o[ds] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bl, o[ds], 0, 0, 0, kNeutralScale, 0,
                                                                 kNeutralScale);
     }
+    // Row sums of the two P terms as the products apply them: a V^T block of
+    // e4m3 ones (0x38) gives, in every row, sum over the step's keys of
+    // P_hi + P_lo for each query.
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bh, lsum, 0, 0, 0, kNeutralScale, 0, kNeutralScale);
+    lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bl, lsum, 0, 0, 0, kNeutralScale, 0, kNeutralScale);
 }
 
 template <int NSUB, int NDS>
@@ -136,7 +145,6 @@ __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, fl
             int r = __builtin_amdgcn_cvt_pk_fp8_f32(e0 - d0.x, e1 - d0.y, 0, false);
             r = __builtin_amdgcn_cvt_pk_fp8_f32(e2 - d1.x, e3 - d1.y, r, true);
             pl[sub][i] = (uint32_t)r;
-            l += (e0 + e1) + (e2 + e3);
         }
     }
 }
@@ -357,8 +365,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         }
         softmax8_update<T::NSUB, T::NDS>(s, cq * sk, sv_prev / sv, m, l, o, ph, pl);
         sv_prev = sv;
-        pv8<D, 0>(bcur + VOFF, ph, pl, lane, o);
-        if (BLK == 128) pv8<D, (BLK == 128 ? 1 : 0)>(bcur + VOFF, ph + 2, pl + 2, lane, o);
+        f32x16 lsum = {};
+        pv8<D, 0>(bcur + VOFF, ph, pl, lane, o, lsum);
+        if (BLK == 128) pv8<D, (BLK == 128 ? 1 : 0)>(bcur + VOFF, ph + 2, pl + 2, lane, o, lsum);
+        // Every lane of a query pair got the whole row sum; the lower half
+        // keeps it (l is summed over the pair at the end).
+        l += half ? 0.f : lsum[0];
         J = Jn;
         sk = skn;
         sv = svn;
