@@ -11,14 +11,22 @@
 // 2 column groups.  A row wave's cost grows with its last query block, so the
 // row waves are dealt to workgroups in a snake (the longest with the
 // shortest, two middle ones together) and every workgroup gets about the
-// same number of (row, column tile) products.  The k_bar rows stream through LDS in column tiles of 32
-// blocks, two tiles per step (one per column group), split once per
-// workgroup into bf16 hi + lo parts; every tile then serves all the rows of
-// the workgroup.  The rows of the step after next are loaded into registers
-// while the current step computes.  The (L/B)^2 score matrix is never stored: phase 1
-// takes each row's max, phase 2 recomputes the same scores (same
-// instruction sequence, bit-identical) into a keep bitmap in LDS, phase 3
-// compacts it in ascending J.  The dot products run on bf16 MFMA with each
+// same number of (row, column tile) products.  The k_bar rows stream
+// through LDS in column tiles of 32 blocks, two tiles per step (one per
+// column group), split once per workgroup into bf16 hi + lo parts; every
+// tile then serves all the rows of the workgroup.  The rows of the step after
+// next are loaded into registers while the current step computes.
+//
+// The (L/B)^2 score matrix is never stored.  Phase 1 walks the column tiles
+// from the last to the first, so a row wave meets its diagonal tile first,
+// keeps each row's running max m (shared by the two column groups after
+// every step) and writes each (tile, row)'s keep bits s - m >= ln(alpha) to
+// a bitmap in LDS.  A bit set against a running max below the final one may
+// be wrong; a bit clear stays clear, since the max only grows.  Phase 2
+// recomputes the same scores (same instruction sequence, bit-identical) only
+// for the tiles holding such words; when the row max lies in the diagonal
+// tile, as it does when nearby blocks score highest, there are none.  Phase 3
+// compacts the bitmap in ascending J.  The dot products run on bf16 MFMA with each
 // fp32 operand split into hi + lo bf16 parts (hi*hi + hi*lo + lo*hi), which
 // is within ~2^-17 of the fp32 product sum -- far below the 1e-3 band in
 // which the threshold decision is allowed to differ from an exact one.
@@ -123,23 +131,24 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Workgroup = up to 128 score rows (4 row waves x TI query blocks x g heads)
 // of one KV head.  Wave wv: row wave rw = wv / 2, column group cg = wv % 2;
-// each step stages two column tiles (phase 1: tiles 2p and 2p + 1 at step
-// p), and column group cg scores the (cg)-th of them for its row wave's
-// rows.  Phase 1: row maxima, combined over the
-// column groups in LDS.  Phase 2: the same scores again, thresholded; each
-// tile's keep bits go to an LDS bitmap [tile][row slot]; tiles whose phase-1
-// maximum lies below every row's threshold are not scored again.  Phase 3:
-// one lane per row slot writes the row's list in ascending J.
+// each step stages two column tiles, and column group cg scores the (cg)-th
+// of them for its row wave's rows.  Phase 1 (tiles in descending order):
+// running row maxima, exchanged between the column groups every step, and
+// each (tile, row)'s keep bits against the running max, in an LDS bitmap
+// [tile][row slot].  Phase 2: the tiles with a word formed before its row's
+// max last grew are scored again against the final max.  Phase 3: one lane
+// per row slot writes the row's list in ascending J.
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     __shared__ TileStage<D> stage[2][kColGroups];
     __shared__ uint32_t bits[kMaxColTiles][kRowSlots];
-    __shared__ float pmax[kColGroups][kRowSlots];
+    __shared__ float xch[kColGroups][kRowSlots];      // phase 1: the step's tile maxima
+    __shared__ int32_t wstale[kWaves];               // phase 1: the wave holds a stale row
     __shared__ uint32_t need[kMaxColTiles / 32];     // phase 2: tiles some row may keep from
     __shared__ int32_t todo[kMaxColTiles];           // ... in ascending order
 
     const int tid = threadIdx.x;
-    const int wv = tid >> 6, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     // Column groups of a row wave on different SIMDs (waves are dealt to the
     // 4 SIMDs in turn): row waves 0 and 2 on SIMDs 0-1, 1 and 3 on SIMDs 2-3.
     const int rw = wv >> 1, cg = wv & 1;
@@ -177,46 +186,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     const Stager<D> sg(tid);
     if (tid < kMaxColTiles / 32) need[tid] = 0u;
 
-    // This lane's query row rho = (query block Iw0 + rho / g, head hk*g + rho % g);
-    // rows without a query block read the first one and are zeroed.  The
-    // row is scaled by sigma before it is split.  With group-pooled lists
-    // every row of a query block holds the sum of its g heads' rows, and the
-    // scale takes the 1/g of their mean.
+    // Phase 1 stages the column tiles from the last to the first: entry i of
+    // the order is tile ntile - 1 - i; past the end, tile ntile, which is
+    // staged but never scored.
+    auto tile1 = [&](int i) { return i < ntile ? ntile - 1 - i : ntile; };
+    // Two register buffers: the rows of step p + 2 load while step p scores.
+    float4 x0[Stager<D>::F / 4], x1[Stager<D>::F / 4];
+
+    // Query rows.  Row slot r (row wave r / 32, row rho = r % 32) is query
+    // block rw_first(r / 32) + rho / g of head hk*g + rho % g; slots without a
+    // query block read the first block and are zeroed by the scale below.
+    // Both column groups of a row wave need the same rows, so the
+    // workgroup's rows are read from memory once, into LDS (the bitmap's
+    // space, unused until phase 1; 16-byte chunks swizzled per row), and
+    // every lane takes its fragment from there: d = 16 kk + 8 half .. + 7.
+    // With group-pooled lists every row of a query block holds the sum of its
+    // g heads' rows, and the scale takes the 1/g of their mean.
     const int rowI = Iw0 + rho / a.g;
     const bool rowOk = rho < rows && rowI < nb;
     const bool pooled = a.shared == 2;
-    float4 qf[D / 8];
+    const int slot = 32 * rw + rho;
+    constexpr int QCH = D / 4;                                  // 16-byte chunks per fp32 row
+    float4* qstage = reinterpret_cast<float4*>(&bits[0][0]);   // [kRowSlots][QCH]
+    auto qpos = [](int r, int c) { return r * QCH + (c ^ (r & (QCH - 1))); };
+    for (int e = tid; e < kRowSlots * QCH; e += kThreads) {
+        const int r = e / QCH, c = e % QCH;
+        const int rr = r % 32;
+        const int I = rw_first(r / 32) + rr / a.g;
+        const bool ok = rr < rows && I < nb;
+        const int h = hk * a.g + rr % a.g;
+        const int64_t qrow = qblock_row(t, b, ok ? I : first);
+        qstage[qpos(r, c)] = reinterpret_cast<const float4*>(a.pq + ((int64_t)h * t.total_qblocks + qrow) * D)[c];
+    }
+    sg.load(a.pk, krow0, tile1(sg.cg), ncol, x0);        // phase 1's first two steps
+    sg.load(a.pk, krow0, tile1(2 + sg.cg), ncol, x1);
+    lds_barrier();
+    bf16x8 qh[D / 16], ql[D / 16];
     {
-        const int64_t qrow = qblock_row(t, b, rowOk ? rowI : first);
-        const int h = hk * a.g + (pooled ? 0 : rho % a.g);
-        const float4* src = reinterpret_cast<const float4*>(a.pq + ((int64_t)h * t.total_qblocks + qrow) * D + 8 * half);
+        float4 qf[D / 8];
+        const int r0 = pooled ? 32 * rw + (rho / a.g) * a.g : slot;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            qf[2 * kk] = src[4 * kk];
-            qf[2 * kk + 1] = src[4 * kk + 1];
+            qf[2 * kk] = qstage[qpos(r0, 4 * kk + 2 * half)];
+            qf[2 * kk + 1] = qstage[qpos(r0, 4 * kk + 2 * half + 1)];
         }
         if (pooled) {
             for (int j = 1; j < a.g; ++j) {
-                src += (int64_t)t.total_qblocks * D / 4;       // head h + j
 #pragma unroll
                 for (int kk = 0; kk < D / 8; ++kk) {
-                    const float4 x = src[4 * (kk / 2) + (kk & 1)];
+                    const float4 x = qstage[qpos(min(r0 + j, 32 * rw + 31), 4 * (kk / 2) + 2 * half + (kk & 1))];
                     qf[kk] = make_float4(qf[kk].x + x.x, qf[kk].y + x.y, qf[kk].z + x.z, qf[kk].w + x.w);
                 }
             }
         }
-    }
-    // Two register buffers: the rows of step p + 2 load while step p scores.
-    float4 x0[Stager<D>::F / 4], x1[Stager<D>::F / 4];
-    sg.load(a.pk, krow0, sg.cg, ncol, x0);               // phase 1's first two steps
-    sg.load(a.pk, krow0, 2 + sg.cg, ncol, x1);
-    bf16x8 qh[D / 16], ql[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        const float sc = rowOk ? (pooled ? a.scale / (float)a.g : a.scale) : 0.f;
-        const float4 u = qf[2 * kk], v = qf[2 * kk + 1];
-        split8(make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc), make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc),
-               qh[kk], ql[kk]);
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const float sc = rowOk ? (pooled ? a.scale / (float)a.g : a.scale) : 0.f;
+            const float4 u = qf[2 * kk], v = qf[2 * kk + 1];
+            split8(make_float4(u.x * sc, u.y * sc, u.z * sc, u.w * sc),
+                   make_float4(v.x * sc, v.y * sc, v.z * sc, v.w * sc), qh[kk], ql[kk]);
+        }
     }
     // One pass over column tiles tile_of(0), tile_of(1), ... (a tile index
     // >= ntile is staged but not scored): step p stages entries 2p and
@@ -241,92 +270,125 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     // valid need no causal mask.  Column block of register r within a tile:
     auto masked = [&](int ct) { return !(rows_full && 32 * ct + 31 <= Iw0); };
     auto colJ = [&](int r) { return (r & 3) + 8 * (r >> 2) + 4 * half; };
-    // Between the phases the bitmap words hold the bits of each (tile, row)'s
-    // score maximum (-inf for rows without a valid entry in the tile).
-
-    // Phase 1: per tile, this row's max (both halves of the wave), kept in
-    // tmax; then the row max over all tiles and both column groups.
-    float m = -INFINITY;
-    sweep((ntile + 1) >> 1, [](int i) { return i; }, [&](int ct, const TileStage<D>& st) {
-        const f32x16 s = tile_scores<D>(qh, ql, st, rho, half);
-        float tm = -INFINITY;
-        if (masked(ct)) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (rowOk && 32 * ct + colJ(r) <= rowI) tm = fmaxf(tm, s[r]);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[r]);
-        }
-        tm = fmaxf(tm, __shfl_xor(tm, 32));
-        if (half == 0) bits[ct][32 * rw + rho] = __float_as_uint(tm);
-        m = fmaxf(m, tm);
-    });
-    if (half == 0) pmax[cg][32 * rw + rho] = m;
-    lds_barrier();
-    m = pmax[0][32 * rw + rho];
-#pragma unroll
-    for (int c2 = 1; c2 < kColGroups; ++c2) m = fmaxf(m, pmax[c2][32 * rw + rho]);
-
-    // Tiles to score again: those where some row's maximum reaches its
-    // threshold (s <= tmax implies s - m <= tmax - m in floating point, so
-    // no other tile keeps anything).  Column group 0 of each row wave marks
-    // them; the list is compacted in ascending order and every other tile's
-    // words are cleared.
-    if (cg == 0) {
-        for (int ct = 0; ct < ntile_w; ++ct) {
-            const float tm = __uint_as_float(bits[ct][32 * rw + rho]);
-            if (__ballot(rowOk && tm - m >= a.ln_alpha) && lane == 0) atomicOr(&need[ct >> 5], 1u << (ct & 31));
-        }
-    }
-    lds_barrier();
-    int nneed = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxColTiles / 32; ++i) nneed += __popc(need[i]);
-    if (tid < ntile) {
-        const uint32_t word = need[tid >> 5], below = word & ((1u << (tid & 31)) - 1u);
-        if ((word >> (tid & 31)) & 1u) {
-            int pos = __popc(below);
-            for (int i = 0; i < (tid >> 5); ++i) pos += __popc(need[i]);
-            todo[pos] = tid;
-        }
-    }
-    for (int e = tid; e < ntile * kRowSlots; e += kThreads) {
-        const int ct = e / kRowSlots;
-        if (!((need[ct >> 5] >> (ct & 31)) & 1u)) bits[ct][e % kRowSlots] = 0u;
-    }
-    lds_barrier();
-    auto todo_tile = [&](int i) { return i < nneed ? todo[i] : ntile; };
-    sg.load(a.pk, krow0, todo_tile(sg.cg), ncol, x0);    // phase 2's first two steps
-    sg.load(a.pk, krow0, todo_tile(2 + sg.cg), ncol, x1);
-
-    // Phase 2: keep bits per listed (tile, row slot); bit j of a word is
-    // column block j of the tile.  Row waves whose rows keep nothing in the
-    // tile skip the scores.  The two halves of the wave hold alternate groups
-    // of 4 columns and are merged before the store.
-    sweep((nneed + 1) >> 1, todo_tile, [&](int ct, const TileStage<D>& st) {
-        const float tm = __uint_as_float(bits[ct][32 * rw + rho]);
+    auto keep_bits = [&](const f32x16& s, int ct, float mrow) {
+        const bool mk = masked(ct);
         uint32_t w = 0u;
-        if (__ballot(rowOk && tm - m >= a.ln_alpha)) {
-            const f32x16 s = tile_scores<D>(qh, ql, st, rho, half);
-            const bool mk = masked(ct);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                bool keep = s[r] - m >= a.ln_alpha;
-                if (mk) keep = keep && rowOk && 32 * ct + colJ(r) <= rowI;
-                w |= keep ? (1u << colJ(r)) : 0u;
-            }
-            w |= __shfl_xor(w, 32);
+        for (int r = 0; r < 16; ++r) {
+            bool keep = s[r] - mrow >= a.ln_alpha;
+            if (mk) keep = keep && rowOk && 32 * ct + colJ(r) <= rowI;
+            w |= keep ? (1u << colJ(r)) : 0u;
         }
-        if (half == 0) bits[ct][32 * rw + rho] = w;
-    });
+        return w | __shfl_xor(w, 32);
+    };
+
+    // Phase 1: per step the two column groups exchange their tile maxima, so
+    // m is the row's max over every tile visited so far, and each visited
+    // (tile, row) gets its keep bits against that running max.  A word is
+    // final unless m grows at a later step and the word holds a bit (a larger
+    // max only clears bits): such a row is flagged stale, and phase 2 scores
+    // its tiles again.  When the row max lies in the diagonal tile -- the
+    // usual case, nearby blocks score highest -- nothing is stale.
+    const int nstep1 = (ntile + 1) >> 1;
+    float m = -INFINITY;     // running row max (the same in both column groups)
+    int last_inc = -1;       // last step at which m grew
+    bool nz = false;         // this column group has formed a word with a bit
+    bool stale_row = false;  // ... and m grew after that
+    sg.store(stage[0], x0);
+    lds_barrier();
+    auto step1 = [&](int p, float4* xnext, float4* xfree) {
+        sg.load(a.pk, krow0, tile1(2 * (p + 2) + sg.cg), ncol, xfree);
+        const int ct = tile1(2 * p + cg);
+        const bool vis = ct < ntile_w;
+        f32x16 s = {};
+        float tm = -INFINITY;
+        if (vis) {
+            s = tile_scores<D>(qh, ql, stage[p & 1][cg], rho, half);
+            if (masked(ct)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (rowOk && 32 * ct + colJ(r) <= rowI) tm = fmaxf(tm, s[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[r]);
+            }
+            tm = fmaxf(tm, __shfl_xor(tm, 32));
+        }
+        if (half == 0) xch[cg][slot] = tm;
+        lds_barrier();
+        const float mt = fmaxf(tm, xch[cg ^ 1][slot]);
+        if (mt > m) {
+            m = mt;
+            last_inc = p;
+            stale_row = stale_row || nz;
+        }
+        if (vis) {
+            const uint32_t w = keep_bits(s, ct, m);
+            if (half == 0) bits[ct][slot] = w;
+            nz = nz || w != 0u;
+        }
+        if (p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
+        lds_barrier();
+    };
+    for (int p = 0; p < nstep1; p += 2) {
+        step1(p, x1, x0);
+        if (p + 1 < nstep1) step1(p + 1, x0, x1);
+    }
+    {
+        const bool wave_stale = __ballot(rowOk && stale_row) != 0ull;   // all lanes vote
+        if (lane == 0) wstale[wv] = wave_stale ? 1 : 0;
+    }
+    lds_barrier();
+    int any_stale = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) any_stale |= wstale[i];
+
+    if (any_stale) {
+        // Tiles to score again: a word formed before its row's max last grew
+        // that holds a bit.  Column group 0 of each row wave marks them; the
+        // list is compacted in ascending order.
+        auto stale = [&](int ct) {
+            return rowOk && ((ntile - 1 - ct) >> 1) < last_inc && bits[ct][slot] != 0u;
+        };
+        if (cg == 0 && (wstale[2 * rw] | wstale[2 * rw + 1])) {
+            for (int ct = 0; ct < ntile_w; ++ct)
+                if (__ballot(stale(ct)) && lane == 0) atomicOr(&need[ct >> 5], 1u << (ct & 31));
+        }
+        lds_barrier();
+        int nneed = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxColTiles / 32; ++i) nneed += __popc(need[i]);
+        if (tid < ntile) {
+            const uint32_t word = need[tid >> 5], below = word & ((1u << (tid & 31)) - 1u);
+            if ((word >> (tid & 31)) & 1u) {
+                int pos = __popc(below);
+                for (int i = 0; i < (tid >> 5); ++i) pos += __popc(need[i]);
+                todo[pos] = tid;
+            }
+        }
+        lds_barrier();
+        auto todo_tile = [&](int i) { return i < nneed ? todo[i] : ntile; };
+        sg.load(a.pk, krow0, todo_tile(sg.cg), ncol, x0);    // phase 2's first two steps
+        sg.load(a.pk, krow0, todo_tile(2 + sg.cg), ncol, x1);
+
+        // Phase 2: the listed tiles' words again, against the final max, for
+        // the row waves that hold a stale word there.
+        sweep((nneed + 1) >> 1, todo_tile, [&](int ct, const TileStage<D>& st) {
+            if (__ballot(stale(ct))) {
+                const f32x16 s = tile_scores<D>(qh, ql, st, rho, half);
+                const uint32_t w = keep_bits(s, ct, m);
+                if (half == 0) bits[ct][slot] = w;
+            }
+        });
+    }
 
     // Phase 3: ordered compaction, one row slot per lane (lanes 0..15 of
     // every wave): the row's tiles in ascending order, each tile's bits
-    // lowest first.
+    // lowest first.  The words are read four tiles at a time, so the LDS
+    // reads of a group are in flight together.
     if (lane < kRowSlots / kWaves) {
-        const int slot = wv * (kRowSlots / kWaves) + lane;
-        const int rw3 = slot / 32, r3 = slot % 32;
+        const int slot3 = wv * (kRowSlots / kWaves) + lane;
+        const int rw3 = slot3 / 32, r3 = slot3 % 32;
         const int ii = r3 / a.g, hi = r3 % a.g;
         const int I = rw_first(rw3) + ii;
         if (r3 < rows && I < nb) {
@@ -334,20 +396,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
             const int nt = I / 32 + 1;                       // tiles holding J <= I
             int32_t* out = a.kv_idx + list_row(t, b, h, I, nb, first);
             int pos = 0;
-            for (int ct = 0; ct < nt; ++ct) {
-                uint32_t w;
-                if (a.shared) {
-                    // Group-shared selection: the union of the g heads' keep bits
-                    // of this query block (row slots ii*g .. ii*g+g-1 of this row
-                    // wave); with group-pooled rows the g rows' bits are equal.
-                    w = 0u;
-                    for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
-                } else {
-                    w = bits[ct][slot];
+            for (int ct0 = 0; ct0 < nt; ct0 += 4) {
+                uint32_t wq[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int ct = min(ct0 + u, nt - 1);
+                    if (a.shared) {
+                        // Group-shared selection: the union of the g heads' keep bits
+                        // of this query block (row slots ii*g .. ii*g+g-1 of this row
+                        // wave); with group-pooled rows the g rows' bits are equal.
+                        uint32_t w = 0u;
+                        for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
+                        wq[u] = w;
+                    } else {
+                        wq[u] = bits[ct][slot3];
+                    }
                 }
-                while (w) {
-                    out[pos++] = 32 * ct + __ffs(w) - 1;
-                    w &= w - 1;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint32_t w = ct0 + u < nt ? wq[u] : 0u;
+                    while (w) {
+                        out[pos++] = 32 * (ct0 + u) + __ffs(w) - 1;
+                        w &= w - 1;
+                    }
                 }
             }
             a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = pos;

@@ -1,7 +1,9 @@
 """Selection at many column tiles: lists against the oracle's masks.
 
 The selection kernel streams the pooled keys in tiles of 32 blocks, two per
-step, and scores a tile again only where some row can keep a block in it.
+step, from the last tile to the first, thresholds every tile against the
+row's running max, and scores a tile again only where a row's bits were set
+before its max last grew.
 These cases span several steps, head-group sizes that do not divide 32
 (unused score rows), one and many query heads per KV head, both head
 dimensions and both block sizes, a ragged last block and the dense and
@@ -108,3 +110,48 @@ def test_maximum_blocks_per_request(fp8):
     worst = max(float(np.abs(o[I * B:(I + 1) * B, h] - o_ref[I * B:(I + 1) * B, h]).max()) for h, I in pairs)
     print(f"  {len(pairs)} sampled pairs: max|o-ref| {worst:.3e}", flush=True)
     assert worst <= tol
+
+
+@pytest.mark.parametrize("alpha", [0.05, 0.3, 1.0])
+@pytest.mark.parametrize("layout", ["scattered", "first", "mixed"])
+def test_row_max_away_from_diagonal(layout, alpha):
+    """Rows whose largest block score lies away from their diagonal tile, so
+    the selection kernel meets it late in its last-to-first walk and must
+    score earlier tiles again.  Query head j shares a direction u_j with the
+    keys, which carry a_jJ u_j in block J: a_jJ random per block
+    ("scattered"), falling from block 0 ("first": the max is always the
+    first block, met last), or per head ("mixed": rising for head 0, whose
+    max is on the diagonal, falling for head 1, random for heads 2 and 3, so
+    rows of one row wave differ in whether they are scored again).  The u_j
+    are orthogonal.  256 blocks of 64 tokens = 8 column tiles."""
+    S, Hq, Hkv, d, B = 16384, 4, 1, 128, 64
+    nB = S // B
+    gen = torch.Generator().manual_seed({"scattered": 41, "first": 42, "mixed": 43}[layout])
+    U = torch.zeros(Hq, d)
+    for j in range(Hq):
+        U[j, 32 * j:32 * (j + 1)] = 2.0                      # orthogonal, |u_j|^2 = 128
+    if layout == "scattered":
+        A = torch.rand(nB, generator=gen).repeat(Hq, 1)
+    elif layout == "first":
+        A = torch.linspace(1.0, 0.0, nB).repeat(Hq, 1)
+    else:
+        A = torch.stack([torch.linspace(0.0, 1.0, nB), torch.linspace(1.0, 0.0, nB),
+                         torch.rand(nB, generator=gen), torch.rand(nB, generator=gen)])
+    A = 4.0 * A          # head 0's max lies in its diagonal tile in 99% of rows (mixed), head 1's in tile 0
+    q = (U[None] + torch.randn(S, Hq, d, generator=gen)).to(torch.bfloat16)
+    kdir = (A.t()[:, :, None] * U[None]).sum(1)              # [nB, d]
+    k = (kdir.repeat_interleave(B, 0)[:, None, :] + torch.randn(S, Hkv, d, generator=gen)).to(torch.bfloat16)
+    v = torch.randn(S, Hkv, d, generator=gen).to(torch.bfloat16)
+    print(f"case {layout} alpha={alpha}", flush=True)
+    qd, kd, vd = (t.to(dev()) for t in (q, k, v))
+    qn, kn, vn = oracle_inputs(q, k, v)
+    p = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=False)
+    sel = fp.fp_select_blocks(p, qd, kd, vd)
+    torch.cuda.synchronize()
+    mask = check_lists(sel.kv_idx, sel.kv_cnt, Hq, nB)
+    ref = O.select_blocks(qn, kn, vn, B, alpha, pool_v=False)
+    outside, inside, band = compare_mask(mask, ref)
+    print(f"  density {mask.sum() / (Hq * nB * (nB + 1) / 2):.4f}, band {band}, in-band mismatches {inside}",
+          flush=True)
+    assert outside == 0
+    assert 0 < mask.sum() < Hq * nB * (nB + 1) // 2
