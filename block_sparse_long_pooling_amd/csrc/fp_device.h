@@ -30,8 +30,8 @@ struct SeqTable {
     int32_t blk_off[FP_TABLE_MAX + 1];   // cumulative KV blocks
     int32_t pre_off[FP_TABLE_MAX + 1];   // cumulative prefix blocks (KV blocks without queries)
     int32_t item_off[FP_TABLE_MAX + 1];
-    int16_t order[FP_TABLE_MAX];
-    int16_t tail[FP_TABLE_MAX];          // tokens in request b's last KV block (1 .. B)
+    alignas(4) int16_t order[FP_TABLE_MAX];
+    alignas(4) int16_t tail[FP_TABLE_MAX];   // tokens in request b's last KV block (1 .. B)
     int32_t batch;
     int32_t total_tokens;                // query tokens
     int32_t total_blocks;                // KV blocks
@@ -41,9 +41,16 @@ struct SeqTable {
 
 __device__ __forceinline__ int seq_blocks(const SeqTable& t, int b) { return t.blk_off[b + 1] - t.blk_off[b]; }
 __device__ __forceinline__ int first_block(const SeqTable& t, int b) { return t.pre_off[b + 1] - t.pre_off[b]; }
+// Entry i of a 16-bit table read as part of an aligned 32-bit word: with a
+// uniform index that is one scalar load of the kernel arguments (a 16-bit
+// load would go through the vector memory path and its counter).
+__device__ __forceinline__ int table16(const int16_t* tab, int i) {
+    const int w = reinterpret_cast<const int32_t*>(tab)[i >> 1];
+    return (i & 1) ? (w >> 16) : (int)(int16_t)w;
+}
 __device__ __forceinline__ int context_len(const SeqTable& t, int b, int B) {
     const int nb = seq_blocks(t, b);
-    return nb > 0 ? (nb - 1) * B + t.tail[b] : 0;
+    return nb > 0 ? (nb - 1) * B + table16(t.tail, b) : 0;
 }
 // Tokens of query block first_block(t, b) that precede the chunk (0 unless a
 // chunk starts inside a block): chunk row 0 is position first * B + phase.
@@ -70,7 +77,7 @@ __device__ __forceinline__ void item_of(const SeqTable& t, int rank, int& b, int
         int mid = (lo + hi + 1) >> 1;
         if (t.item_off[mid] <= rank) lo = mid; else hi = mid - 1;
     }
-    b = t.order[lo];
+    b = table16(t.order, lo);
     local = rank - t.item_off[lo];
 }
 

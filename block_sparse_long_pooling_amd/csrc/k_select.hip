@@ -129,6 +129,19 @@ __device__ __forceinline__ f32x16 tile_scores(const bf16x8* qh, const bf16x8* ql
 // Workgroup barrier over LDS only: the next step's global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Combine a lane's value with that of lane l ^ 32 (the other half of the
+// wave holds the other 16 columns of the same score row).  permlane32_swap
+// exchanges the halves of two copies of v, which then hold the lower and the
+// upper half's values in every lane: a register move, no LDS round trip.
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ uint32_t or_halves(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] | r[1];
+}
+
 // Workgroup = up to 128 score rows (4 row waves x TI query blocks x g heads)
 // of one KV head.  Wave wv: row wave rw = wv / 2, column group cg = wv % 2;
 // each step stages two column tiles, and column group cg scores the (cg)-th
@@ -209,17 +222,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     constexpr int QCH = D / 4;                                  // 16-byte chunks per fp32 row
     float4* qstage = reinterpret_cast<float4*>(&bits[0][0]);   // [kRowSlots][QCH]
     auto qpos = [](int r, int c) { return r * QCH + (c ^ (r & (QCH - 1))); };
-    for (int e = tid; e < kRowSlots * QCH; e += kThreads) {
-        const int r = e / QCH, c = e % QCH;
-        const int rr = r % 32;
-        const int I = rw_first(r / 32) + rr / a.g;
-        const bool ok = rr < rows && I < nb;
-        const int h = hk * a.g + rr % a.g;
-        const int64_t qrow = qblock_row(t, b, ok ? I : first);
-        qstage[qpos(r, c)] = reinterpret_cast<const float4*>(a.pq + ((int64_t)h * t.total_qblocks + qrow) * D)[c];
-    }
     sg.load(a.pk, krow0, tile1(sg.cg), ncol, x0);        // phase 1's first two steps
     sg.load(a.pk, krow0, tile1(2 + sg.cg), ncol, x1);
+    {
+        // All of a thread's loads are issued before the first LDS write, so
+        // the gather waits on memory once.
+        constexpr int NQ = kRowSlots * QCH / kThreads;
+        float4 qv[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = tid + i * kThreads;
+            const int r = e / QCH, c = e % QCH;
+            const int rr = r % 32;
+            const int I = rw_first(r / 32) + rr / a.g;
+            const bool ok = rr < rows && I < nb;
+            const int h = hk * a.g + rr % a.g;
+            const int64_t qrow = qblock_row(t, b, ok ? I : first);
+            qv[i] = reinterpret_cast<const float4*>(a.pq + ((int64_t)h * t.total_qblocks + qrow) * D)[c];
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = tid + i * kThreads;
+            qstage[qpos(e / QCH, e % QCH)] = qv[i];
+        }
+    }
     lds_barrier();
     bf16x8 qh[D / 16], ql[D / 16];
     {
@@ -270,16 +296,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
     // valid need no causal mask.  Column block of register r within a tile:
     auto masked = [&](int ct) { return !(rows_full && 32 * ct + 31 <= Iw0); };
     auto colJ = [&](int r) { return (r & 3) + 8 * (r >> 2) + 4 * half; };
+    // Columns of tile ct that this lane's row may keep: J <= rowI, and none
+    // for rows without a query block.
+    auto colmask = [&](int ct) -> uint32_t {
+        if (!masked(ct)) return 0xffffffffu;
+        const int lim = rowI - 32 * ct;             // last column the row may keep
+        const uint32_t cm = lim >= 31 ? 0xffffffffu : lim < 0 ? 0u : (2u << lim) - 1u;
+        return rowOk ? cm : 0u;
+    };
+    // Keep bits of the row (both halves' columns), branch-free.
     auto keep_bits = [&](const f32x16& s, int ct, float mrow) {
-        const bool mk = masked(ct);
         uint32_t w = 0u;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            bool keep = s[r] - mrow >= a.ln_alpha;
-            if (mk) keep = keep && rowOk && 32 * ct + colJ(r) <= rowI;
-            w |= keep ? (1u << colJ(r)) : 0u;
-        }
-        return w | __shfl_xor(w, 32);
+        for (int r = 0; r < 16; ++r) w |= (s[r] - mrow >= a.ln_alpha) ? (1u << colJ(r)) : 0u;
+        return or_halves(w) & colmask(ct);
     };
 
     // Phase 1: per step the two column groups exchange their tile maxima, so
@@ -302,17 +332,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
         const bool vis = ct < ntile_w;
         f32x16 s = {};
         float tm = -INFINITY;
+        // The next step's rows go into the other stage buffer (its last
+        // readers finished before the previous barrier) while this step's
+        // products run.
         if (vis) {
             s = tile_scores<D>(qh, ql, stage[p & 1][cg], rho, half);
+            if (p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
             if (masked(ct)) {
+                const uint32_t cm = colmask(ct);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (rowOk && 32 * ct + colJ(r) <= rowI) tm = fmaxf(tm, s[r]);
+                for (int r = 0; r < 16; ++r) tm = fmaxf(tm, ((cm >> colJ(r)) & 1u) ? s[r] : -INFINITY);
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[r]);
             }
-            tm = fmaxf(tm, __shfl_xor(tm, 32));
+            tm = max_halves(tm);
+        } else if (p + 1 < nstep1) {
+            sg.store(stage[(p + 1) & 1], xnext);
         }
         if (half == 0) xch[cg][slot] = tm;
         lds_barrier();
@@ -327,7 +363,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
             if (half == 0) bits[ct][slot] = w;
             nz = nz || w != 0u;
         }
-        if (p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
         lds_barrier();
     };
     for (int p = 0; p < nstep1; p += 2) {
