@@ -417,46 +417,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
         });
     }
 
-    // Phase 3: ordered compaction, one row slot per lane (lanes 0..15 of
-    // every wave): the row's tiles in ascending order, each tile's bits
-    // lowest first.  The words are read four tiles at a time, so the LDS
-    // reads of a group are in flight together.
-    if (lane < kRowSlots / kWaves) {
-        const int slot3 = wv * (kRowSlots / kWaves) + lane;
+    // Phase 3: ordered compaction.  Four lanes per row slot (16 slots per
+    // wave), each taking a consecutive quarter of the row's tiles: the lanes
+    // count their bits, scan the counts across the four lanes, and write
+    // their blocks from that offset, each tile's bits lowest first.
+    {
+        const int q4 = lane & 3;
+        const int slot3 = wv * (kRowSlots / kWaves) + (lane >> 2);
         const int rw3 = slot3 / 32, r3 = slot3 % 32;
         const int ii = r3 / a.g, hi = r3 % a.g;
         const int I = rw_first(rw3) + ii;
-        if (r3 < rows && I < nb) {
+        const bool live = r3 < rows && I < nb;
+        const int nt = live ? I / 32 + 1 : 0;            // tiles holding J <= I
+        const int per = (nt + 3) >> 2;
+        const int c0 = min(nt, q4 * per), c1 = min(nt, c0 + per);
+        auto word = [&](int ct) -> uint32_t {
+            if (a.shared) {
+                // Group-shared selection: the union of the g heads' keep bits
+                // of this query block (row slots ii*g .. ii*g+g-1 of this row
+                // wave); with group-pooled rows the g rows' bits are equal.
+                uint32_t w = 0u;
+                for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
+                return w;
+            }
+            return bits[ct][slot3];
+        };
+        int cnt = 0;
+        for (int ct = c0; ct < c1; ++ct) cnt += __popc(word(ct));
+        int incl = cnt;
+        int up = __shfl_up(incl, 1, 4);
+        if (q4 >= 1) incl += up;
+        up = __shfl_up(incl, 2, 4);
+        if (q4 >= 2) incl += up;
+        if (live) {
             const int h = hk * a.g + hi;
-            const int nt = I / 32 + 1;                       // tiles holding J <= I
             int32_t* out = a.kv_idx + list_row(t, b, h, I, nb, first);
-            int pos = 0;
-            for (int ct0 = 0; ct0 < nt; ct0 += 4) {
-                uint32_t wq[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int ct = min(ct0 + u, nt - 1);
-                    if (a.shared) {
-                        // Group-shared selection: the union of the g heads' keep bits
-                        // of this query block (row slots ii*g .. ii*g+g-1 of this row
-                        // wave); with group-pooled rows the g rows' bits are equal.
-                        uint32_t w = 0u;
-                        for (int j = 0; j < a.g; ++j) w |= bits[ct][32 * rw3 + ii * a.g + j];
-                        wq[u] = w;
-                    } else {
-                        wq[u] = bits[ct][slot3];
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uint32_t w = ct0 + u < nt ? wq[u] : 0u;
-                    while (w) {
-                        out[pos++] = 32 * (ct0 + u) + __ffs(w) - 1;
-                        w &= w - 1;
-                    }
+            int pos = incl - cnt;
+            for (int ct = c0; ct < c1; ++ct) {
+                uint32_t w = word(ct);
+                while (w) {
+                    out[pos++] = 32 * ct + __ffs(w) - 1;
+                    w &= w - 1;
                 }
             }
-            a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = pos;
+            if (q4 == 3) a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)] = incl;
         }
     }
 }
