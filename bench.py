@@ -327,8 +327,9 @@ def mask_agreement(sel_a, sel_b, S, Hq, B, dev):
 
 def hbm_anchor(stream, dev):
     """Streaming bandwidth of torch's own kernels on this GPU, as a sanity
-    anchor for the 8 TB/s peak: a 4 GiB fp32 sum (read) and a 2 GiB copy
-    (read + write)."""
+    anchor for the 8 TB/s peak: a 4 GiB fp32 sum (read), a 2 GiB copy (read +
+    write), and a bf16 -> e4m3 conversion of 1.5 GiB (2 bytes read per byte
+    written: the read/write mix of the fused fp8 preparation)."""
     import torch
     buf = torch.ones(1 << 30, dtype=torch.float32, device=dev)
     t_sum = timed_ms(lambda: buf.sum(), 5, stream)
@@ -336,8 +337,13 @@ def hbm_anchor(stream, dev):
     dst = torch.empty_like(src)
     t_copy = timed_ms(lambda: dst.copy_(src), 5, stream)
     del buf, src, dst
+    src16 = torch.ones(3 << 28, dtype=torch.bfloat16, device=dev)
+    dst8 = torch.empty(3 << 28, dtype=torch.float8_e4m3fn, device=dev)
+    t_cvt = timed_ms(lambda: dst8.copy_(src16), 5, stream)
+    del src16, dst8
     return {"torch_sum_read_gbps": round(4 * (1 << 30) / (t_sum * 1e-3) / 1e9, 1),
-            "torch_copy_gbps": round(2 * 4 * (1 << 29) / (t_copy * 1e-3) / 1e9, 1)}
+            "torch_copy_gbps": round(2 * 4 * (1 << 29) / (t_copy * 1e-3) / 1e9, 1),
+            "torch_bf16_to_fp8_gbps": round(3 * (3 << 28) / (t_cvt * 1e-3) / 1e9, 1)}
 
 
 def timed_ms(fn, n, stream):

@@ -24,6 +24,8 @@
 // rounded quotient (Markstein's correction step).  Quotients small enough to
 // lose precision as fp32 subnormals lie far below the smallest e4m3 code and
 // encode as zero either way.
+#include <type_traits>
+
 #include "fp_launch.h"
 
 // The quotient steps below are explicit FMAs; nothing else may be fused.
@@ -75,31 +77,50 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     auto row_of = [=](int tok) -> int64_t { return pg ? kv_row<true>(kv, b, 0, t0 + tok) : tok; };
     const uint16_t* src = a.src[ts] + base;
 
+    // Q_bar may average only the skeleton queries (every q_stride-th token).
+    const int stride = ts == 0 ? a.q_stride : 1;
+    // Whole blocks of packed rows with every head of the group present and
+    // every token counted (the common case) take a path without per-token
+    // tests: unconditional loads and stores at 32-bit offsets from the
+    // block's first row.
+    const bool full = !pg && n == B && stride == 1 && (g + 1) * HPG <= H;
     uint4 x[NS];
+    if (full) {
+        const char* src8 = reinterpret_cast<const char*>(src);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int tok = 2 * kWaves * s + 2 * w + hf;
-        const int64_t r = row_of(min(tok, n - 1));
-        x[s] = (hv && tok < n && r >= 0) ? *reinterpret_cast<const uint4*>(src + r * row) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < NS; ++s) {
+            const int tok = 2 * kWaves * s + 2 * w + hf;
+            x[s] = *reinterpret_cast<const uint4*>(src8 + (uint32_t)tok * (uint32_t)(row * 2));
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int tok = 2 * kWaves * s + 2 * w + hf;
+            const int64_t r = row_of(min(tok, n - 1));
+            x[s] = (hv && tok < n && r >= 0) ? *reinterpret_cast<const uint4*>(src + r * row)
+                                            : make_uint4(0, 0, 0, 0);
+        }
     }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float amax = 0.f;
-    // Q_bar may average only the skeleton queries (every q_stride-th token).
-    const int stride = ts == 0 ? a.q_stride : 1;
+    auto accumulate = [&](auto all_counted) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
-        const bool counted = (2 * kWaves * s + 2 * w + hf) % stride == 0;
+        for (int s = 0; s < NS; ++s) {
+            const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+            const bool counted = decltype(all_counted)::value || (2 * kWaves * s + 2 * w + hf) % stride == 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
-            if (counted) {
-                sum[2 * i] += lo;
-                sum[2 * i + 1] += hi;
+            for (int i = 0; i < 4; ++i) {
+                const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
+                sum[2 * i] += counted ? lo : 0.f;
+                sum[2 * i + 1] += counted ? hi : 0.f;
+                amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
             }
-            amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
         }
-    }
+    };
+    if (full)
+        accumulate(std::true_type());
+    else
+        accumulate(std::false_type());
     // Sums: the two token halves of a wave, then the waves (in wave order,
     // so the sum order is fixed).
 #pragma unroll
@@ -167,7 +188,7 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int tok = 2 * kWaves * s + 2 * w + hf;
-        if (tok >= n) continue;
+        if (!full && tok >= n) continue;
         const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
         uint32_t out[2];
 #pragma unroll
@@ -182,8 +203,12 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
             v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
             out[i] = (uint32_t)v;
         }
-        const int64_t r = row_of(tok);
-        if (r >= 0) *reinterpret_cast<uint2*>(dst + r * row) = make_uint2(out[0], out[1]);
+        if (full) {
+            *reinterpret_cast<uint2*>(dst + (uint32_t)tok * (uint32_t)row) = make_uint2(out[0], out[1]);
+        } else {
+            const int64_t r = row_of(tok);
+            if (r >= 0) *reinterpret_cast<uint2*>(dst + r * row) = make_uint2(out[0], out[1]);
+        }
     }
 }
 
