@@ -94,15 +94,20 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
     DmaPlan<D, BLK, G::NT> plan;
     const uint4* zero = &kZeroChunk;
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * w * 16);
+    constexpr int NLOAD = DmaPlan<D, BLK, G::NT>::NLOAD;
+    // A kept tile's DMAs; K and V rows share their pages: one set of page
+    // ids (paged layout) for both.
+    auto issue_kept = [&](const It& itm, int code, char* kdst, char* vdst, const int* pg) {
+        issue_tile<D, BLK, G::NT, PAGED>(itm.kfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero, kdst,
+                                      wave_base);
+        issue_tile<D, BLK, G::NT, PAGED>(itm.vfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero, vdst,
+                                      wave_base);
+    };
     auto issue = [&](const It& itm, int code, char* kdst, char* vdst) {
         if (code < kCorr) {
-            // K and V rows share their pages: one set of page ids for both.
-            int pg[DmaPlan<D, BLK, G::NT>::NLOAD];
+            int pg[NLOAD];
             if (PAGED) load_tile_pages(itm.pages, a.kv, code, itm.len - code * BLK, plan, pg);
-            issue_tile<D, BLK, G::NT, PAGED>(itm.kfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero,
-                                          kdst, wave_base);
-            issue_tile<D, BLK, G::NT, PAGED>(itm.vfirst, pg, a.kv, rs, code, itm.len - code * BLK, plan, zero,
-                                          vdst, wave_base);
+            issue_kept(itm, code, kdst, vdst, pg);
         } else {
             // Pooled rows of this request's blocks for the KV head (contiguous, row stride D).
             const int ct = code - kCorr;
@@ -178,6 +183,17 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
     lds_barrier();
     int J = next_tile(cur, act);
     if (J != INT_MAX) issue(cur, J, kb1, vb1);
+    // Paged layout: the walk runs one tile further ahead.  Jn, the tile
+    // after J, is known a step before its DMA, and the page ids of its rows
+    // (pgn) are loaded then, so a step issues its DMA right after the
+    // barrier instead of first waiting on the block table.
+    int Jn = INT_MAX, actn = 0;
+    int pgn[NLOAD];
+    auto ahead = [&](It& itm) {
+        Jn = next_tile(itm, actn);
+        if (Jn < kCorr) load_tile_pages(itm.pages, a.kv, Jn, itm.len - Jn * BLK, plan, pgn);
+    };
+    if (PAGED && J != INT_MAX) ahead(cur);
     load_q(cur);
 
     float m, l;
@@ -191,8 +207,19 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
     auto step = [&](char* kcur, char* vcur, char* knext, char* vnext) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA for tile J is done
         lds_barrier();                                   // ... every thread's; the other buffers are free
-        const int Jn = next_tile(cur, act_next);
-        if (Jn != INT_MAX) issue(cur, Jn, knext, vnext);
+        int Jn1;
+        if (PAGED) {
+            Jn1 = Jn;
+            act_next = actn;
+            if (Jn1 < kCorr)
+                issue_kept(cur, Jn1, knext, vnext, pgn);
+            else if (Jn1 != INT_MAX)
+                issue(cur, Jn1, knext, vnext);
+            if (Jn1 != INT_MAX) ahead(cur);
+        } else {
+            Jn1 = next_tile(cur, act_next);
+            if (Jn1 != INT_MAX) issue(cur, Jn1, knext, vnext);
+        }
         if ((act >> hs) & 1) {
             const bool corr = J >= kCorr;
             // Correction tile: bit j of skip[sub] <=> pooled block ct*BLK + 32 sub + j
@@ -245,7 +272,7 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
             half_tile(std::integral_constant<int, 0>());
             if (G::NSUB > SH) half_tile(std::integral_constant<int, (G::NSUB > SH ? SH : 0)>());
         }
-        J = Jn;
+        J = Jn1;
         act = act_next;
     };
 
@@ -287,6 +314,7 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         lds_barrier();                                   // zeroed bitmap; staging buffers free
         if (has_next) mark(nxt, Jn0, actn0);
+        if (PAGED && has_next) ahead(nxt);
         auto stage_rows = [&](char* buf) {
             uint4* stage = reinterpret_cast<uint4*>(buf);
 #pragma unroll
