@@ -295,13 +295,17 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     const uint16_t* kfirst = reinterpret_cast<const uint16_t*>(k8 + kvbase);
     const uint16_t* vfirst = reinterpret_cast<const uint16_t*>(v8 + kvbase);
     const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
-    auto issue8 = [&](int J, char* dst) {
-        int pg[DmaPlan<D / 2, BLK, NTH>::NLOAD];
-        if (PAGED) load_tile_pages(pages, a.kv, J, len - J * BLK, plan, pg);
+    constexpr int NLOAD = DmaPlan<D / 2, BLK, NTH>::NLOAD;
+    auto issue8_pg = [&](int J, char* dst, const int* pg) {
         issue_tile<D / 2, BLK, NTH, PAGED>(kfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk, dst,
                                            wave_base);
         issue_tile<D / 2, BLK, NTH, PAGED>(vfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk,
                                            dst + VOFF, wave_base);
+    };
+    auto issue8 = [&](int J, char* dst) {
+        int pg[NLOAD];
+        if (PAGED) load_tile_pages(pages, a.kv, J, len - J * BLK, plan, pg);
+        issue8_pg(J, dst, pg);
     };
     char* buf0 = reinterpret_cast<char*>(lk);
     char* buf1 = reinterpret_cast<char*>(lv);
@@ -338,17 +342,39 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     };
     int J = 0;
     float sk = 1.f, sv = 1.f;
+    // Paged layout: the walk runs one tile further ahead -- tile it + 1's
+    // block, scales and page ids (Ja, ska, sva, pga) are known a step before
+    // its DMA, so a step issues the DMA right after the barrier instead of
+    // first waiting on the block table.
+    int Ja = 0;
+    float ska = 1.f, sva = 1.f;
+    int pga[NLOAD];
     if (cnt > 0) {
         load_window(0);
         from_window(0, J, sk, sv);
         issue8(J, buf0);
+        if (PAGED && cnt > 1) {
+            from_window(1, Ja, ska, sva);
+            load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+        }
     }
     auto step = [&](int it, char* bcur, char* bnext) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of tile it is done
         lds_barrier();                                   // ... every thread's; the other buffer is free
         int Jn = 0;
         float skn = 1.f, svn = 1.f;
-        if (it + 1 < cnt) {
+        if (PAGED) {
+            // The window move waits on memory; nothing else is in flight yet.
+            if (it + 2 < cnt && it + 2 - wbase == 64) load_window(it + 2);
+            Jn = Ja;
+            skn = ska;
+            svn = sva;
+            if (it + 1 < cnt) issue8_pg(Jn, bnext, pga);
+            if (it + 2 < cnt) {
+                from_window(it + 2, Ja, ska, sva);
+                load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+            }
+        } else if (it + 1 < cnt) {
             if (it + 1 - wbase == 64) load_window(it + 1);
             from_window(it + 1, Jn, skn, svn);
             issue8(Jn, bnext);

@@ -24,8 +24,6 @@
 // rounded quotient (Markstein's correction step).  Quotients small enough to
 // lose precision as fp32 subnormals lie far below the smallest e4m3 code and
 // encode as zero either way.
-#include <type_traits>
-
 #include "fp_launch.h"
 
 // The quotient steps below are explicit FMAs; nothing else may be fused.
@@ -82,8 +80,10 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     // Whole blocks of packed rows with every head of the group present and
     // every token counted (the common case) take a path without per-token
     // tests: unconditional loads and stores at 32-bit offsets from the
-    // block's first row.
-    const bool full = !pg && n == B && stride == 1 && (g + 1) * HPG <= H;
+    // block's first row.  Only in the packed-layout kernel: in the paged one
+    // the second path's registers spilled inside the token loops (2.3x
+    // slower).
+    const bool full = !PAGED && n == B && stride == 1 && (g + 1) * HPG <= H;
     uint4 x[NS];
     if (full) {
         const char* src8 = reinterpret_cast<const char*>(src);
@@ -103,24 +103,18 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float amax = 0.f;
-    auto accumulate = [&](auto all_counted) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
-            const bool counted = decltype(all_counted)::value || (2 * kWaves * s + 2 * w + hf) % stride == 0;
+    for (int s = 0; s < NS; ++s) {
+        const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+        const bool counted = full || (2 * kWaves * s + 2 * w + hf) % stride == 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
-                sum[2 * i] += counted ? lo : 0.f;
-                sum[2 * i + 1] += counted ? hi : 0.f;
-                amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(wd[i]), hi = bf16_hi(wd[i]);
+            sum[2 * i] += counted ? lo : 0.f;
+            sum[2 * i + 1] += counted ? hi : 0.f;
+            amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
         }
-    };
-    if (full)
-        accumulate(std::true_type());
-    else
-        accumulate(std::false_type());
+    }
     // Sums: the two token halves of a wave, then the waves (in wave order,
     // so the sum order is fixed).
 #pragma unroll
