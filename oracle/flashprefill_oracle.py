@@ -462,6 +462,41 @@ def quantize_fp8_blockwise(x, block: int):
     return codes, scales
 
 
+def quantize_fp8_chunk(q, block: int, P0: int):
+    """Codes and scales of a chunk's queries for fp8 chunked prefill (reading
+    R10 applied to the chunk's query blocks): row r is position P0 + r, and
+    query block I holds the chunk's rows at positions
+    [max(I block, P0), min((I + 1) block, P0 + q_len)); each (head, query
+    block) gets scale amax / 448 over those rows (1 if all zero) and codes
+    E4M3(clamp(x / scale)), the division in fp32.
+    q [q_len, H, d] -> (codes uint8 [q_len, H, d], scales fp32 [H, n]) for
+    query blocks first .. first + n - 1, first = P0 // block."""
+    x32 = np.asarray(q, dtype=np.float32)
+    q_len, H, d = x32.shape
+    codes = np.empty((q_len, H, d), dtype=np.uint8)
+    if q_len == 0:
+        return codes, np.empty((H, 0), dtype=np.float32)
+    first, last = P0 // block, (P0 + q_len - 1) // block
+    scales = np.empty((H, last - first + 1), dtype=np.float32)
+    for i, I in enumerate(range(first, last + 1)):
+        r0 = max(I * block, P0) - P0
+        r1 = min((I + 1) * block, P0 + q_len) - P0
+        seg = x32[r0:r1]
+        amax = np.abs(seg).max(axis=(0, 2))
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        scales[:, i] = sc
+        y = np.clip(seg / sc[None, :, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+        codes[r0:r1] = e4m3_encode(y)
+    return codes, scales
+
+
+def dequantize_chunk(codes_value, scales, block: int, P0: int) -> np.ndarray:
+    """x = x8 * scale[h, I - first] for a chunk's fp8 values (row r at position P0 + r)."""
+    x8 = _f64(codes_value)
+    I = (P0 + np.arange(x8.shape[0])) // block - P0 // block
+    return x8 * _f64(scales)[:, I].T[:, :, None]
+
+
 def dequantize_blockwise(codes_value, scales, block: int) -> np.ndarray:
     """x = x8 * scale[h, t // block] for fp8 values decoded to float ([S, H, d])."""
     x8 = _f64(codes_value)

@@ -553,6 +553,44 @@ def test_quantize_blockwise_matches_generator_quantizer():
         assert np.array_equal(c_o, c_t.numpy()) and np.array_equal(s_o, s_t.numpy())
 
 
+def test_quantize_chunk_aligned_equals_blockwise():
+    """A chunk that starts on a block boundary has the blockwise codes and
+    scales of its own rows."""
+    r = np.random.default_rng(5)
+    q = (r.standard_normal((300, 3, 16)) * 3).astype(np.float32)
+    c, s = O.quantize_fp8_chunk(q, 128, 2 * 128)
+    c_ref, s_ref = O.quantize_fp8_blockwise(q, 128)
+    assert np.array_equal(c, c_ref) and np.array_equal(s, s_ref)
+
+
+@pytest.mark.parametrize("P0", [37, 127, 128 + 1])
+def test_quantize_chunk_windows_from_positions(P0):
+    """Each query block's scale and codes come from exactly the chunk's rows
+    whose positions fall in it: the first window holds the rows up to the
+    next block boundary, the last one stops at the chunk's end."""
+    B, q_len = 128, 400
+    r = np.random.default_rng(P0)
+    q = (r.standard_normal((q_len, 2, 8)) * r.uniform(0.5, 4, (q_len, 1, 1))).astype(np.float32)
+    c, s = O.quantize_fp8_chunk(q, B, P0)
+    pos = P0 + np.arange(q_len)
+    blocks = np.unique(pos // B)
+    assert s.shape == (2, len(blocks))
+    for i, I in enumerate(blocks):
+        rows = np.nonzero(pos // B == I)[0]                      # the chunk's rows in block I
+        if i == 0:
+            assert len(rows) == B - P0 % B
+        seg = q[rows]
+        for h in range(2):
+            assert s[h, i] == np.float32(np.abs(seg[:, h]).max()) / np.float32(448)
+        cs, ss = O.quantize_fp8_blockwise(seg, len(rows))          # the window as a one-block sequence
+        assert np.array_equal(c[rows], cs) and np.array_equal(s[:, i], ss[:, 0])
+    # dequantized values sit within E4M3's half-ulp (2^-4 relative) of the input in its normal range
+    deq = O.dequantize_chunk(O.e4m3_decode(c), s, B, P0)
+    big = np.abs(q) >= 2.0 ** -6 * s[:, pos // B - P0 // B].T[:, :, None]
+    assert big.mean() > 0.9
+    assert (np.abs(deq - q)[big] / np.abs(q)[big]).max() <= 2.0 ** -4
+
+
 # ------------------------------------------------- group-shared selection
 
 def _brute_force_union(q, k, B, alpha):
