@@ -17,7 +17,7 @@ bandwidth of torch's own sum and copy kernels on the same GPU.  The CPU
 baseline is the fp64 oracle on a bounded sample of the same workload.
 
 Beside the headline: the fp8 layer, the paged batch (bf16 and fp8) and its
-chunked variant; the tiny (1K) and 32K workloads with their own latency,
+chunked variant (bf16 and fp8); the tiny (1K) and 32K workloads with their own latency,
 effective TFLOP/s and alpha = 0 dense reference (`configs`); and, outside every
 timed region, a parity summary of all five workloads against the oracle
 (`parity`: mask mismatches inside and outside the threshold band, band size,
@@ -366,7 +366,7 @@ def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
     the bf16 data, so the lists are the headline's up to threshold-band
     rounding; then fp8 attention), the paged continuous batch of 8 requests
     (selection and attention in one call), and the same batch as chunked
-    prefill."""
+    prefill, in bf16 and with fp8 attention."""
     import torch
     res = {}
     S, Hq, d = q.shape
@@ -429,7 +429,7 @@ def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
                         "step_ms": round(t8, 4), "tokens_per_s": round(cu[-1] / (t8 * 1e-3), 1),
                         "kept_blocks": kept8, "tflops": round(f_8 / (t8 * 1e-3) / 1e12, 2)}
     log(f"bench: paged fp8 {res['paged_fp8']}")
-    del r8, c8
+    del r8
 
     # Chunked prefill on the same contexts: the last CHUNK tokens of each
     # request are new; the prefix means were pooled into the cache by an
@@ -459,6 +459,25 @@ def other_layouts(fp, synth, q, k, v, head, stream, dev, corr):
                       "new_tokens_per_s": round(cu_new[-1] / (tc * 1e-3), 1), "kept_blocks": kept,
                       "tflops": round(f_c / (tc * 1e-3) / 1e12, 2)}
     log(f"bench: chunked {res['chunked']}")
+
+    # The same chunks with fp8 attention: the e4m3 pages of the prefixes are
+    # those the fp8 paged call wrote; the timed call encodes the chunks' query
+    # blocks (Q into its workspace, K and V into the pages) and reads the
+    # prefix means from the same pooled cache.
+    r8c = fp.fp_sparse_prefill_chunked_paged_fp8(p8, q_new, kc, vc, bt, cu_new, lens, c8, pooled_cache=cache,
+                                                 prefix_pooled=True)
+    tc8 = timed_ms(lambda: fp.fp_sparse_prefill_chunked_paged_fp8(p8, q_new, kc, vc, bt, cu_new, lens, c8,
+                                                                  pooled_cache=cache, prefix_pooled=True,
+                                                                  workspace=r8c.workspace, out=r8c.out),
+                   5, stream)
+    kept8, skipped8 = list_work(r8c.kv_idx, r8c.kv_cnt, lens, cut, Hqp, Bp, dev)
+    f_c8 = 4.0 * dp * Bp * (Bp * kept8 + (skipped8 if corr else 0))
+    res["chunked_fp8"] = {"workload": w.name + "_last4096_fp8", "dtype": "fp8_e4m3", "new_tokens": cu_new[-1],
+                          "context_tokens": cu[-1], "chunk": CHUNK, "step_ms": round(tc8, 4),
+                          "new_tokens_per_s": round(cu_new[-1] / (tc8 * 1e-3), 1), "kept_blocks": kept8,
+                          "tflops": round(f_c8 / (tc8 * 1e-3) / 1e12, 2)}
+    log(f"bench: chunked fp8 {res['chunked_fp8']}")
+    del r8c, c8
     return res
 
 

@@ -68,6 +68,11 @@ EXPORTS = {
                                                        ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
                                                        _I32P, _I32P, ctypes.c_int32, _P, ctypes.c_int32,
                                                        _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "fp_sparse_prefill_chunked_paged_fp8": (ctypes.c_int, [ctypes.POINTER(fp_params), _P, _P, _P,
+                                                           ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                                           _I32P, _I32P, ctypes.c_int32, _P, ctypes.c_int32,
+                                                           _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
+                                                           _P]),
     "fp_chunked_sizes": (ctypes.c_int, [ctypes.POINTER(fp_params), _I32P, _I32P, ctypes.c_int32,
                                         ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                         ctypes.POINTER(ctypes.c_size_t)]),
@@ -404,6 +409,38 @@ def fp_sparse_prefill_chunked_paged(params: fp_params, q: torch.Tensor, k_cache:
     _check(lib().fp_sparse_prefill_chunked_paged(
         ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
         _ptr(block_table), block_table.shape[1], cu, kl, batch, _ptr(pooled_cache), int(bool(prefix_pooled)),
+        _ptr(kv_idx), _ptr(kv_cnt), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
+
+
+def fp_sparse_prefill_chunked_paged_fp8(params: fp_params, q: torch.Tensor, k_cache: torch.Tensor,
+                                        v_cache: torch.Tensor, block_table: torch.Tensor, cu_seqlens_q,
+                                        kv_lens, cache: Fp8Cache, pooled_cache: Optional[torch.Tensor] = None,
+                                        prefix_pooled: bool = False, return_lse: bool = False,
+                                        workspace: Optional[torch.Tensor] = None,
+                                        out: Optional[torch.Tensor] = None) -> VarlenResult:
+    """Chunked prefill with fp8 attention: selection on the bf16 pages as in
+    fp_sparse_prefill_chunked_paged; the chunks' query blocks are encoded into
+    the e4m3 pages of `cache` (earlier blocks must hold the codes of earlier
+    calls), and attention reads the e4m3 pages."""
+    T, Hq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    dev = q.device
+    cu = _cu_host(cu_seqlens_q)
+    kl = _cu_host(kv_lens)
+    batch = len(cu) - 1
+    cap, ncnt, wsb = fp_chunked_sizes(params, list(cu), list(kl))
+    kv_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty(max(ncnt, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().fp_sparse_prefill_chunked_paged_fp8(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), page_size, num_pages,
+        _ptr(block_table), block_table.shape[1], cu, kl, batch, _ptr(pooled_cache), int(bool(prefix_pooled)),
+        _ptr(cache.k8), _ptr(cache.v8), _ptr(cache.k_scale), _ptr(cache.v_scale),
         _ptr(kv_idx), _ptr(kv_cnt), _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(dev)))
     return VarlenResult(out, lse, kv_idx, kv_cnt, workspace)
 

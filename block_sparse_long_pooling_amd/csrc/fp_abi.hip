@@ -356,7 +356,7 @@ FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const
     qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = device_status(launch_quant_pool(qa, t, false, st), "quantize + pool");
+    rc = device_status(launch_quant_pool(qa, t, false, false, st), "quantize + pool");
     if (rc) return rc;
     rc = run_scores(p, cu, nullptr, 1, pooled_q, pooled_k, kv_idx, kv_cnt, st);
     return rc ? rc : ok();
@@ -412,17 +412,31 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
 }
 
 namespace {
+// e4m3 pages of fp8 chunked prefill: codes in the layout of the bf16 pages,
+// one fp32 scale per (page, KV head) at the entry of a block's first page.
+struct Fp8Pages {
+    void* k8;
+    void* v8;
+    float* ks;
+    float* vs;
+};
+
 // The paged entries: pooling, selection and attention of a continuous batch.
 // kv_lens NULL: whole prompts; else context lengths (chunked prefill), with
-// the pooled cache pcache (may be NULL) and its reuse flag.
+// the pooled cache pcache (may be NULL) and its reuse flag.  f8 non-NULL:
+// fp8 attention over the e4m3 pages, whose query blocks' codes and scales
+// are written first (chunked prefill; params in fp8).
 int paged_prefill(const fp_params* params, const void* q, const void* k_cache, const void* v_cache, int32_t page_size,
                   int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_q,
-                  const int32_t* kv_lens, int32_t batch, float* pcache, int32_t reuse, int32_t* kv_idx,
-                  int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+                  const int32_t* kv_lens, int32_t batch, float* pcache, int32_t reuse, const Fp8Pages* f8,
+                  int32_t* kv_idx, int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                  void* stream) {
     int rc = check_params(params);
     if (rc) return rc;
     const fp_params& p = *params;
-    if (p.dtype != FP_DTYPE_BF16) return fail(FP_UNSUPPORTED, "the paged entries read bf16 only");
+    if (f8 && p.dtype != FP_DTYPE_FP8_E4M3FN)
+        return fail(FP_INVALID_ARGUMENT, "fp_sparse_prefill_chunked_paged_fp8: params->dtype must be fp8");
+    if (!f8 && p.dtype != FP_DTYPE_BF16) return fail(FP_UNSUPPORTED, "the paged entries read bf16 only");
     SeqTable t;
     rc = build_table(p, cu_q, kv_lens, batch, 1, t);
     if (rc) return rc;
@@ -443,6 +457,10 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
         return fail(FP_INVALID_ARGUMENT, "block_table, kv_idx and kv_cnt must be non-NULL and 4-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(FP_INVALID_ARGUMENT, "lse must be 4-byte aligned");
     if (pcache && !aligned(pcache, 16)) return fail(FP_INVALID_ARGUMENT, "pooled_cache must be 16-byte aligned");
+    if (f8 && (!aligned(f8->k8, 16) || !aligned(f8->v8, 16)))
+        return fail(FP_INVALID_ARGUMENT, "k8_cache and v8_cache must be non-NULL and 16-byte aligned");
+    if (f8 && (!aligned(f8->ks, 4) || !aligned(f8->vs, 4)))
+        return fail(FP_INVALID_ARGUMENT, "k_scale_cache and v_scale_cache must be non-NULL and 4-byte aligned");
     const WsLayout ws = ws_layout(p, t);
     if (!aligned(workspace, 256)) return fail(FP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (workspace_bytes < ws.total)
@@ -462,6 +480,39 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
     a.k = k_cache;
     a.v = v_cache;
     a.q_scale = a.k_scale = a.v_scale = nullptr;
+    if (f8) {
+        // Codes and scales of the chunks' query blocks: Q into the workspace,
+        // K and V into the e4m3 pages (blocks before them were encoded by
+        // earlier calls).
+        uint8_t* q8 = reinterpret_cast<uint8_t*>(wsb + ws.q8);
+        float* qs = reinterpret_cast<float*>(wsb + ws.qs);
+        QuantArgs qa;
+        std::memset(&qa, 0, sizeof qa);
+        qa.src[0] = static_cast<const uint16_t*>(q);
+        qa.src[1] = static_cast<const uint16_t*>(k_cache);
+        qa.src[2] = static_cast<const uint16_t*>(v_cache);
+        qa.codes[0] = q8;
+        qa.codes[1] = static_cast<uint8_t*>(f8->k8);
+        qa.codes[2] = static_cast<uint8_t*>(f8->v8);
+        qa.scale[0] = qs;
+        qa.scale[1] = f8->ks;
+        qa.scale[2] = f8->vs;
+        qa.kv = kv;
+        qa.H[0] = p.num_q_heads;
+        qa.H[1] = qa.H[2] = p.num_kv_heads;
+        qa.D = p.head_dim;
+        qa.B = p.block_size;
+        qa.nB = t.total_qblocks;
+        qa.q_stride = 1;
+        rc = device_status(launch_quant_pool(qa, t, true, true, st), "quantize (chunked)");
+        if (rc) return rc;
+        a.q = q8;
+        a.k = f8->k8;
+        a.v = f8->v8;
+        a.q_scale = qs;
+        a.k_scale = f8->ks;
+        a.v_scale = f8->vs;
+    }
     a.kv_idx = kv_idx;
     a.kv_cnt = kv_cnt;
     a.pk16 = pkv16;
@@ -474,7 +525,8 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
     a.g = p.num_q_heads / p.num_kv_heads;
     a.scale_log2 = (float)(sigma_of(p) * 1.4426950408889634);
     a.correction = p.mean_correction;
-    rc = device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, true, st), "attention (paged)");
+    rc = f8 ? device_status(launch_attn_fp8(a, t, p.head_dim, p.block_size, true, st), "attention (fp8, chunked)")
+            : device_status(launch_attn_bf16(a, t, p.head_dim, p.block_size, true, st), "attention (paged)");
     return rc ? rc : ok();
 }
 }  // namespace
@@ -486,8 +538,8 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged(const fp_params* params, const void
                                              int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
                                              size_t workspace_bytes, void* out, float* lse, void* stream) {
     return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
-                         cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, workspace, workspace_bytes, out,
-                         lse, stream);
+                         cu_seqlens_host, nullptr, batch, nullptr, 0, nullptr, kv_idx, kv_cnt, workspace,
+                         workspace_bytes, out, lse, stream);
 }
 
 // Scratch of the allocation-free paged entry: one copy per GPU, in the
@@ -543,7 +595,7 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged_noalloc(const fp_params* params, co
     rc = scratch_on_current_device(&ws);
     if (rc) return rc;
     return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
-                         cu_seqlens_host, nullptr, batch, nullptr, 0, kv_idx, kv_cnt, ws,
+                         cu_seqlens_host, nullptr, batch, nullptr, 0, nullptr, kv_idx, kv_cnt, ws,
                          (size_t)FP_NOALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
@@ -617,7 +669,7 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const 
     qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = device_status(launch_quant_pool(qa, t, true, st), "quantize + pool (paged)");
+    rc = device_status(launch_quant_pool(qa, t, true, false, st), "quantize + pool (paged)");
     if (rc) return rc;
     rc = run_scores(p, cu_seqlens_host, nullptr, batch, pq, pk, kv_idx, kv_cnt, st);
     if (rc) return rc;
@@ -670,6 +722,24 @@ FP_EXPORT int fp_sparse_prefill_chunked_paged(const fp_params* params, const voi
     if (prefix_pooled != 0 && prefix_pooled != 1) return fail(FP_INVALID_ARGUMENT, "prefix_pooled must be 0 or 1");
     if (prefix_pooled && !pooled_cache) return fail(FP_INVALID_ARGUMENT, "prefix_pooled needs a pooled_cache");
     return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
-                         cu_seqlens_q_host, kv_lens_host, batch, pooled_cache, prefix_pooled, kv_idx, kv_cnt,
+                         cu_seqlens_q_host, kv_lens_host, batch, pooled_cache, prefix_pooled, nullptr, kv_idx, kv_cnt,
+                         workspace, workspace_bytes, out, lse, stream);
+}
+
+FP_EXPORT int fp_sparse_prefill_chunked_paged_fp8(const fp_params* params, const void* q, const void* k_cache,
+                                                  const void* v_cache, int32_t page_size, int32_t num_pages,
+                                                  const int32_t* block_table, int32_t max_pages_per_seq,
+                                                  const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                                  int32_t batch, float* pooled_cache, int32_t prefix_pooled,
+                                                  void* k8_cache, void* v8_cache, float* k_scale_cache,
+                                                  float* v_scale_cache, int32_t* kv_idx, int32_t* kv_cnt,
+                                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                                  void* stream) {
+    if (!kv_lens_host) return fail(FP_INVALID_ARGUMENT, "kv_lens_host is NULL");
+    if (prefix_pooled != 0 && prefix_pooled != 1) return fail(FP_INVALID_ARGUMENT, "prefix_pooled must be 0 or 1");
+    if (prefix_pooled && !pooled_cache) return fail(FP_INVALID_ARGUMENT, "prefix_pooled needs a pooled_cache");
+    const Fp8Pages f8 = {k8_cache, v8_cache, k_scale_cache, v_scale_cache};
+    return paged_prefill(params, q, k_cache, v_cache, page_size, num_pages, block_table, max_pages_per_seq,
+                         cu_seqlens_q_host, kv_lens_host, batch, pooled_cache, prefix_pooled, &f8, kv_idx, kv_cnt,
                          workspace, workspace_bytes, out, lse, stream);
 }

@@ -82,8 +82,9 @@ __device__ __forceinline__ void softmax_update(f32x16* s, float c, float bias, f
 // Normalise O, stage the bf16 tile in LDS (reusing the K tile) and store full
 // rows; write the natural-log sum of exp when requested.
 template <int D, int BLK>
-__device__ __forceinline__ void store_output(const AttnArgs& a, const SeqTable& t, int h, int q0, int nI, int qr,
-                                             int half, float m, float l, const f32x16* o, uint4* lk, int tid) {
+__device__ __forceinline__ void store_output(const AttnArgs& a, const SeqTable& t, int h, int q0, int lo, int nI,
+                                             int qr, int half, float m, float l, const f32x16* o, uint4* lk,
+                                             int tid) {
     using T = Tile<D, BLK>;
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -98,12 +99,12 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, const SeqTable& 
             reinterpret_cast<uint2*>(&lk[qr * T::KCH + (chunk ^ (qr % T::KCH))])[half] = v2;
         }
     __syncthreads();
-    for (int i = tid; i < nI * T::KCH; i += T::NT) {
-        const int row = i / T::KCH, ch = i % T::KCH;
+    for (int i = tid; i < (nI - lo) * T::KCH; i += T::NT) {
+        const int row = lo + i / T::KCH, ch = i % T::KCH;
         *reinterpret_cast<uint4*>(a.out + ((int64_t)(q0 + row) * a.Hq + h) * D + ch * 8) =
             lk[row * T::KCH + (ch ^ (row % T::KCH))];
     }
-    if (a.lse && half == 0 && qr < nI)
+    if (a.lse && half == 0 && qr >= lo && qr < nI)
         a.lse[(int64_t)h * t.total_tokens + q0 + qr] = (m + __log2f(l_tot)) * kLn2;
 }
 

@@ -68,6 +68,16 @@ __device__ __forceinline__ int64_t count_index(const SeqTable& t, int Hq, int b,
 }
 // Row of query block I of request b among all query blocks of the launch.
 __device__ __forceinline__ int qblock_row(const SeqTable& t, int b, int I) { return t.blk_off[b] - t.pre_off[b + 1] + I; }
+// Query block row r -> request (the last one whose rows start at or before r:
+// requests without query blocks are passed over).
+__device__ __forceinline__ int request_of_qblock(const SeqTable& t, int r) {
+    int lo = 0, hi = t.batch - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (t.blk_off[mid] - t.pre_off[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
 
 // Rank (in visiting order) -> (request, item index counted from the request's
 // last item, so that long rows go first).

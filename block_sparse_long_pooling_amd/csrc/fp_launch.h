@@ -42,7 +42,7 @@ struct AttnArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* q_scale;        // fp8: [Hq, total_blocks]
+    const float* q_scale;        // fp8: [Hq, total_qblocks] (by qblock_row)
     const float* k_scale;        // fp8: [Hkv, total_blocks]
     const float* v_scale;
     const int32_t* kv_idx;
@@ -69,12 +69,14 @@ struct QuantArgs {
     KVLayout kv;                 // pages of K and V (used when paged)
     int32_t H[3];                // Hq, Hkv, Hkv
     int32_t groups[3];           // head groups per tensor (set by the launcher)
-    int32_t D, B, nB;            // nB: blocks of all requests
+    int32_t D, B, nB;            // nB: blocks of all requests (chunk mode: query blocks)
     int32_t q_stride;            // Q_bar averages the block's tokens 0, q_stride, 2 q_stride, ...
 };
 
 hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s);
-hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s);
+// chunk: codes and scales of the query blocks of each request's chunk only
+// (paged; nB = t.total_qblocks), no means.
+hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, bool chunk, hipStream_t s);
 hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);
 // Workgroups launch_attn_bf16 uses for these arguments (0 without items, -1

@@ -1,6 +1,9 @@
 // fp8 (OCP e4m3fn) sparse attention over the kept blocks (FlashPrefill V2
 // abstract: FP8 inference).  One workgroup of BLK/32 waves (32 query rows
 // each) per (query block, query head), at least two workgroups per CU.
+// Query blocks are those of a request table: whole prompts, or the chunks of
+// chunked prefill (each chunk at the end of its context, possibly starting
+// inside its first query block).
 //
 // Inputs carry one fp32 scale per (head, block): x = code * scale.  Scores
 // come from v_mfma_scale_f32_32x32x64_f8f6f4 on the raw codes and are scaled
@@ -246,28 +249,36 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     const int h = xcd_head(blockIdx.x % a.Hq, a.Hq);
     int b, local;
     item_of(t, rank, b, local);
-    const int nb = seq_blocks(t, b);                   // whole sequences only: no prefix blocks
+    const int nb = seq_blocks(t, b);
+    const int first = first_block(t, b);               // query blocks are first .. nb-1
     const int I = nb - 1 - local;
     const int tok0 = t.tok_off[b];
     const int len = context_len(t, b, BLK);
-    const int q0 = tok0 + I * BLK;
+    // Row r of the block is query row q0 + r; a chunk that starts inside its
+    // first block has no rows before lo there.
+    const int phase = chunk_phase(t, b, BLK);
+    const int q0 = tok0 + (I - first) * BLK - phase;
+    const int lo = I == first ? phase : 0;
     const int nI = min(BLK, len - I * BLK);
     const int hk = h / a.g;
-    const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, 0);
-    const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, 0)];
+    const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, first);
+    const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)];
     const int qr = 32 * w + col;
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
     const uint8_t* k8 = static_cast<const uint8_t*>(a.k);
     const uint8_t* v8 = static_cast<const uint8_t*>(a.v);
     const int64_t sblk = (int64_t)t.blk_off[b];
-    const float sq = a.q_scale[(int64_t)h * t.total_blocks + sblk + I];
-    const uint8_t* qrow = q8 + ((int64_t)(q0 + qr) * a.Hq + h) * D;
+    const float sq = a.q_scale[(int64_t)h * t.total_qblocks + qblock_row(t, b, I)];
+    // Rows outside lo .. nI-1 hold zero queries (their outputs are not
+    // stored); their address is clamped to a row of the block.
+    const bool qok = qr >= lo && qr < nI;
+    const uint8_t* qrow = q8 + ((int64_t)(q0 + min(max(qr, lo), nI - 1)) * a.Hq + h) * D;
 
     i32x8 qf[D / 64];
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) {
         uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-        if (qr < nI) {
+        if (qok) {
             x0 = *reinterpret_cast<const uint4*>(qrow + 32 * half + 64 * kk);
             x1 = *reinterpret_cast<const uint4*>(qrow + 32 * half + 64 * kk + 16);
         }
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             uint2 x = make_uint2(0, 0);
-            if (qr < nI) x = *reinterpret_cast<const uint2*>(qrow + 8 * half + 16 * kk);
+            if (qok) x = *reinterpret_cast<const uint2*>(qrow + 8 * half + 16 * kk);
             const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, false);
             const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, true);
             const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, false);
@@ -433,7 +444,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, qb, reinterpret_cast<char*>(lk),
                                reinterpret_cast<char*>(lv), kept_bits, tid, col, half, a.scale_log2, m, l, o);
     }
-    store_output<D, BLK>(a, t, h, q0, nI, qr, half, m, l, o, lk, tid);
+    store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, lk, tid);
 }
 
 template <int D, int BLK>

@@ -7,6 +7,13 @@
 // Blocks are those of a request table (one sequence, or a batch whose K and
 // V rows may live in a paged cache: codes then go to the same place in an
 // e4m3 page pool, and each block's scale to the entry of its first page).
+// In chunk mode (chunked prefill over the paged cache) the grid covers only
+// the query blocks of each request's chunk and forms codes and scales, no
+// means (the pooling kernel forms those): K and V of such a block are
+// re-encoded whole from the bf16 pages, the tokens before the chunk
+// included, so a block that an earlier chunk left partial ends up encoded as
+// a prefill of the whole context would encode it; Q of the block holds only
+// the chunk's queries in it.
 // A workgroup (8 waves) owns one block of one tensor for a group of heads
 // whose chunks of 8 bf16 make 32 chunks per token row (two heads at d 128,
 // four at d 64), i.e. 512 contiguous bytes.  Lane l of wave w handles chunk
@@ -35,7 +42,7 @@ constexpr int kWaves = 8;
 
 // Six waves per SIMD (three workgroups per CU): more loads in flight, at
 // the cost of a 16-byte spill.
-template <int D, int B, bool PAGED>
+template <int D, int B, bool PAGED, bool CHUNK>
 __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqTable t) {
     constexpr int CPH = D / 8;             // chunks per head
     constexpr int HPG = 32 / CPH;          // heads per workgroup
@@ -43,7 +50,7 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     __shared__ float psum[kWaves][32][8];
     __shared__ float pmax[kWaves][HPG];
 
-    const int J = blockIdx.x;                       // block of all requests
+    const int J = blockIdx.x;                       // block of all requests (chunk mode: query block row)
     int g = blockIdx.y, ts = 0;
     if (g >= a.groups[0]) {
         g -= a.groups[0];
@@ -59,16 +66,31 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     const int hl = ch / CPH;               // head within the group
     const int h = g * HPG + hl;
     const bool hv = h < H;
-    const int b = request_of_block(t, J);
-    const int I = J - t.blk_off[b];                 // block of request b
+    int b, I;                                       // request, block of request b
+    if (CHUNK) {
+        b = request_of_qblock(t, J);
+        I = first_block(t, b) + J - (t.blk_off[b] - t.pre_off[b]);
+    } else {
+        b = request_of_block(t, J);
+        I = J - t.blk_off[b];
+    }
     const int t0 = I * B;
     const int n = min(B, context_len(t, b, B) - t0);
+    // Q rows of a chunk: tokens lo .. n-1 of the block, query row q0 + tok
+    // (the chunk may start inside its first block).
+    int lo = 0;
+    int64_t q0 = (int64_t)t.tok_off[b] + t0;
+    if (CHUNK && ts == 0) {
+        const int first = first_block(t, b), ph = chunk_phase(t, b, B);
+        lo = I == first ? ph : 0;
+        q0 = (int64_t)t.tok_off[b] + (I - first) * B - ph;
+    }
     const bool pg = PAGED && ts > 0;                // K and V rows live in pages
     const int64_t row = (int64_t)H * D;
     const int64_t col = (int64_t)g * HPG * D + ch * 8;
-    // Packed rows: offsets from the block's first row; paged rows: from the
+    // Packed rows: offsets from the block's row 0; paged rows: from the
     // pool's start.
-    const int64_t base = pg ? col : ((int64_t)t.tok_off[b] + t0) * row + col;
+    const int64_t base = pg ? col : q0 * row + col;
     const KVLayout kv = a.kv;
     // Row of token tok of this block relative to the base (-1: a page id out
     // of range, read as zeros and not written).
@@ -96,9 +118,9 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int tok = 2 * kWaves * s + 2 * w + hf;
-            const int64_t r = row_of(min(tok, n - 1));
-            x[s] = (hv && tok < n && r >= 0) ? *reinterpret_cast<const uint4*>(src + r * row)
-                                            : make_uint4(0, 0, 0, 0);
+            const int64_t r = row_of(min(max(tok, lo), n - 1));
+            x[s] = (hv && tok >= lo && tok < n && r >= 0) ? *reinterpret_cast<const uint4*>(src + r * row)
+                                                          : make_uint4(0, 0, 0, 0);
         }
     }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -139,24 +161,26 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     const float sc = am > 0.f ? __fdiv_rn(am, kE4M3Max) : 1.f;
     const float ry = __fdiv_rn(1.f, sc);
     if (w == 0 && hf == 0) {
-        float m[8];
+        if (!CHUNK) {   // means: the pooling kernel forms them in chunk mode
+            float m[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float t = psum[0][ch][i];
+            for (int i = 0; i < 8; ++i) {
+                float t = psum[0][ch][i];
 #pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2) t += psum[w2][ch][i];
-            m[i] = t / (float)((n + stride - 1) / stride);
+                for (int w2 = 1; w2 < kWaves; ++w2) t += psum[w2][ch][i];
+                m[i] = t / (float)((n + stride - 1) / stride);
+            }
+            const int64_t off = ((int64_t)h * a.nB + J) * D + (ch % CPH) * 8;
+            float* dst = ts == 0 ? a.pq : (ts == 1 ? a.pk : nullptr);
+            if (dst) {
+                reinterpret_cast<float4*>(dst + off)[0] = make_float4(m[0], m[1], m[2], m[3]);
+                reinterpret_cast<float4*>(dst + off)[1] = make_float4(m[4], m[5], m[6], m[7]);
+            }
+            if (ts > 0 && a.pkv16)
+                *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
+                    make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
+                               pack_bf16(m[6], m[7]));
         }
-        const int64_t off = ((int64_t)h * a.nB + J) * D + (ch % CPH) * 8;
-        float* dst = ts == 0 ? a.pq : (ts == 1 ? a.pk : nullptr);
-        if (dst) {
-            reinterpret_cast<float4*>(dst + off)[0] = make_float4(m[0], m[1], m[2], m[3]);
-            reinterpret_cast<float4*>(dst + off)[1] = make_float4(m[4], m[5], m[6], m[7]);
-        }
-        if (ts > 0 && a.pkv16)
-            *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
-                make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
-                           pack_bf16(m[6], m[7]));
         if (ch % CPH == 0) {
             if (pg) {
                 // Paged K and V: the scale goes with the page of the block's first token.
@@ -182,7 +206,7 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int tok = 2 * kWaves * s + 2 * w + hf;
-        if (!full && tok >= n) continue;
+        if (!full && (tok < lo || tok >= n)) continue;
         const uint32_t wd[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
         uint32_t out[2];
 #pragma unroll
@@ -207,25 +231,28 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
 }
 
 template <int D, int B>
-hipError_t launch_t(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+hipError_t launch_t(const QuantArgs& a, const SeqTable& t, bool paged, bool chunk, hipStream_t s) {
     constexpr int HPG = 32 / (D / 8);
     QuantArgs b = a;
     for (int i = 0; i < 3; ++i) b.groups[i] = (a.H[i] + HPG - 1) / HPG;
     const dim3 grid(a.nB, b.groups[0] + b.groups[1] + b.groups[2]);
-    if (paged)
-        hipLaunchKernelGGL((k_quant_pool<D, B, true>), grid, dim3(64 * kWaves), 0, s, b, t);
+    if (chunk)
+        hipLaunchKernelGGL((k_quant_pool<D, B, true, true>), grid, dim3(64 * kWaves), 0, s, b, t);
+    else if (paged)
+        hipLaunchKernelGGL((k_quant_pool<D, B, true, false>), grid, dim3(64 * kWaves), 0, s, b, t);
     else
-        hipLaunchKernelGGL((k_quant_pool<D, B, false>), grid, dim3(64 * kWaves), 0, s, b, t);
+        hipLaunchKernelGGL((k_quant_pool<D, B, false, false>), grid, dim3(64 * kWaves), 0, s, b, t);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
+hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, bool chunk, hipStream_t s) {
     if (a.nB == 0) return hipSuccess;
-    if (a.D == 128 && a.B == 128) return launch_t<128, 128>(a, t, paged, s);
-    if (a.D == 128 && a.B == 64) return launch_t<128, 64>(a, t, paged, s);
-    if (a.D == 64 && a.B == 128) return launch_t<64, 128>(a, t, paged, s);
-    if (a.D == 64 && a.B == 64) return launch_t<64, 64>(a, t, paged, s);
+    if (chunk && (!paged || a.nB != t.total_qblocks)) return hipErrorInvalidValue;
+    if (a.D == 128 && a.B == 128) return launch_t<128, 128>(a, t, paged, chunk, s);
+    if (a.D == 128 && a.B == 64) return launch_t<128, 64>(a, t, paged, chunk, s);
+    if (a.D == 64 && a.B == 128) return launch_t<64, 128>(a, t, paged, chunk, s);
+    if (a.D == 64 && a.B == 64) return launch_t<64, 64>(a, t, paged, chunk, s);
     return hipErrorInvalidValue;
 }

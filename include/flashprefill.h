@@ -274,7 +274,7 @@ int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const void* q,
  *   workspace: at least the bytes fp_chunked_sizes gives; contents on return
  *     are unspecified.
  *   out [T,Hq,d] bf16, lse [Hq,T] fp32 or NULL (rows of the chunks).
- * bf16 only.  batch <= FP_MAX_BATCH.
+ * bf16 (fp8 attention: fp_sparse_prefill_chunked_paged_fp8).  batch <= FP_MAX_BATCH.
  */
 int fp_sparse_prefill_chunked_paged(const fp_params* params, const void* q,
                                     const void* k_cache, const void* v_cache,
@@ -286,10 +286,49 @@ int fp_sparse_prefill_chunked_paged(const fp_params* params, const void* q,
                                     void* workspace, size_t workspace_bytes,
                                     void* out, float* lse, void* stream);
 
-/* Sizes for fp_sparse_prefill_chunked_paged (host only): kv_idx entries,
- * kv_cnt entries and workspace bytes, written where the pointers are not
- * NULL.  Returns FP_OK or the error the call itself would give for these
- * lengths. */
+/*
+ * Chunked prefill with fp8 attention (FlashPrefill V2 abstract: FP8
+ * inference, and the attention backend with paged KV and continuous
+ * batching of the authors' post).  The chunk, its context, the pooled cache
+ * and the lists are those of fp_sparse_prefill_chunked_paged: pooling and
+ * selection read the bf16 pages.  Attention reads e4m3 pages kept beside
+ * them, in the form fp_sparse_prefill_varlen_paged_fp8 writes: codes in the
+ * layout of the bf16 pages and one fp32 scale per (page, KV head) at the
+ * entry of the page that holds a block's first token.  The call encodes the
+ * query blocks first .. nb-1 of each request (blockwise absmax / 448 scales,
+ * OCP E4M3 codes): K and V of those blocks whole, from the bf16 pages (the
+ * tokens of block first that precede the chunk included), Q over the chunk's
+ * queries in each block (workspace).  Blocks 0 .. first-1 are read as they
+ * stand, so they must hold the codes of earlier calls of this entry (or of
+ * fp_sparse_prefill_varlen_paged_fp8) over the same tokens.  The result then
+ * equals fp8 attention over the whole context's blockwise codes, with the
+ * chunk's Q blocks encoded over the chunk's queries.
+ *   q, k_cache, v_cache, page_size, num_pages, block_table,
+ *   max_pages_per_seq, cu_seqlens_q_host, kv_lens_host, batch, pooled_cache,
+ *   prefix_pooled, kv_idx, kv_cnt, out, lse: as for
+ *   fp_sparse_prefill_chunked_paged.
+ *   k8_cache, v8_cache: uint8 [num_pages, page_size, Hkv, d], 16-byte aligned;
+ *     k_scale_cache, v_scale_cache: fp32 [num_pages, Hkv].  Read and written.
+ *   workspace: at least the bytes fp_chunked_sizes gives for these params
+ *     (with dtype fp8 it includes the Q codes and scales).
+ * FP_INVALID_ARGUMENT when params->dtype is not fp8.
+ */
+int fp_sparse_prefill_chunked_paged_fp8(const fp_params* params, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        int32_t page_size, int32_t num_pages,
+                                        const int32_t* block_table, int32_t max_pages_per_seq,
+                                        const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host,
+                                        int32_t batch, float* pooled_cache, int32_t prefix_pooled,
+                                        void* k8_cache, void* v8_cache,
+                                        float* k_scale_cache, float* v_scale_cache,
+                                        int32_t* kv_idx, int32_t* kv_cnt,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* out, float* lse, void* stream);
+
+/* Sizes for fp_sparse_prefill_chunked_paged and
+ * fp_sparse_prefill_chunked_paged_fp8 (host only): kv_idx entries, kv_cnt
+ * entries and workspace bytes, written where the pointers are not NULL.
+ * Returns FP_OK or the error the call itself would give for these lengths. */
 int fp_chunked_sizes(const fp_params* params, const int32_t* cu_seqlens_q_host,
                      const int32_t* kv_lens_host, int32_t batch,
                      int64_t* index_capacity, int64_t* count_entries, size_t* workspace_bytes);

@@ -267,6 +267,35 @@ def test_fp8_paged_validation_and_workspace():
     assert call(p8, ws=ws16) == fp.FP_WORKSPACE_TOO_SMALL               # the bf16 size is not enough
 
 
+def test_chunked_fp8_validation_and_workspace():
+    l = fp.lib()
+    p16, p8 = _p(), _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    a256 = lambda x: (x + 255) // 256 * 256
+    # chunk of 200 queries from 800 (query blocks 6, 7): Q codes of 200 rows, Q scales of 2 blocks
+    _, _, ws16 = fp.fp_chunked_sizes(p16, [0, 200], [1000])
+    _, _, ws8 = fp.fp_chunked_sizes(p8, [0, 200], [1000])
+    assert ws8 == ws16 + a256(200 * 32 * 128) + a256(2 * 32 * 4)
+
+    def call(p, cu=(0, 200), kv=(1000,), k8=FAKE, ks=FAKE, ws=1 << 30, pooled=None, reuse=0, kv_null=False):
+        c = (ctypes.c_int32 * len(cu))(*cu)
+        k = None if kv_null else (ctypes.c_int32 * len(kv))(*kv)
+        return l.fp_sparse_prefill_chunked_paged_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, 64, 100, FAKE, 64, c, k,
+                                                     len(cu) - 1, pooled, reuse, k8, FAKE, ks, FAKE, FAKE, FAKE,
+                                                     ctypes.c_void_p(1 << 24), ws, FAKE, None, None)
+    assert call(p16) == fp.FP_INVALID_ARGUMENT                          # bf16 params
+    assert "fp8" in l.fp_last_error().decode()
+    assert call(p8, kv_null=True) == fp.FP_INVALID_ARGUMENT
+    assert call(p8, reuse=1) == fp.FP_INVALID_ARGUMENT                  # reuse without a pooled cache
+    assert call(p8, cu=(0, 1200)) == fp.FP_INVALID_ARGUMENT             # more queries than context
+    assert call(p8, k8=None) == fp.FP_INVALID_ARGUMENT                  # no fp8 pages
+    assert call(p8, k8=MISALIGNED) == fp.FP_INVALID_ARGUMENT
+    assert call(p8, ks=None) == fp.FP_INVALID_ARGUMENT                  # no scale cache
+    assert call(p8, ws=ws16) == fp.FP_WORKSPACE_TOO_SMALL               # the bf16 size is not enough
+    assert call(_p(dtype=fp.FP_DTYPE_FP8_E4M3FN, query_probes=16)) == fp.FP_UNSUPPORTED   # probes, unaligned
+    assert call(p8, cu=(0, 0, 0), kv=(256, 512)) == fp.FP_OK            # no queries: nothing to do
+    assert l.fp_last_error() == b""
+
+
 def test_noalloc_entry_rejects_batches_beyond_its_scratch():
     """The allocation-free entry checks the pooled-mean scratch it needs
     against its fixed array on the host, before any device work."""
