@@ -1,7 +1,10 @@
 """Build libflashprefill.so (HIP, gfx950) in-tree with hipcc.
 
 Every source is compiled on each call (no staleness check), four at a time,
-then linked into one shared library next to this file.
+then linked into one shared library next to this file.  build_serial() makes
+the debug variant libflashprefill_serial.so, whose kernels fill an LDS tile
+buffer only after every read of the previous tile (FP_SERIAL_DMA=1): the race
+check compares its results with the pipelined library's bit for bit.
 """
 from __future__ import annotations
 
@@ -15,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashprefill.so")
+SERIAL_LIB = os.path.join(PKG, "libflashprefill_serial.so")
 SOURCES = ["fp_abi.hip", "k_pool.hip", "k_quant.hip", "k_select.hip", "k_attn.hip", "k_attn_fp8.hip"]
 ARCH = "gfx950"
 
@@ -36,12 +40,12 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def _build_lib(lib: str, objdir: str, defines, verbose: bool) -> str:
+    os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        out = _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        out = _run([HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, out
 
     with ThreadPoolExecutor(max_workers=4) as ex:
@@ -49,11 +53,20 @@ def build(verbose: bool = False) -> str:
     for obj, out in results:
         if verbose and out.strip():
             print(out, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fvisibility=hidden", "-o", tmp,
           *[o for o, _ in results]])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    return _build_lib(LIB, OBJ, [], verbose)
+
+
+def build_serial(verbose: bool = False) -> str:
+    """The debug variant with serialised LDS tile fills (same entry points)."""
+    return _build_lib(SERIAL_LIB, os.path.join(OBJ, "serial"), ["-DFP_SERIAL_DMA=1"], verbose)
 
 
 ASAN_DIR = os.path.join(PKG, "_build", "asan")

@@ -3,6 +3,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug build (-DFP_SERIAL_DMA=1): every fill of an LDS tile buffer (DMA or
+// register-staged) is issued only after every wave has finished reading the
+// tile before it, so no fill overlaps compute.  The arithmetic and its order
+// are unchanged, so results must equal the pipelined build's bit for bit; a
+// difference would expose a fill racing with a read.
+#ifndef FP_SERIAL_DMA
+#define FP_SERIAL_DMA 0
+#endif
+constexpr bool kSerialFill = FP_SERIAL_DMA != 0;
+
 #define FP_TABLE_MAX 128   // requests per call (kernel-argument tables)
 #define FP_MAX_BLOCKS 8192 // query blocks per request (kept-block bitmap in LDS)
 

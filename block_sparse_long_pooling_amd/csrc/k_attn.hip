@@ -208,18 +208,21 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA for tile J is done
         lds_barrier();                                   // ... every thread's; the other buffers are free
         int Jn1;
-        if (PAGED) {
-            Jn1 = Jn;
-            act_next = actn;
-            if (Jn1 < kCorr)
-                issue_kept(cur, Jn1, knext, vnext, pgn);
-            else if (Jn1 != INT_MAX)
-                issue(cur, Jn1, knext, vnext);
-            if (Jn1 != INT_MAX) ahead(cur);
-        } else {
-            Jn1 = next_tile(cur, act_next);
-            if (Jn1 != INT_MAX) issue(cur, Jn1, knext, vnext);
-        }
+        auto prefetch = [&]() {
+            if (PAGED) {
+                Jn1 = Jn;
+                act_next = actn;
+                if (Jn1 < kCorr)
+                    issue_kept(cur, Jn1, knext, vnext, pgn);
+                else if (Jn1 != INT_MAX)
+                    issue(cur, Jn1, knext, vnext);
+                if (Jn1 != INT_MAX) ahead(cur);
+            } else {
+                Jn1 = next_tile(cur, act_next);
+                if (Jn1 != INT_MAX) issue(cur, Jn1, knext, vnext);
+            }
+        };
+        if (!kSerialFill) prefetch();
         if ((act >> hs) & 1) {
             const bool corr = J >= kCorr;
             // Correction tile: bit j of skip[sub] <=> pooled block ct*BLK + 32 sub + j
@@ -272,6 +275,10 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
             half_tile(std::integral_constant<int, 0>());
             if (G::NSUB > SH) half_tile(std::integral_constant<int, (G::NSUB > SH ? SH : 0)>());
         }
+        if (kSerialFill) {
+            lds_barrier();                               // every wave is done with tile J
+            prefetch();
+        }
         J = Jn1;
         act = act_next;
     };
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
             nxt.setup(a, t, nidx, hs);
             zero_bits(nxt);
             Jn0 = nxt.u.next(actn0);                     // a kept block (lists are never empty)
-            if (Jn0 != INT_MAX) issue(nxt, Jn0, kb1, vb1);
+            if (!kSerialFill && Jn0 != INT_MAX) issue(nxt, Jn0, kb1, vb1);
         }
 
         // Epilogue: normalise, stage each head's bf16 tile in LDS (kb0 for the
@@ -354,6 +361,10 @@ __global__ __launch_bounds__(64 * HP * (BLK / 32)) void k_attn_bf16(AttnArgs a, 
         }
         if (a.lse && half == 0 && qr >= cur.lo && qr < cur.nI)
             a.lse[(int64_t)cur.h * t.total_tokens + cur.q0 + qr] = (m + __log2f(l_tot)) * kLn2;
+        if (kSerialFill) {
+            lds_barrier();                               // the staged rows are read
+            if (has_next && Jn0 != INT_MAX) issue(nxt, Jn0, kb1, vb1);
+        }
         if (!has_next) break;
         cur = nxt;
         idx = nidx;

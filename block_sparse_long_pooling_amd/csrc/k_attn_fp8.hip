@@ -213,7 +213,7 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
         lds_barrier();                                   // ... every thread's; the other buffer is free
         const int nxt = next_step(cur);
-        if (nxt < nht) issue(nxt, bnext);
+        if (!kSerialFill && nxt < nht) issue(nxt, bnext);
         uint32_t sk[NS];
         skips(cur, sk);
         qk<D, BLK, 1, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
@@ -226,6 +226,10 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
         }
         softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
         pv<D, BLK, 1, 0, NS>(bcur + HALF, pk, lane, o);
+        if (kSerialFill) {
+            lds_barrier();                               // every wave is done with step cur
+            if (nxt < nht) issue(nxt, bnext);
+        }
         cur = nxt;
     };
     while (cur < nht) {
@@ -374,22 +378,25 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         lds_barrier();                                   // ... every thread's; the other buffer is free
         int Jn = 0;
         float skn = 1.f, svn = 1.f;
-        if (PAGED) {
-            // The window move waits on memory; nothing else is in flight yet.
-            if (it + 2 < cnt && it + 2 - wbase == 64) load_window(it + 2);
-            Jn = Ja;
-            skn = ska;
-            svn = sva;
-            if (it + 1 < cnt) issue8_pg(Jn, bnext, pga);
-            if (it + 2 < cnt) {
-                from_window(it + 2, Ja, ska, sva);
-                load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+        auto prefetch = [&]() {
+            if (PAGED) {
+                // The window move waits on memory; nothing else is in flight yet.
+                if (it + 2 < cnt && it + 2 - wbase == 64) load_window(it + 2);
+                Jn = Ja;
+                skn = ska;
+                svn = sva;
+                if (it + 1 < cnt) issue8_pg(Jn, bnext, pga);
+                if (it + 2 < cnt) {
+                    from_window(it + 2, Ja, ska, sva);
+                    load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+                }
+            } else if (it + 1 < cnt) {
+                if (it + 1 - wbase == 64) load_window(it + 1);
+                from_window(it + 1, Jn, skn, svn);
+                issue8(Jn, bnext);
             }
-        } else if (it + 1 < cnt) {
-            if (it + 1 - wbase == 64) load_window(it + 1);
-            from_window(it + 1, Jn, skn, svn);
-            issue8(Jn, bnext);
-        }
+        };
+        if (!kSerialFill) prefetch();
         qk8<D, 0, T::NSUB>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
         if (J == I) {
 #pragma unroll
@@ -405,6 +412,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         f32x16 lsum = {};
         pv8<D, 0>(bcur + VOFF, ph, pl, lane, o, lsum);
         if (BLK == 128) pv8<D, (BLK == 128 ? 1 : 0)>(bcur + VOFF, ph + 2, pl + 2, lane, o, lsum);
+        if (kSerialFill) {
+            lds_barrier();                               // every wave is done with tile it
+            prefetch();
+        }
         // Every lane of a query pair got the whole row sum; the lower half
         // keeps it (l is summed over the pair at the end).
         l += half ? 0.f : lsum[0];

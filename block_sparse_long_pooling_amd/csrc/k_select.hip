@@ -284,8 +284,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
             sg.load(a.pk, krow0, tile_of(2 * (p + 2) + sg.cg), ncol, xfree);
             const int ct = tile_of(2 * p + cg);
             if (ct < ntile_w) visit(ct, stage[p & 1][cg]);
-            if (p + 1 < nstep) sg.store(stage[(p + 1) & 1], xnext);
+            if (!kSerialFill && p + 1 < nstep) sg.store(stage[(p + 1) & 1], xnext);
             lds_barrier();
+            if (kSerialFill) {                           // fill only after every read of this step
+                if (p + 1 < nstep) sg.store(stage[(p + 1) & 1], xnext);
+                lds_barrier();
+            }
         };
         for (int p = 0; p < nstep; p += 2) {
             step(p, x1, x0);
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
         // products run.
         if (vis) {
             s = tile_scores<D>(qh, ql, stage[p & 1][cg], rho, half);
-            if (p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
+            if (!kSerialFill && p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
             if (masked(ct)) {
                 const uint32_t cm = colmask(ct);
 #pragma unroll
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
                 for (int r = 0; r < 16; ++r) tm = fmaxf(tm, s[r]);
             }
             tm = max_halves(tm);
-        } else if (p + 1 < nstep1) {
+        } else if (!kSerialFill && p + 1 < nstep1) {
             sg.store(stage[(p + 1) & 1], xnext);
         }
         if (half == 0) xch[cg][slot] = tm;
@@ -364,6 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_select(SelArgs a, SeqTable t) {
             nz = nz || w != 0u;
         }
         lds_barrier();
+        if (kSerialFill) {                               // fill only after every read of this step
+            if (p + 1 < nstep1) sg.store(stage[(p + 1) & 1], xnext);
+            lds_barrier();
+        }
     };
     for (int p = 0; p < nstep1; p += 2) {
         step1(p, x1, x0);

@@ -363,11 +363,14 @@ def select_blocks_chunked(q, k, v, block: int, alpha: float, sigma: Optional[flo
 
 
 def sparse_attention_chunked(q, k, v, sel: Selection, correction: bool, sigma: Optional[float] = None,
-                             keep: Optional[np.ndarray] = None):
+                             keep: Optional[np.ndarray] = None,
+                             pairs: Optional[Iterable[Tuple[int, int]]] = None):
     """Attention of a chunk (see select_blocks_chunked): o [q_len, Hq, d], lse [Hq, q_len].
 
     Row r of the chunk is position kv_len - q_len + r and sees every key at or
-    before it in the kept blocks, plus the correction entries.
+    before it in the kept blocks, plus the correction entries.  ``pairs``
+    (head, i) limits the work to query blocks first + i of those heads; other
+    rows stay NaN.
     """
     q_len, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -379,15 +382,16 @@ def sparse_attention_chunked(q, k, v, sel: Selection, correction: bool, sigma: O
     P0 = k.shape[0] - q_len
     o = np.full((q_len, Hq, d), np.nan)
     lse = np.full((Hq, q_len), np.nan)
-    for h in range(Hq):
-        for i in range(keep.shape[1]):
-            I = sel.first + i
-            z, vals = block_entries(q, k, v, keep[h, i], h, I, block, sigma, g, correction,
-                                    sel.k_bar, sel.v_bar, q_offset=P0)
-            M, w, l = softmax_rows(z)
-            r0, r1 = max(I * block, P0) - P0, min(k.shape[0], (I + 1) * block) - P0
-            o[r0:r1, h] = (w @ vals) / l[:, None]
-            lse[h, r0:r1] = M + np.log(l)
+    if pairs is None:
+        pairs = [(h, i) for h in range(Hq) for i in range(keep.shape[1])]
+    for h, i in pairs:
+        I = sel.first + i
+        z, vals = block_entries(q, k, v, keep[h, i], h, I, block, sigma, g, correction,
+                                sel.k_bar, sel.v_bar, q_offset=P0)
+        M, w, l = softmax_rows(z)
+        r0, r1 = max(I * block, P0) - P0, min(k.shape[0], (I + 1) * block) - P0
+        o[r0:r1, h] = (w @ vals) / l[:, None]
+        lse[h, r0:r1] = M + np.log(l)
     return o, lse
 
 

@@ -236,6 +236,98 @@ def test_paged_batch8_chunked_last4096_full_size():
     print(f"  {cu_new[-1]} new rows and {cu_pre[-1]} prefix rows equal the whole-prompt rows", flush=True)
 
 
+def test_paged_batch8_chunked_fp8_last4096_full_size():
+    """The fp8 chunked entry in the configuration the benchmark times: the
+    e4m3 pages of the whole prompts come from the fp8 paged entry, the
+    prefix means from the pooled cache of a bf16 prefix call, and the timed
+    call encodes the last 4096 tokens of each context.  The chunks' e4m3
+    blocks equal the oracle's codes bit for bit, the lists equal the bf16
+    chunked entry's, and sampled (head, query block) outputs and LSE match
+    the oracle's attention on the dequantized codes under those lists."""
+    w = synth.WORKLOADS["paged_batch8"]
+    Hq, Hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print("generating paged_batch8 (fp8 chunked)", flush=True)
+    pb = synth.workload_inputs(w)
+    page = pb.k_cache.shape[1]
+    alpha = w.alphas[0]
+    p16 = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True)
+    p8 = fp.make_params(Hq, Hkv, d, B, alpha, mean_correction=True, dtype=fp.FP_DTYPE_FP8_E4M3FN)
+    qd, kc, vc, bt = (x.to(dev()) for x in (pb.q, pb.k_cache, pb.v_cache, pb.block_table))
+    _, c8 = fp.fp_sparse_prefill_varlen_paged_fp8(p8, qd, kc, vc, bt, pb.cu_seqlens)
+    cu = [int(x) for x in pb.cu_seqlens]
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    cut = [max(0, L - 4096) for L in lens]
+    cache = fp.alloc_pooled_cache(p16, kc.shape[0], dev())
+    q_pre = torch.cat([qd[cu[b]:cu[b] + cut[b]] for b in range(len(lens))])
+    cu_pre = [0]
+    for c_ in cut:
+        cu_pre.append(cu_pre[-1] + c_)
+    fp.fp_sparse_prefill_chunked_paged(p16, q_pre, kc, vc, bt, cu_pre, cut, pooled_cache=cache)
+    q_new = torch.cat([qd[cu[b] + cut[b]:cu[b + 1]] for b in range(len(lens))])
+    cu_new = [0]
+    for b in range(len(lens)):
+        cu_new.append(cu_new[-1] + lens[b] - cut[b])
+    res = fp.fp_sparse_prefill_chunked_paged_fp8(p8, q_new, kc, vc, bt, cu_new, lens, c8, pooled_cache=cache,
+                                                 prefix_pooled=True, return_lse=True)
+    r16 = fp.fp_sparse_prefill_chunked_paged(p16, q_new, kc, vc, bt, cu_new, lens, pooled_cache=cache,
+                                             prefix_pooled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(res.kv_cnt, r16.kv_cnt)
+    out = res.out.float().cpu().numpy()
+    lse = res.lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    idx8, idx16, cnt = res.kv_idx.cpu().numpy(), r16.kv_idx.cpu().numpy(), res.kv_cnt.cpu().numpy()
+    k8, v8 = c8.k8.cpu(), c8.v8.cpu()
+    ks, vs = c8.k_scale.cpu().numpy(), c8.v_scale.cpu().numpy()
+    tri = lambda n: n * (n + 1) // 2
+    io = co = 0
+    for b, (L, P0) in enumerate(zip(lens, cut)):
+        nb, first = (L + B - 1) // B, P0 // B
+        nq, rowsz = nb - first, tri(nb) - tri(first)
+        qb, kb, vb = (t.float().numpy() for t in pb.requests[b])
+        pages = pb.block_table[b, :(L + page - 1) // page].tolist()
+        # lists: equal to the bf16 chunked entry's, read into a mask
+        mask = np.zeros((Hq, nq, nb), dtype=bool)
+        for h in range(Hq):
+            for i in range(nq):
+                c = int(cnt[co + h * nq + i])
+                s0 = io + h * rowsz + tri(first + i) - tri(first)
+                assert np.array_equal(idx8[s0:s0 + c], idx16[s0:s0 + c]), (b, h, i)
+                mask[h, i, idx8[s0:s0 + c]] = True
+        ref = O.select_blocks_chunked(qb[P0:], kb, vb, B, alpha)
+        outside, inside, band = compare_mask(mask, ref)
+        assert outside == 0, (b, outside)
+        # the chunk's blocks in the e4m3 pages, against the oracle's codes
+        deq = {}
+        pairs = _sample_pairs(Hq, nq, 8, seed=70 + b)
+        need = sorted({J for h, i in pairs for J in np.nonzero(mask[h, i])[0]} | set(range(first, nb)))
+        for name, pool, sc, x in (("k", k8, ks, kb), ("v", v8, vs, vb)):
+            full = np.full(x.shape, np.nan)
+            for J in need:                                # blockwise codes: each block on its own
+                c_ref, s_ref = O.quantize_fp8_blockwise(x[J * B:(J + 1) * B], B)
+                if J >= first:
+                    r0 = J * B
+                    got = pool[pages[r0 // page:(r0 + B + page - 1) // page]].reshape(-1, Hkv, d)
+                    assert np.array_equal(got[:min(B, L - r0)].numpy(), c_ref), (b, name, J)
+                    assert np.array_equal(sc[pages[r0 // page]], s_ref[:, 0]), (b, name, J)
+                full[J * B:(J + 1) * B] = O.dequantize_blockwise(
+                    synth.fp8_codes_to_float(torch.from_numpy(c_ref)).numpy(), s_ref, B)
+            deq[name] = full
+        qc, qs = O.quantize_fp8_chunk(qb[P0:], B, P0)
+        q_deq = O.dequantize_chunk(synth.fp8_codes_to_float(torch.from_numpy(qc)).numpy(), qs, B, P0)
+        o_ref, lse_ref = O.sparse_attention_chunked(q_deq, deq["k"], deq["v"], ref, True, keep=mask, pairs=pairs)
+        worst = lworst = 0.0
+        for h, i in pairs:
+            r0, r1 = i * B, min(L - P0, (i + 1) * B)
+            worst = max(worst, float(np.abs(out[cu_new[b] + r0:cu_new[b] + r1, h] - o_ref[r0:r1, h]).max()))
+            lworst = max(lworst, float(np.abs(lse[h, cu_new[b] + r0:cu_new[b] + r1] - lse_ref[h, r0:r1]).max()))
+        print(f"  request {b} L={L}: kept {int(mask.sum())}, sampled max|o-ref| {worst:.3e} "
+              f"max|lse-ref| {lworst:.3e}", flush=True)
+        assert worst <= FP8_TOL and lworst <= 5e-2, (b, worst, lworst)
+        io += Hq * rowsz
+        co += Hq * nq
+
+
 @pytest.mark.parametrize("shared,probes", [(True, 0), ("pooled", 0), (False, 16)],
                          ids=["shared_lists", "pooled_lists", "skeleton16"])
 def test_128k_selection_options_full_size(s128k, shared, probes):

@@ -306,6 +306,20 @@ def test_pairs_subset_matches_full():
     assert np.isnan(o2[16:32, 0]).all()
 
 
+def test_chunked_pairs_subset_matches_full():
+    q, k, v = _rand_qkv(100, 4, 2, 8, seed=18)
+    P0 = 37                                                   # the chunk enters block 2 at row 5
+    sel = O.select_blocks_chunked(q[P0:], k, v, 16, 0.4)
+    o, lse = O.sparse_attention_chunked(q[P0:], k, v, sel, True)
+    pairs = [(0, 0), (3, 4), (1, 2)]
+    o2, lse2 = O.sparse_attention_chunked(q[P0:], k, v, sel, True, pairs=pairs)
+    for h, i in pairs:
+        r0, r1 = max(16 * (2 + i), P0) - P0, min(100, 16 * (3 + i)) - P0
+        np.testing.assert_array_equal(o2[r0:r1, h], o[r0:r1, h])
+        np.testing.assert_array_equal(lse2[h, r0:r1], lse[h, r0:r1])
+    assert np.isnan(o2[:11, 1]).all() and np.isfinite(o2[:11, 0]).all()
+
+
 def test_flop_count_dense_closed_form():
     S, B, d, Hq = 256, 64, 16, 2
     q, k, v = _rand_qkv(S, Hq, 1, d, seed=1)
