@@ -52,3 +52,32 @@ def run_single(q, k, v, B, alpha, correction=True, lse=True):
 
 def oracle_inputs(q, k, v):
     return q.float().numpy(), k.float().numpy(), v.float().numpy()
+
+
+def chunk_masks(kv_idx, kv_cnt, Hq, kv_lens, starts, B):
+    """Per request the [Hq, nq, nb] mask of lists in the chunked layout (query
+    blocks first .. nb-1, first = start // B, none for an empty chunk); the
+    lists must be ascending, causal and non-empty."""
+    tri = lambda n: n * (n + 1) // 2
+    idx = kv_idx.cpu().numpy()
+    cnt = kv_cnt.reshape(-1).cpu().numpy()
+    io = co = 0
+    masks = []
+    for L, P0 in zip(kv_lens, starts):
+        nb = (L + B - 1) // B
+        first = P0 // B if P0 < L else nb
+        nq, rowsz = nb - first, tri(nb) - tri(first)
+        m = np.zeros((Hq, nq, nb), dtype=bool)
+        for h in range(Hq):
+            for i in range(nq):
+                I = first + i
+                c = int(cnt[co + h * nq + i])
+                assert 1 <= c <= I + 1, (h, I, c)
+                s0 = io + h * rowsz + tri(I) - tri(first)
+                lst = idx[s0:s0 + c]
+                assert np.all(np.diff(lst) > 0) and lst[0] >= 0 and lst[-1] <= I, (h, I, lst)
+                m[h, i, lst] = True
+        masks.append(m)
+        io += Hq * rowsz
+        co += Hq * nq
+    return masks

@@ -24,7 +24,7 @@ import block_sparse_long_pooling_amd as fp
 import oracle as O
 from block_sparse_long_pooling_amd import synth
 
-from gpu_util import FP8_TOL, compare_mask, dev
+from gpu_util import FP8_TOL, chunk_masks, compare_mask, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +45,6 @@ def _case_id(c):
     return "b%d_d%d_B%d_p%d%s" % (len(c[0]), c[4], c[5], c[6], "" if aligned else "_unaligned")
 
 
-def _tri(n):
-    return n * (n + 1) // 2
-
-
 def _queries(pb, lo, hi):
     """Queries [lo[b], hi[b]) of each request packed back to back, and cu_seqlens_q."""
     parts, cu = [], [0]
@@ -59,30 +55,7 @@ def _queries(pb, lo, hi):
 
 
 def _masks(res, Hq, kv_lens, starts, B):
-    """Per request the [Hq, nq, nb] mask of the chunk-layout lists (ascending,
-    causal, non-empty)."""
-    idx = res.kv_idx.cpu().numpy()
-    cnt = res.kv_cnt.cpu().numpy()
-    io = co = 0
-    masks = []
-    for L, P0 in zip(kv_lens, starts):
-        nb = (L + B - 1) // B
-        first = P0 // B if P0 < L else nb
-        nq, rowsz = nb - first, _tri(nb) - _tri(first)
-        m = np.zeros((Hq, nq, nb), dtype=bool)
-        for h in range(Hq):
-            for i in range(nq):
-                I = first + i
-                c = int(cnt[co + h * nq + i])
-                assert 1 <= c <= I + 1, (h, I, c)
-                s0 = io + h * rowsz + _tri(I) - _tri(first)
-                lst = idx[s0:s0 + c]
-                assert np.all(np.diff(lst) > 0) and lst[0] >= 0 and lst[-1] <= I, (h, I, lst)
-                m[h, i, lst] = True
-        masks.append(m)
-        io += Hq * rowsz
-        co += Hq * nq
-    return masks
+    return chunk_masks(res.kv_idx, res.kv_cnt, Hq, kv_lens, starts, B)
 
 
 def _two_calls(pb, starts, p, cache, pooled=None, reuse_second=False):
