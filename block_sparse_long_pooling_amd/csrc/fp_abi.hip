@@ -150,15 +150,13 @@ int select_tile(const fp_params& p) { return 32 / (p.num_q_heads / p.num_kv_head
 int run_scores(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const float* pq,
                const float* pk, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
 
-// Pooling and selection.  kv_lens: context lengths (chunked prefill) or NULL;
-// pcache: the caller's pooled cache (chunked prefill) or NULL; reuse: read
-// the prefix blocks' means from it instead of pooling them.
-int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const void* q,
-               const void* k, const void* v, const KVLayout& kv, bool paged, float* pq, float* pk, float* pv,
-               uint16_t* pkv16, float* pcache, int reuse, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
-    SeqTable t;
-    int rc = build_table(p, cu, kv_lens, batch, 1, t);
-    if (rc) return rc;
+// Pooling.  pcache: the caller's pooled cache (chunked prefill) or NULL;
+// reuse: read the prefix blocks' means from it instead of pooling them;
+// prefix_only: K and V of the prefix blocks only (the fused fp8 chunk pass
+// pools the chunks' blocks).
+int run_pool(const fp_params& p, const SeqTable& t, const void* q, const void* k, const void* v,
+             const KVLayout& kv, bool paged, float* pq, float* pk, float* pv, uint16_t* pkv16, float* pcache,
+             int reuse, bool prefix_only, hipStream_t st) {
     PoolArgs pa;
     pa.q = static_cast<const uint16_t*>(q);
     pa.k = static_cast<const uint16_t*>(k);
@@ -179,7 +177,18 @@ int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, in
     pa.q_chunks = p.num_q_heads * p.head_dim / 8;
     pa.k_chunks = p.num_kv_heads * p.head_dim / 8;
     pa.total_chunks = pa.q_chunks + pa.k_chunks * (pool_v ? 2 : 1);
-    rc = device_status(launch_pool(pa, t, paged, st), "pool");
+    pa.prefix_only = prefix_only ? 1 : 0;
+    return device_status(launch_pool(pa, t, paged, st), "pool");
+}
+
+// Pooling and selection.  kv_lens: context lengths (chunked prefill) or NULL.
+int run_select(const fp_params& p, const int32_t* cu, const int32_t* kv_lens, int32_t batch, const void* q,
+               const void* k, const void* v, const KVLayout& kv, bool paged, float* pq, float* pk, float* pv,
+               uint16_t* pkv16, float* pcache, int reuse, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
+    SeqTable t;
+    int rc = build_table(p, cu, kv_lens, batch, 1, t);
+    if (rc) return rc;
+    rc = run_pool(p, t, q, k, v, kv, paged, pq, pk, pv, pkv16, pcache, reuse, false, st);
     if (rc) return rc;
     return run_scores(p, cu, kv_lens, batch, pq, pk, kv_idx, kv_cnt, st);
 }
@@ -346,6 +355,7 @@ FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const
     qa.pq = pooled_q;
     qa.pk = pooled_k;
     qa.pkv16 = p.mean_correction ? static_cast<uint16_t*>(pooled_kv_bf16) : nullptr;
+    qa.pcache = nullptr;
     qa.H[0] = p.num_q_heads;
     qa.H[1] = qa.H[2] = p.num_kv_heads;
     qa.groups[0] = qa.groups[1] = qa.groups[2] = 0;
@@ -472,18 +482,24 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
     KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    rc = run_select(p, cu_q, kv_lens, batch, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, pcache, reuse,
-                    kv_idx, kv_cnt, st);
-    if (rc) return rc;
+    if (!f8) {
+        rc = run_select(p, cu_q, kv_lens, batch, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, pcache, reuse,
+                        kv_idx, kv_cnt, st);
+        if (rc) return rc;
+    }
     AttnArgs a;
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;
     a.q_scale = a.k_scale = a.v_scale = nullptr;
     if (f8) {
-        // Codes and scales of the chunks' query blocks: Q into the workspace,
-        // K and V into the e4m3 pages (blocks before them were encoded by
-        // earlier calls).
+        // The prefix blocks' K/V means (from the pooled cache, or pooled
+        // now); then one pass over the chunks' query blocks: Q codes and
+        // scales into the workspace, K and V codes into the e4m3 pages
+        // (blocks before them were encoded by earlier calls), and their
+        // means (the same bits the pooling kernel forms); then selection.
+        rc = run_pool(p, t, q, k_cache, v_cache, kv, true, pq, pk, nullptr, pkv16, pcache, reuse, true, st);
+        if (rc) return rc;
         uint8_t* q8 = reinterpret_cast<uint8_t*>(wsb + ws.q8);
         float* qs = reinterpret_cast<float*>(wsb + ws.qs);
         QuantArgs qa;
@@ -500,11 +516,17 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
         qa.kv = kv;
         qa.H[0] = p.num_q_heads;
         qa.H[1] = qa.H[2] = p.num_kv_heads;
+        qa.pq = pq;
+        qa.pk = pk;
+        qa.pkv16 = pkv16;
+        qa.pcache = pcache;
         qa.D = p.head_dim;
         qa.B = p.block_size;
         qa.nB = t.total_qblocks;
-        qa.q_stride = 1;
-        rc = device_status(launch_quant_pool(qa, t, true, true, st), "quantize (chunked)");
+        qa.q_stride = p.query_probes > 0 ? p.block_size / p.query_probes : 1;
+        rc = device_status(launch_quant_pool(qa, t, true, true, st), "quantize + pool (chunked)");
+        if (rc) return rc;
+        rc = run_scores(p, cu_q, kv_lens, batch, pq, pk, kv_idx, kv_cnt, st);
         if (rc) return rc;
         a.q = q8;
         a.k = f8->k8;
@@ -659,6 +681,7 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const 
     qa.pq = pq;
     qa.pk = pk;
     qa.pkv16 = pkv16;
+    qa.pcache = nullptr;
     qa.kv = kv;
     qa.H[0] = p.num_q_heads;
     qa.H[1] = qa.H[2] = p.num_kv_heads;

@@ -21,6 +21,7 @@ struct PoolArgs {
     int32_t q_chunks;    // Hq * d / 8
     int32_t k_chunks;    // Hkv * d / 8
     int32_t total_chunks;
+    int32_t prefix_only; // K and V of prefix blocks only (the fused fp8 chunk pass pools the rest)
 };
 
 // A selection workgroup holds kSelectRowWaves row waves of 32 score rows, i.e.
@@ -63,9 +64,10 @@ struct QuantArgs {
     const uint16_t* src[3];      // bf16 [T, H, d] packed rows; K and V may be pages [num_pages, page, Hkv, d]
     uint8_t* codes[3];           // e4m3 codes in the layout of src
     float* scale[3];             // fp32 [H, nB]; paged K and V: [num_pages, Hkv], entry of a block's first page
-    float* pq;                   // fp32 Q_bar [Hq, nB, d]
-    float* pk;                   // fp32 K_bar [Hkv, nB, d]
-    uint16_t* pkv16;             // bf16 [2, Hkv, nB, d] (K_bar then V_bar) or null
+    float* pq;                   // fp32 Q_bar [Hq, nB, d] (by query-block row)
+    float* pk;                   // fp32 K_bar [Hkv, total_blocks, d]
+    uint16_t* pkv16;             // bf16 [2, Hkv, total_blocks, d] (K_bar then V_bar) or null
+    float* pcache;               // chunk mode: fp32 [2, num_pages, Hkv, d] pooled cache (K/V means) or null
     KVLayout kv;                 // pages of K and V (used when paged)
     int32_t H[3];                // Hq, Hkv, Hkv
     int32_t groups[3];           // head groups per tensor (set by the launcher)
@@ -74,8 +76,8 @@ struct QuantArgs {
 };
 
 hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStream_t s);
-// chunk: codes and scales of the query blocks of each request's chunk only
-// (paged; nB = t.total_qblocks), no means.
+// chunk: codes, scales and means of the query blocks of each request's chunk
+// only (paged; nB = t.total_qblocks), K/V means also into a.pcache.
 hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, bool chunk, hipStream_t s);
 hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);

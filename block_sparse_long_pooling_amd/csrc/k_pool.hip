@@ -12,14 +12,13 @@
 // One workgroup covers one KV block of one request and 256 column chunks
 // of 8 bf16 (16 bytes) taken from the concatenated row [Q | K | V].  Each
 // thread walks the block's tokens, so a wave reads 1 KiB contiguous per
-// token step; the token loop is unrolled 4 deep so that every thread keeps 4
-// loads in flight (8 measured 2% slower).  Sums are fp32 in token order, then divided by n_J.
+// token step, with 4 loads in flight per thread.  Sums are fp32, in the
+// token tree of the fused fp8 pass (tree_sum below), then divided by n_J.
 #include "fp_launch.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
 // Q, K and V are streamed once here: non-temporal loads (they are not kept in
 // the caches for reuse) run the pass about 10% faster.
@@ -36,14 +35,45 @@ __device__ __forceinline__ void add8(float* acc, uint4 x) {
     acc[6] += bf16_lo(x.w); acc[7] += bf16_hi(x.w);
 }
 
+// Block sum of one 8-value column chunk, in the order in which the fused fp8
+// pass (k_quant.hip) adds the same tokens: partial (w, hf), w = 0..7,
+// hf = 0..1, takes tokens 16 s + 2 w + hf in s order; the two halves of a w
+// are added, then the w partials in w order.  The means of both kernels are
+// then bit-identical (tokens that do not count add nothing; the fused pass
+// adds zeros for them, which leaves every partial unchanged).  load(tok)
+// gives the chunk of token tok and whether it counts; two values of s are in
+// flight at a time (four loads).
+template <typename Load>
+__device__ __forceinline__ void tree_sum(int B, Load&& load, float* tot) {
+    const int ns = B / 16;
+#pragma unroll 1
+    for (int w = 0; w < 8; ++w) {
+        float a0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float a1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < ns; s += 2) {
+            uint4 x[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ok[u] = load(16 * (s + (u >> 1)) + 2 * w + (u & 1), x[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (ok[u]) add8((u & 1) ? a1 : a0, x[u]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot[i] = w == 0 ? a0[i] + a1[i] : tot[i] + (a0[i] + a1[i]);
+    }
+}
+
 template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
     const int gb = blockIdx.x;
-    const int c = blockIdx.y * kThreads + threadIdx.x;
+    // prefix_only: the grid covers the K and V chunks of prefix blocks only.
+    const int c = (a.prefix_only ? a.q_chunks : 0) + blockIdx.y * kThreads + threadIdx.x;
     if (c >= a.total_chunks) return;
     const int b = request_of_block(t, gb);
     const int I = gb - t.blk_off[b];
     const int first = first_block(t, b);
+    if (a.prefix_only && I >= first) return;
     const int len = context_len(t, b, a.B);
     const int t0 = I * a.B;
     const int n = min(a.B, len - t0);
@@ -60,19 +90,16 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
         const int lo = I == first ? ph : 0;
         // With skeleton queries only every q_stride-th token of the block
         // counts (the host admits them for block-aligned chunks only).
-        const int64_t row_elems = (int64_t)a.Hq * a.D * a.q_stride;
-        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B - ph + lo) * a.Hq * a.D + col;
-        const int nq = (n - lo + a.q_stride - 1) / a.q_stride;
-        int r = 0;
-        for (; r + kUnroll <= nq; r += kUnroll) {
-            uint4 x[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                x[u] = ntload(p + (int64_t)(r + u) * row_elems);
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
-        }
-        for (; r < nq; ++r) add8(acc, *reinterpret_cast<const uint4*>(p + (int64_t)r * row_elems));
+        const int64_t row_elems = (int64_t)a.Hq * a.D;
+        // Row 0 of the block is query row q0 (tokens before lo are not in the call).
+        const uint16_t* p = a.q + (int64_t)(t.tok_off[b] + (I - first) * a.B - ph) * row_elems + col;
+        const int stride = a.q_stride;
+        tree_sum(a.B, [&](int tok, uint4& x) {
+            const bool ok = tok >= lo && tok < n && tok % stride == 0;
+            x = ok ? ntload(p + (int64_t)tok * row_elems) : make_uint4(0, 0, 0, 0);
+            return ok;
+        }, acc);
+        const int nq = (n - lo + stride - 1) / stride;
         const float fn = (float)nq;
 #pragma unroll
         for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
@@ -107,22 +134,11 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
         const uint16_t* base = isv ? a.v : a.k;
         const int64_t row_elems = (int64_t)a.Hkv * a.D;
         const int tok0 = t.tok_off[b];
-        int r = 0;
-        for (; r + kUnroll <= n; r += kUnroll) {
-            uint4 x[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t row = kv_row<PAGED>(a.kv, b, tok0, t0 + r + u);
-                x[u] = row >= 0 ? ntload(base + row * row_elems + col)
-                                : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) add8(acc, x[u]);
-        }
-        for (; r < n; ++r) {
-            const int64_t row = kv_row<PAGED>(a.kv, b, tok0, t0 + r);
-            if (row >= 0) add8(acc, *reinterpret_cast<const uint4*>(base + row * row_elems + col));
-        }
+        tree_sum(a.B, [&](int tok, uint4& x) {
+            const int64_t row = tok < n ? kv_row<PAGED>(a.kv, b, tok0, t0 + tok) : -1;
+            x = row >= 0 ? ntload(base + row * row_elems + col) : make_uint4(0, 0, 0, 0);
+            return row >= 0;
+        }, acc);
         const float fn = (float)n;
 #pragma unroll
         for (int i = 0; i < 8; ++i) mean[i] = acc[i] / fn;
@@ -152,7 +168,9 @@ hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStre
     // Blocks vary fastest in the dispatch order, so the workgroups in flight
     // spread over the whole tensors (dispatching a block's three chunk groups
     // together ran 5% slower).
-    dim3 grid(t.total_blocks, (a.total_chunks + kThreads - 1) / kThreads);
+    const int nchunks = a.total_chunks - (a.prefix_only ? a.q_chunks : 0);
+    if (nchunks <= 0) return hipSuccess;
+    dim3 grid(t.total_blocks, (nchunks + kThreads - 1) / kThreads);
     if (paged)
         hipLaunchKernelGGL(k_pool<true>, grid, dim3(kThreads), 0, s, a, t);
     else

@@ -8,12 +8,14 @@
 // V rows may live in a paged cache: codes then go to the same place in an
 // e4m3 page pool, and each block's scale to the entry of its first page).
 // In chunk mode (chunked prefill over the paged cache) the grid covers only
-// the query blocks of each request's chunk and forms codes and scales, no
-// means (the pooling kernel forms those): K and V of such a block are
+// the query blocks of each request's chunk: K and V of such a block are
 // re-encoded whole from the bf16 pages, the tokens before the chunk
 // included, so a block that an earlier chunk left partial ends up encoded as
 // a prefill of the whole context would encode it; Q of the block holds only
-// the chunk's queries in it.
+// the chunk's queries in it.  Its K and V means also go to the caller's
+// pooled cache.  The block sums run in a fixed token tree that the pooling
+// kernel reproduces (tree_sum in k_pool.hip), so both kernels' means are
+// bit-identical.
 // A workgroup (8 waves) owns one block of one tensor for a group of heads
 // whose chunks of 8 bf16 make 32 chunks per token row (two heads at d 128,
 // four at d 64), i.e. 512 contiguous bytes.  Lane l of wave w handles chunk
@@ -66,13 +68,15 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     const int hl = ch / CPH;               // head within the group
     const int h = g * HPG + hl;
     const bool hv = h < H;
-    int b, I;                                       // request, block of request b
+    int b, I, kvJ;                                  // request, block of request b, block of all requests
     if (CHUNK) {
         b = request_of_qblock(t, J);
         I = first_block(t, b) + J - (t.blk_off[b] - t.pre_off[b]);
+        kvJ = t.blk_off[b] + I;
     } else {
         b = request_of_block(t, J);
         I = J - t.blk_off[b];
+        kvJ = J;
     }
     const int t0 = I * B;
     const int n = min(B, context_len(t, b, B) - t0);
@@ -161,25 +165,37 @@ __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqT
     const float sc = am > 0.f ? __fdiv_rn(am, kE4M3Max) : 1.f;
     const float ry = __fdiv_rn(1.f, sc);
     if (w == 0 && hf == 0) {
-        if (!CHUNK) {   // means: the pooling kernel forms them in chunk mode
+        {
             float m[8];
+            const float cnt = (float)((n - lo + stride - 1) / stride);   // counted tokens (lo = 0 when stride > 1)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float t = psum[0][ch][i];
 #pragma unroll
                 for (int w2 = 1; w2 < kWaves; ++w2) t += psum[w2][ch][i];
-                m[i] = t / (float)((n + stride - 1) / stride);
+                m[i] = t / cnt;
             }
-            const int64_t off = ((int64_t)h * a.nB + J) * D + (ch % CPH) * 8;
+            // Q means by query-block row J; K and V means by KV block of all requests.
+            const int dd = (ch % CPH) * 8;
+            const int64_t off = ((int64_t)h * (CHUNK && ts > 0 ? t.total_blocks : a.nB) + (ts > 0 ? kvJ : J)) * D + dd;
             float* dst = ts == 0 ? a.pq : (ts == 1 ? a.pk : nullptr);
             if (dst) {
                 reinterpret_cast<float4*>(dst + off)[0] = make_float4(m[0], m[1], m[2], m[3]);
                 reinterpret_cast<float4*>(dst + off)[1] = make_float4(m[4], m[5], m[6], m[7]);
             }
             if (ts > 0 && a.pkv16)
-                *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * a.nB * D : 0) + off) =
+                *reinterpret_cast<uint4*>(a.pkv16 + (ts == 2 ? (int64_t)a.H[1] * (CHUNK ? t.total_blocks : a.nB) * D : 0) + off) =
                     make_uint4(pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3]), pack_bf16(m[4], m[5]),
                                pack_bf16(m[6], m[7]));
+            if (CHUNK && ts > 0 && a.pcache) {
+                // The pooled cache entry of the page that holds the block's first token.
+                const int page = a.kv.block_table[(int64_t)b * a.kv.max_pages + t0 / a.kv.page_size];
+                if ((unsigned)page < (unsigned)a.kv.num_pages) {
+                    float* e = a.pcache + (((int64_t)(ts == 2 ? a.kv.num_pages : 0) + page) * H + h) * D + dd;
+                    reinterpret_cast<float4*>(e)[0] = make_float4(m[0], m[1], m[2], m[3]);
+                    reinterpret_cast<float4*>(e)[1] = make_float4(m[4], m[5], m[6], m[7]);
+                }
+            }
         }
         if (ch % CPH == 0) {
             if (pg) {

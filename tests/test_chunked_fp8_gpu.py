@@ -131,7 +131,9 @@ def test_chunked_fp8_matches_oracle(case, corr):
 def test_chunked_fp8_pooled_cache_between_calls(cut):
     """With the pooled cache kept between the calls, the second call reads the
     prefix means from it: it equals a second call that pools the prefix
-    itself, bit for bit."""
+    itself, bit for bit, and the cache holds the same bits as after the same
+    two calls through the bf16 chunked entry (the encoding pass forms the
+    chunk blocks' means in the pooling kernel's summation order)."""
     lengths, Hq, Hkv, d, B, page = [1500, 700], 8, 2, 128, 128, 32
     pb = synth.make_paged_batch(lengths, Hq, Hkv, d, seed_base=97, verticals=True, page_size=page)
     p = fp.make_params(Hq, Hkv, d, B, 0.15, mean_correction=True, dtype=FP8)
@@ -144,6 +146,20 @@ def test_chunked_fp8_pooled_cache_between_calls(cut):
     torch.cuda.synchronize()
     assert torch.equal(r_reuse.out, r_fresh.out) and torch.equal(r_reuse.lse, r_fresh.lse)
     assert torch.equal(r_reuse.kv_cnt, r_fresh.kv_cnt)
+    p16 = fp.make_params(Hq, Hkv, d, B, 0.15, mean_correction=True)
+    pooled16 = fp.alloc_pooled_cache(p16, pb.k_cache.shape[0], dev())
+    bt, kd, vd = pb.block_table.to(dev()), pb.k_cache.to(dev()), pb.v_cache.to(dev())
+    q1, cu1 = _queries(pb, [0, 0], cut)
+    fp.fp_sparse_prefill_chunked_paged(p16, q1.to(dev()), kd, vd, bt, cu1, cut, pooled_cache=pooled16)
+    r16 = fp.fp_sparse_prefill_chunked_paged(p16, q2.to(dev()), kd, vd, bt, cu2, kv_lens, pooled_cache=pooled16,
+                                             prefix_pooled=True)
+    torch.cuda.synchronize()
+    used = torch.zeros(pb.k_cache.shape[0], dtype=torch.bool)
+    for b, L in enumerate(lengths):
+        for J in range((L + B - 1) // B):
+            used[int(pb.block_table[b, J * B // page])] = True
+    assert torch.equal(pooled[:, used.to(dev())], pooled16[:, used.to(dev())])
+    assert torch.equal(r_reuse.kv_cnt, r16.kv_cnt)
 
 
 def test_chunked_fp8_rejects_bf16_params():

@@ -1,7 +1,9 @@
 """The one-pass fp8 preparation (fp_select_blocks_fp8): its e4m3 codes and
 scales equal the oracle's quantizer bit for bit, its block means equal the
-oracle's to fp32 rounding, its lists match the oracle's selection outside the
-threshold band, and attention on its outputs matches the oracle."""
+oracle's to fp32 rounding and the bf16 selection's (fp_select_blocks) bit for
+bit -- both kernels sum a block in the same token tree -- so its lists are the
+bf16 selection's, which match the oracle's outside the threshold band; and
+attention on its outputs matches the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -52,6 +54,25 @@ def test_codes_scales_and_means(shape):
     for i, x in enumerate((k, v)):
         ref = O.block_means(x.float().numpy(), B)
         assert np.abs(pkv[i] - ref).max() <= np.abs(ref).max() * 2.0 ** -8 + 1e-6   # bf16 rounding of the means
+
+
+@pytest.mark.parametrize("probes", [0, 16])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "S%d_h%d-%d_d%d_B%d" % s)
+def test_means_and_lists_equal_the_bf16_selection(shape, probes):
+    """The fused pass and the pooling kernel add a block's tokens in the same
+    order, so the means (fp32 and their bf16 copies), counts and lists agree
+    bit for bit."""
+    S, Hq, Hkv, d, B = shape
+    q, k, v = (t.to(dev()) for t in synth.make_sequence(S, Hq, Hkv, d, seed=3 * S + Hq, verticals=True))
+    p16 = fp.make_params(Hq, Hkv, d, B, 0.1, mean_correction=True, query_probes=probes)
+    p8 = fp.make_params(Hq, Hkv, d, B, 0.1, mean_correction=True, dtype=fp.FP_DTYPE_FP8_E4M3FN, query_probes=probes)
+    s16 = fp.fp_select_blocks(p16, q, k, v)
+    s8, _ = fp.fp_select_blocks_fp8(p8, q, k, v)
+    torch.cuda.synchronize()
+    for name in ("pooled_q", "pooled_k", "pooled_kv", "kv_cnt"):
+        assert torch.equal(getattr(s8, name), getattr(s16, name)), name
+    nB = (S + B - 1) // B
+    assert np.array_equal(fp.lists_to_mask(s8.kv_idx, s8.kv_cnt, Hq, nB), fp.lists_to_mask(s16.kv_idx, s16.kv_cnt, Hq, nB))
 
 
 @pytest.mark.parametrize("alpha", [0.0, 0.1, 0.5])
