@@ -66,7 +66,9 @@ attention in closed form when K and V are constant within blocks; constant V
 gives constant output; the argmax block is always kept and masks nest in
 alpha; GQA equals MHA with repeated K/V; a varlen batch equals its requests;
 a chunk equals per-token brute force written from positions, and the last
-rows of the full prefill.  The correction's definition itself is a reading, not a formula from the pages;
+rows of the full prefill; the chunk's fp8 query codes equal the blockwise
+quantizer when the chunk starts on a block boundary, and each query block's
+codes and scale come from exactly the chunk rows whose positions fall in it.  The correction's definition itself is a reading, not a formula from the pages;
 only its implementation under that reading is pinned.
 """
 from __future__ import annotations
