@@ -297,6 +297,11 @@ def main():
         "density": round(head["density"], 5), "attn_tflops": round(attn_tflops, 2),
         "select_gbps": round(sel_gbps, 1), "select_hbm_frac": round(sel_gbps / PEAK_HBM_GBPS, 4),
         "flops": {"kept": head["f_kept"], "corr": head["f_corr"]},
+        # beside the headline: the kept blocks' share alone, and the dense
+        # causal work (4 d Hq S^2 / 2) over the sparse attention time -- a
+        # dense-equivalent rate, not work the kernel does
+        "attn_kept_tflops": round(head["f_kept"] / (head["attn_ms"] * 1e-3) / 1e12, 2),
+        "attn_dense_equivalent_tflops": round(4.0 * d * Hq * S * S / 2 / (head["attn_ms"] * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu,
     }
     rec.update(extra)
