@@ -43,7 +43,7 @@ namespace {
 constexpr int kWaves = 8;
 
 // Six waves per SIMD (three workgroups per CU): more loads in flight, at
-// the cost of a 16-byte spill.
+// the cost of a small spill (28 bytes) in the paged variants.
 template <int D, int B, bool PAGED, bool CHUNK>
 __global__ __launch_bounds__(64 * kWaves, 6) void k_quant_pool(QuantArgs a, SeqTable t) {
     constexpr int CPH = D / 8;             // chunks per head
