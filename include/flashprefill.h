@@ -290,8 +290,10 @@ int fp_sparse_prefill_chunked_paged(const fp_params* params, const void* q,
  * Chunked prefill with fp8 attention (FlashPrefill V2 abstract: FP8
  * inference, and the attention backend with paged KV and continuous
  * batching of the authors' post).  The chunk, its context, the pooled cache
- * and the lists are those of fp_sparse_prefill_chunked_paged: pooling and
- * selection read the bf16 pages.  Attention reads e4m3 pages kept beside
+ * and the lists are those of fp_sparse_prefill_chunked_paged, bit for bit:
+ * the block means come from the bf16 pages (the chunks' blocks in the same
+ * pass that encodes them, summed in the pooling kernel's order), and the
+ * pooled cache receives the same entries.  Attention reads e4m3 pages kept beside
  * them, in the form fp_sparse_prefill_varlen_paged_fp8 writes: codes in the
  * layout of the bf16 pages and one fp32 scale per (page, KV head) at the
  * entry of the page that holds a block's first token.  The call encodes the
