@@ -284,7 +284,7 @@ def main():
 
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "kernel": "k_attn_bf16<128,128,2>", "traffic": measured_traffic(),
+            "kernel": "k_attn_bf16<128,128>", "traffic": measured_traffic(),
             "traffic_unit": "bytes/launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)"}
     rec = {
         "metric": METRIC, "value": round(step_tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,

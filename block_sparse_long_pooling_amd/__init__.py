@@ -155,9 +155,9 @@ def fp_varlen_workspace_bytes(params: fp_params, cu_seqlens: Sequence[int]) -> i
 
 
 def fp_attention_workgroups(params: fp_params, cu_seqlens: Sequence[int], paged: bool = False) -> int:
-    """Workgroups the attention launch uses for these lengths on the current
-    device (bf16: the persistent grid of this kernel variant; fp8: one per
-    query block and head); -1 for invalid arguments."""
+    """Workgroups the attention launch uses for these lengths: one per query
+    block and query head (bf16 and fp8, contiguous or paged); -1 for invalid
+    arguments."""
     cu = _cu_host(cu_seqlens)
     return int(lib().fp_attention_workgroups(ctypes.byref(params), cu, len(cu) - 1, int(bool(paged))))
 

@@ -1,13 +1,9 @@
-// Work-item walk shared by the attention kernels: the persistent item loop's
-// pieces (list cursor, item setup, tile DMA, grid sizing).  A work item is
-// (query block I of one request, HP query heads of one KV head); its tiles
-// are the union of the heads' kept KV blocks followed by the tiles of pooled
-// means that form the correction (FlashPrefill, gist.science technical
-// summary, section 2.C; FlashPrefill V2 abstract).
+// Pieces of the tile walk shared by the bf16 and fp8 attention kernels
+// (gfx950): the tile DMA plan and issue, the bf16 S = K Q^T and O += V^T P^T
+// products on LDS tiles, and the mean-correction pass over the pooled means
+// of skipped past blocks (FlashPrefill, gist.science technical summary,
+// section 2.C; FlashPrefill V2 abstract).
 #pragma once
-#include <mutex>
-#include <type_traits>
-
 #include "fp_attn.h"
 
 namespace fp_walk {
@@ -31,26 +27,15 @@ __device__ __forceinline__ int swz(int row) {
     return (row >> 2) & 3;   // D == 32: 64-byte rows of fp8 d = 64 tiles
 }
 
-// Workgroup geometry of the bf16 kernel: 32 query rows per wave.
-template <int D, int BLK, int HP>
-struct Geo {
-    static constexpr int WPH = BLK / 32;          // waves per head
-    static constexpr int NW = WPH * HP;           // waves per workgroup
-    static constexpr int NT = 64 * NW;            // threads
-    static constexpr int NCH = D / 8;             // 16-byte chunks per row
-    static constexpr int TILE = BLK * D * 2;      // bytes per K or V tile
-    static constexpr int NSUB = BLK / 32;
-    static constexpr int NDS = D / 32;
-};
-
-// Per-thread DMA plan for a [BLK][D] bf16 tile: load i of this thread fills
-// LDS chunk i*NT + tid, i.e. row row0 + i*NT/NCH and chunk position chunk0,
-// which holds logical chunk (chunk0 XOR swizzle of the row).  Two registers;
-// the rest is recomputed per load.
-template <int D, int BLK, int NT>
+// Per-thread DMA plan for a [ROWS][D] bf16 tile (ROWS keys or pooled
+// blocks): load i of this thread fills LDS chunk i*NT + tid, i.e. row
+// row0 + i*NT/NCH and chunk position chunk0, which holds logical chunk
+// (chunk0 XOR swizzle of the row).  Two registers; the rest is recomputed
+// per load.
+template <int D, int ROWS, int NT>
 struct DmaPlan {
     static constexpr int NCH = D / 8;
-    static constexpr int NLOAD = BLK * NCH / NT;
+    static constexpr int NLOAD = ROWS * NCH / NT;
     static constexpr int ROWSTEP = NT / NCH;
     int row0, chunk0;
     __device__ __forceinline__ void init(int tid) {
@@ -67,28 +52,29 @@ struct DmaPlan {
 // with the DMAs before it.  Rows past the request's end (row >= nvalid) look
 // up its last valid row's page, so the block-table read stays inside the
 // pages that cover the request.
-template <int D, int BLK, int NT>
+template <int D, int ROWS, int NT>
 __device__ __forceinline__ void load_tile_pages(const int32_t* pages, const KVLayout& L, int J, int nvalid,
-                                                const DmaPlan<D, BLK, NT>& plan, int* pg) {
+                                                const DmaPlan<D, ROWS, NT>& plan, int* pg) {
 #pragma unroll
-    for (int i = 0; i < DmaPlan<D, BLK, NT>::NLOAD; ++i)
-        pg[i] = pages[(J * BLK + min(plan.row(i), nvalid - 1)) / L.page_size];
+    for (int i = 0; i < DmaPlan<D, ROWS, NT>::NLOAD; ++i)
+        pg[i] = pages[(J * ROWS + min(plan.row(i), nvalid - 1)) / L.page_size];
 }
 
-// DMA one tile: rows J*BLK .. of the request whose first row is `first`
-// (contiguous), or of its pages pg from load_tile_pages (paged).
-template <int D, int BLK, int NT, bool PAGED>
+// DMA one tile: rows J*ROWS .. J*ROWS+ROWS-1 of the request whose first row
+// is `first` (contiguous), or of its pages pg from load_tile_pages (paged).
+// nvalid >= 1 rows of the tile hold data.
+template <int D, int ROWS, int NT, bool PAGED>
 __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg, const KVLayout& L,
-                                           int64_t rs, int J, int nvalid, const DmaPlan<D, BLK, NT>& plan,
+                                           int64_t rs, int J, int nvalid, const DmaPlan<D, ROWS, NT>& plan,
                                            const uint4* zero, char* lds, int wave_base) {
-    using P = DmaPlan<D, BLK, NT>;
-    static_assert((BLK * P::NCH) % NT == 0, "tile chunks must split evenly");
+    using P = DmaPlan<D, ROWS, NT>;
+    static_assert((ROWS * P::NCH) % NT == 0, "tile chunks must split evenly");
     if (!PAGED) {
         // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
         // addressing form).
-        const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * BLK * rs);
+        const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * ROWS * rs);
         // Rows past the end of the sequence re-read its last row: they occur
-        // only in the diagonal tile, where the causal mask removes them, and
+        // only on the diagonal block, where the causal mask removes them, and
         // finite values keep 0 * v at 0.  The row index is opaque so the
         // compiler does not keep a precomputed offset per chunk and row stride
         // (it would spill).
@@ -103,7 +89,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
 #pragma unroll
         for (int i = 0; i < P::NLOAD; ++i) {
             const int row = plan.row(i);
-            const int tr = J * BLK + row;
+            const int tr = J * ROWS + row;
             const int page = pg[i];
             // Opaque column offset: keeps the compiler from holding a 64-bit
             // pointer per chunk across the loop (it would spill).
@@ -119,15 +105,15 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
 
 // S^T for subtiles SUB0 .. SUB0+NS-1 (keys 32 SUB0 ..) of this wave's 32
 // queries; each subtile's 8 K operands are read before its MFMA chain.
-template <int D, int BLK, int HP, int SUB0, int NS>
+template <int D, int SUB0, int NS>
 __device__ __forceinline__ void qk(const uint4* kt, const bf16x8* qf, int col, int half, f32x16* s) {
-    using G = Geo<D, BLK, HP>;
+    constexpr int NCH = D / 8;                   // 16-byte chunks per row
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int row = 32 * (SUB0 + j) + col;
         uint4 av[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) av[kk] = kt[row * G::NCH + ((half + 2 * kk) ^ swz<D>(row))];
+        for (int kk = 0; kk < D / 16; ++kk) av[kk] = kt[row * NCH + ((half + 2 * kk) ^ swz<D>(row))];
         __builtin_amdgcn_sched_barrier(0);               // keep the reads ahead of the MFMA chain
         f32x16 acc = {};
 #pragma unroll
@@ -143,13 +129,12 @@ __device__ __forceinline__ void qk(const uint4* kt, const bf16x8* qf, int col, i
 // (r = 0, 1; t = 0..3) -- the same key order as the P registers.  Each
 // ds_read_b64_tr_b16 reads, per source lane, 4 columns of one key row; the
 // hardware transpose hands each lane its column for 4 consecutive keys.
-template <int D, int BLK, int HP, int SUB0, int NS>
+template <int D, int SUB0, int NS>
 __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int lane, f32x16* o) {
-    using G = Geo<D, BLK, HP>;
     const int gl = lane & 15, gi = lane >> 4;
     const int hf = gi >> 1;
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) {
+    for (int ds = 0; ds < D / 32; ++ds) {
         const int col_e = 32 * ds + 16 * (gi & 1) + 4 * (gl & 3);
         const int chunk = col_e >> 3, within = (col_e & 7) * 2;
         s16x4 part[2 * NS][2];
@@ -174,143 +159,92 @@ __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int 
     }
 }
 
-// Ascending-merge cursor over the lists of the HP heads of a workgroup.
-template <int HP>
-struct Union {
-    const int32_t* list[HP];
-    int cnt[HP];
-    int cap;         // capacity of each list (I + 1): windows never read past it
-    int pos[HP];     // entries of list h consumed so far
-    int wbase[HP];   // list index held by lane 0 of win[h]
-    int win[HP];     // lane l: list[h][wbase[h] + l] (INT_MAX past the end)
-    // Lists are read 64 entries at a time, one per lane, so the walk waits
-    // on memory once per 64 kept blocks instead of once per block.  A window
-    // is bounded by the list's capacity, not its count, so it need not wait
-    // for the count; entries past the count are never used.
-    __device__ __forceinline__ void load_window(int h) {
-        wbase[h] = pos[h];
-        const int i = pos[h] + (int)__lane_id();
-        win[h] = i < cap ? list[h][i] : INT_MAX;
+// Mean-correction pass over the skipped past blocks J < I of row block I:
+// BLK/2 pooled blocks per step, double-buffered DMA into buf0 / buf1 (each a
+// [BLK][D] bf16 tile buffer: BLK/2 K_bar rows, then BLK/2 V_bar rows, chunks
+// swizzled per row).
+template <int D, int BLK>
+__device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable& t, int b, int I, int hk, int cnt,
+                                               const int32_t* list, const bf16x8* qf, char* buf0, char* buf1,
+                                               uint32_t* kept_bits, int tid, int col, int half, float c, float& m,
+                                               float& l, f32x16* o) {
+    constexpr int NT = 2 * BLK;                          // threads
+    constexpr int HT = BLK / 2;                          // pooled blocks per step
+    constexpr int NS = HT / 32;                          // 32-key subtiles per step
+    constexpr int HALF = HT * D * 2;                     // bytes of K_bar (or V_bar) rows per step
+    const int lane = tid & 63;
+    const int nwords = (I + 31) >> 5;
+    for (int i = tid; i < nwords; i += NT) kept_bits[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += NT) {
+        const int J = list[i];
+        if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
     }
-    __device__ __forceinline__ int val(int h) const {
-        return pos[h] < cnt[h] ? __builtin_amdgcn_readlane(win[h], pos[h] - wbase[h]) : INT_MAX;
-    }
-    // Next block of the union and the heads that keep it (bit mask); INT_MAX when done.
-    __device__ __forceinline__ int next(int& act) {
-        int v[HP];
-        int J = INT_MAX;
+    __syncthreads();
+    const uint16_t* kfirst = a.pk16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
+    const uint16_t* vfirst = a.pv16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
+    DmaPlan<D, HT, NT> plan;
+    plan.init(tid);
+    const int wave_base = __builtin_amdgcn_readfirstlane(64 * (tid >> 6) * 16);
+    const float log2_blk = __log2f((float)BLK);          // every block J < I is full
+    const int nht = (I + HT - 1) / HT;
+    // Skip bits of step hh: bit j of word sub <=> block HT hh + 32 sub + j is past and not kept.
+    auto skips = [&](int hh, uint32_t* sk) {
+        uint32_t any = 0;
 #pragma unroll
-        for (int h = 0; h < HP; ++h) {
-            v[h] = val(h);
-            J = min(J, v[h]);
+        for (int sub = 0; sub < NS; ++sub) {
+            const int j0 = HT * hh + 32 * sub;
+            const int nvalid = min(32, max(0, I - j0));
+            const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+            sk[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[j0 >> 5] & valid);
+            any |= sk[sub];
         }
-        act = 0;
-#pragma unroll
-        for (int h = 0; h < HP; ++h)
-            if (J != INT_MAX && v[h] == J) {
-                act |= 1 << h;
-                if (++pos[h] - wbase[h] == 64) load_window(h);
-            }
-        return J;
-    }
-};
-
-// One work item: query block I of one request, HP heads of one KV head.
-template <int D, int BLK, int HP, bool PAGED>
-struct Item {
-    int b, nb, I, tok0, len, q0, lo, nI, hk, h;  // h: this wave's query head; rows lo .. nI-1 exist
-    int nct;                                      // correction tiles (blocks 0 .. I-1 in tiles of BLK)
-    int ct;                                       // next correction tile to examine; -1 while kept blocks remain
-    Union<HP> u;
-    const uint16_t* kfirst;                       // K rows of this request / KV head (or the pool)
-    const uint16_t* vfirst;
-    const int32_t* pages;                         // block-table row (paged)
-
-    __device__ __forceinline__ void setup(const AttnArgs& a, const SeqTable& t, int idx, int hs) {
-        const int npairs = a.Hq / HP;
-        const int rank = idx / npairs;
-        h = HP * xcd_head(idx % npairs, npairs) + hs;
-        int local;
-        item_of(t, rank, b, local);
-        nb = seq_blocks(t, b);
-        const int first = first_block(t, b);          // query blocks are first .. nb-1
-        I = nb - 1 - local;
-        tok0 = t.tok_off[b];
-        len = context_len(t, b, BLK);
-        // Row r of the block is query row q0 + r; a chunk that starts inside
-        // its first block has no rows before lo there.
-        const int ph = chunk_phase(t, b, BLK);
-        q0 = tok0 + (I - first) * BLK - ph;
-        lo = I == first ? ph : 0;
-        nI = min(BLK, len - I * BLK);
-        hk = h / a.g;
-        const int64_t rs = (int64_t)a.Hkv * D;
-        const int h0 = h - hs;
-        // The heads' counts and first list windows load together (unconditional
-        // loads, lanes past the capacity re-read the last entry and are masked
-        // after), so setting up an item waits on memory once.
-        int cnt_raw[HP], win_raw[HP];
-        u.cap = I + 1;
-#pragma unroll
-        for (int j = 0; j < HP; ++j) {
-            u.list[j] = a.kv_idx + list_row(t, b, h0 + j, I, nb, first);
-            cnt_raw[j] = a.kv_cnt[count_index(t, a.Hq, b, h0 + j, I, nb, first)];
-            win_raw[j] = u.list[j][min((int)__lane_id(), I)];
-        }
-        __builtin_amdgcn_sched_barrier(0);               // all four loads before the first use
-#pragma unroll
-        for (int j = 0; j < HP; ++j) {
-            u.cnt[j] = __builtin_amdgcn_readfirstlane(cnt_raw[j]);
-            u.pos[j] = 0;
-            u.wbase[j] = 0;
-            u.win[j] = (int)__lane_id() < u.cap ? win_raw[j] : INT_MAX;
-        }
-        nct = (a.correction && I > 0) ? (I + BLK - 1) / BLK : 0;
-        ct = -1;
-        const int64_t base = (PAGED ? 0 : (int64_t)tok0 * rs) + (int64_t)hk * D;
-        kfirst = static_cast<const uint16_t*>(a.k) + base;
-        vfirst = static_cast<const uint16_t*>(a.v) + base;
-        pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
-    }
-};
-
-// Tiles of a work item are coded as ints: a kept KV block J (0 <= J <= I), or
-// kCorr + ct for correction tile ct (pooled blocks ct*BLK .. ct*BLK+BLK-1).
-constexpr int kCorr = FP_MAX_BLOCKS;
-
-// Persistent grid: as many workgroups as the device holds at once (a multiple
-// of the 8 XCDs), at most one per item.  The resident count depends on the
-// kernel (its registers and LDS) and the block size, so it is computed once
-// per (kernel, block size, device) and cached under that key: every
-// instantiation of a kernel template has the same function type, so a cache
-// keyed by type alone would let the first variant launched size all others.
-inline int resident_workgroups(const void* kernel, int block) {
-    struct Entry {
-        const void* fn;
-        int block, dev, n;
+        return any != 0;
     };
-    constexpr int kMaxEntries = 256;
-    static std::mutex mu;
-    static Entry cache[kMaxEntries];
-    static int used = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-        if (cache[i].fn == kernel && cache[i].block == block && cache[i].dev == dev) return cache[i].n;
-    int ncu = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
-        return 0;
-    const int n = max(8, (ncu * max(per_cu, 1)) / 8 * 8);
-    if (used < kMaxEntries) cache[used++] = Entry{kernel, block, dev, n};
-    return n;
-}
-
-template <typename K>
-int persistent_grid(K kernel, int block, int nitems) {
-    const int n = resident_workgroups(reinterpret_cast<const void*>(kernel), block);
-    return n > 0 ? max(1, min(nitems, n)) : nitems;
+    auto next_step = [&](int hh) {
+        uint32_t sk[NS];
+        for (++hh; hh < nht; ++hh)
+            if (skips(hh, sk)) return hh;
+        return nht;
+    };
+    auto issue = [&](int hh, char* dst) {
+        const int nvalid = I - HT * hh;
+        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
+        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
+    };
+    f32x16 s[NS];
+    uint32_t pk[NS][8];
+    int cur = next_step(-1);
+    if (cur < nht) issue(cur, buf0);
+    auto step = [&](char* bcur, char* bnext) {
+        __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
+        lds_barrier();                                   // ... every thread's; the other buffer is free
+        const int nxt = next_step(cur);
+        if (!kSerialFill && nxt < nht) issue(nxt, bnext);
+        uint32_t sk[NS];
+        skips(cur, sk);
+        qk<D, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+#pragma unroll
+        for (int sub = 0; sub < NS; ++sub) {
+            const uint32_t bits = sk[sub] >> (4 * half);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
+        }
+        softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
+        pv<D, 0, NS>(bcur + HALF, pk, lane, o);
+        if (kSerialFill) {
+            lds_barrier();                               // every wave is done with step cur
+            if (nxt < nht) issue(nxt, bnext);
+        }
+        cur = nxt;
+    };
+    while (cur < nht) {
+        step(buf0, buf1);
+        if (cur >= nht) break;
+        step(buf1, buf0);
+    }
+    lds_barrier();                                       // buffers free for the output staging
 }
 
 }  // namespace fp_walk

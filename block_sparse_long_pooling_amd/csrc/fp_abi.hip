@@ -273,15 +273,7 @@ FP_EXPORT int64_t fp_attention_workgroups(const fp_params* params, const int32_t
     SeqTable t;
     if (check_params(params) || build_table(*params, cu_seqlens_host, nullptr, batch, 1, t)) return -1;
     if (paged != 0 && paged != 1) return -1;
-    if (params->dtype == FP_DTYPE_FP8_E4M3FN) return (int64_t)t.total_items * params->num_q_heads;
-    AttnArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.Hq = params->num_q_heads;
-    a.Hkv = params->num_kv_heads;
-    a.g = a.Hq / a.Hkv;
-    (void)hipGetLastError();
-    const int n = attn_bf16_grid(a, t, params->head_dim, params->block_size, paged != 0);
-    return n;
+    return (int64_t)t.total_items * params->num_q_heads;
 }
 
 FP_EXPORT size_t fp_varlen_workspace_bytes(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch) {

@@ -81,7 +81,4 @@ hipError_t launch_pool(const PoolArgs& a, const SeqTable& t, bool paged, hipStre
 hipError_t launch_quant_pool(const QuantArgs& a, const SeqTable& t, bool paged, bool chunk, hipStream_t s);
 hipError_t launch_select(const SelArgs& a, const SeqTable& t, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);
-// Workgroups launch_attn_bf16 uses for these arguments (0 without items, -1
-// for an unsupported shape).
-int attn_bf16_grid(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged);
 hipError_t launch_attn_fp8(const AttnArgs& a, const SeqTable& t, int D, int B, bool paged, hipStream_t s);

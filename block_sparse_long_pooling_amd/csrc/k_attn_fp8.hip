@@ -152,94 +152,6 @@ __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, fl
     }
 }
 
-// Mean-correction pass over the skipped past blocks J < I of row block I:
-// BLK/2 pooled blocks per step, double-buffered DMA into buf0 / buf1 (each a
-// [BLK][D] bf16 tile buffer: BLK/2 K_bar rows, then BLK/2 V_bar rows, chunks
-// swizzled per row).
-template <int D, int BLK>
-__device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable& t, int b, int I, int hk, int cnt,
-                                               const int32_t* list, const bf16x8* qf, char* buf0, char* buf1,
-                                               uint32_t* kept_bits, int tid, int col, int half, float c, float& m,
-                                               float& l, f32x16* o) {
-    constexpr int NT = 2 * BLK;                          // threads
-    constexpr int HT = BLK / 2;                          // pooled blocks per step
-    constexpr int NS = HT / 32;                          // 32-key subtiles per step
-    constexpr int HALF = HT * D * 2;                     // bytes of K_bar (or V_bar) rows per step
-    const int lane = tid & 63;
-    const int nwords = (I + 31) >> 5;
-    for (int i = tid; i < nwords; i += NT) kept_bits[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < cnt; i += NT) {
-        const int J = list[i];
-        if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
-    }
-    __syncthreads();
-    const uint16_t* kfirst = a.pk16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
-    const uint16_t* vfirst = a.pv16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
-    DmaPlan<D, HT, NT> plan;
-    plan.init(tid);
-    const int wave_base = __builtin_amdgcn_readfirstlane(64 * (tid >> 6) * 16);
-    const float log2_blk = __log2f((float)BLK);          // every block J < I is full
-    const int nht = (I + HT - 1) / HT;
-    // Skip bits of step hh: bit j of word sub <=> block HT hh + 32 sub + j is past and not kept.
-    auto skips = [&](int hh, uint32_t* sk) {
-        uint32_t any = 0;
-#pragma unroll
-        for (int sub = 0; sub < NS; ++sub) {
-            const int j0 = HT * hh + 32 * sub;
-            const int nvalid = min(32, max(0, I - j0));
-            const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-            sk[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[j0 >> 5] & valid);
-            any |= sk[sub];
-        }
-        return any != 0;
-    };
-    auto next_step = [&](int hh) {
-        uint32_t sk[NS];
-        for (++hh; hh < nht; ++hh)
-            if (skips(hh, sk)) return hh;
-        return nht;
-    };
-    auto issue = [&](int hh, char* dst) {
-        const int nvalid = I - HT * hh;
-        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
-        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
-    };
-    f32x16 s[NS];
-    uint32_t pk[NS][8];
-    int cur = next_step(-1);
-    if (cur < nht) issue(cur, buf0);
-    auto step = [&](char* bcur, char* bnext) {
-        __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
-        lds_barrier();                                   // ... every thread's; the other buffer is free
-        const int nxt = next_step(cur);
-        if (!kSerialFill && nxt < nht) issue(nxt, bnext);
-        uint32_t sk[NS];
-        skips(cur, sk);
-        qk<D, BLK, 1, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
-#pragma unroll
-        for (int sub = 0; sub < NS; ++sub) {
-            const uint32_t bits = sk[sub] >> (4 * half);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
-        }
-        softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
-        pv<D, BLK, 1, 0, NS>(bcur + HALF, pk, lane, o);
-        if (kSerialFill) {
-            lds_barrier();                               // every wave is done with step cur
-            if (nxt < nht) issue(nxt, bnext);
-        }
-        cur = nxt;
-    };
-    while (cur < nht) {
-        step(buf0, buf1);
-        if (cur >= nht) break;
-        step(buf1, buf0);
-    }
-    lds_barrier();                                       // buffers free for the output staging
-}
-
 template <int D, int BLK, bool PAGED>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t) {
     using T = Tile<D, BLK>;          // bf16 geometry: LDS sized for the correction tiles

@@ -342,14 +342,10 @@ int64_t fp_count_entries(const fp_params* params, const int32_t* cu_seqlens_host
 size_t  fp_varlen_workspace_bytes(const fp_params* params, const int32_t* cu_seqlens_host,
                                   int32_t batch);
 
-/* Workgroups the attention kernel is launched with for these arguments on
- * the current device (host only, no device work; it reads the device's
- * compute-unit count and the kernel's occupancy).  bf16: the persistent grid,
- * the number of workgroups of this kernel variant (head_dim, block_size, head
- * packing, paged or not) that the device holds at once, rounded down to a
- * multiple of 8 and at most one per work item.  fp8: one workgroup per
- * (query block, query head).  paged: 0 for fp_sparse_prefill_fwd, 1 for the
- * paged entries.  Returns -1 on invalid arguments. */
+/* Workgroups the attention kernel is launched with for these arguments
+ * (host only, no device work): one per (query block, query head), bf16 and
+ * fp8 alike, contiguous (paged = 0, fp_sparse_prefill_fwd) or paged
+ * (paged = 1, the paged entries).  Returns -1 on invalid arguments. */
 int64_t fp_attention_workgroups(const fp_params* params, const int32_t* cu_seqlens_host, int32_t batch,
                                 int32_t paged);
 

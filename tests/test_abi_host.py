@@ -61,12 +61,16 @@ def test_sizes():
 
 
 def test_attention_workgroups_host():
-    """fp8 attention launches one workgroup per (query block, head); bad
-    arguments give -1 (the bf16 persistent grid needs a device and is checked
-    by the GPU tests)."""
+    """Attention launches one workgroup per (query block, head), bf16 and fp8,
+    contiguous or paged; bad arguments give -1."""
     p8 = _p(dtype=fp.FP_DTYPE_FP8_E4M3FN)
-    assert fp.fp_attention_workgroups(p8, [0, 1000]) == 32 * 8
-    assert fp.fp_attention_workgroups(p8, [0, 100, 300, 300, 1000]) == 32 * (1 + 2 + 0 + 6)
+    for p in (_p(), p8):
+        for paged in (False, True):
+            assert fp.fp_attention_workgroups(p, [0, 1000], paged=paged) == 32 * 8
+            assert fp.fp_attention_workgroups(p, [0, 100, 300, 300, 1000], paged=paged) == 32 * (1 + 2 + 0 + 6)
+    p64 = _p(block_size=64)
+    assert fp.fp_attention_workgroups(p64, [0, 1000]) == 32 * 16
+    assert fp.fp_attention_workgroups(_p(), [0, 0]) == 0
     assert fp.fp_attention_workgroups(_p(head_dim=96), [0, 1000]) == -1
     assert fp.fp_attention_workgroups(_p(), [1, 1000]) == -1
     cu = (ctypes.c_int32 * 2)(0, 1000)

@@ -2,8 +2,8 @@
 benchmark times: every block list against the oracle's selection (bit-exact
 outside the threshold band), and outputs of a sample of (head, query block)
 pairs -- always including the first and last query blocks, at 32K and 128K
-one pair in every band of the persistent attention grid and every XCD slot,
-and 16 pairs per request of the paged batch -- against the oracle evaluated
+64 workgroups spread over the attention launch and every XCD slot, and 16
+pairs per request of the paged batch -- against the oracle evaluated
 under the GPU's mask."""
 import numpy as np
 import pytest
@@ -26,24 +26,20 @@ def _sample_pairs(Hq, nB, n, seed):
     return sorted(pairs)
 
 
-def _band_pairs(Hq, nB, grid, HP=2):
-    """One (head, query block) pair per band of `grid` consecutive work items
-    of the persistent attention kernel (items: query blocks longest first,
-    times the Hq / HP head pairs, heads of one KV head on one XCD), taking
-    XCD slot k mod 8 in band k, so every band and every XCD slot is sampled."""
-    npairs = Hq // HP
-    nitems = nB * npairs
+def _launch_pairs(Hq, nB, grid):
+    """(head, query block) pairs of 64 workgroups evenly spaced over the
+    attention launch (one workgroup per pair: query blocks longest first, the
+    heads of one KV head on one XCD), every head and XCD slot among them."""
+    assert grid == nB * Hq
 
     def xcd_head(slot):
-        return (slot % 8) * (npairs // 8) + slot // 8 if npairs % 8 == 0 else slot
+        return (slot % 8) * (Hq // 8) + slot // 8 if Hq % 8 == 0 else slot
 
     pairs = set()
-    for k in range((nitems + grid - 1) // grid):
-        idx = k * grid + k % 8 + 8 * ((5 * k) % max(1, grid // 8))
-        if idx >= nitems:
-            idx = min(nitems - 1, k * grid + k % 8)
-        rank, slot = divmod(idx, npairs)
-        pairs.add((HP * xcd_head(slot) + k % HP, nB - 1 - rank))
+    for k in range(64):
+        idx = min(grid - 1, k * grid // 64 + (5 * k) % Hq)
+        rank, slot = divmod(idx, Hq)
+        pairs.add((xcd_head(slot), nB - 1 - rank))
     return pairs
 
 
@@ -89,9 +85,9 @@ def _check_full(seq, alpha, n_pairs, seed):
     # pooled means against the oracle's
     np.testing.assert_allclose(sel.pooled_k.cpu().numpy(), ref.k_bar, rtol=0, atol=1e-5)
     grid = fp.fp_attention_workgroups(p, [0, S])
-    bands = _band_pairs(Hq, nB, grid)
-    pairs = sorted(set(_sample_pairs(Hq, nB, n_pairs, seed)) | bands)
-    print(f"  grid {grid}: {len(bands)} pairs over the persistent bands", flush=True)
+    spread = _launch_pairs(Hq, nB, grid)
+    pairs = sorted(set(_sample_pairs(Hq, nB, n_pairs, seed)) | spread)
+    print(f"  grid {grid}: {len(spread)} pairs spread over the launch", flush=True)
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, ref, True, pairs=pairs, keep=mask)
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()

@@ -4,8 +4,9 @@ reading the tile before it (built with FP_SERIAL_DMA=1).  Both run the same
 arithmetic in the same order, so every output -- lists, counts, pooled
 means, O, LSE, fp8 codes -- must be bit-identical; a fill that raced with a
 read in the pipelined kernels would show as a difference.  The cases span
-several bands of the persistent attention grid, kept and correction tiles,
-the paged and chunked walks, and the fp8 kept and correction pipelines."""
+the bf16 kernel at block sizes 128 and 64 (thousands of workgroups, kept
+and correction tiles, a last block of at most 64 tokens), the paged and
+chunked walks, and the fp8 kept and correction pipelines."""
 import contextlib
 import ctypes
 import os
@@ -62,9 +63,10 @@ def _equal(a, b, what):
 
 
 @pytest.mark.parametrize("S,Hq,Hkv,d,B,alpha", [
-    (16384, 32, 8, 128, 128, 0.1),     # 2048 items: 8 bands of the 256-workgroup grid
+    (16384, 32, 8, 128, 128, 0.1),     # 4096 workgroups
     (16384, 32, 8, 128, 128, 0.0),     # every block kept
-    (5000, 4, 1, 64, 64, 0.3),         # ragged last block, HP = 2 of g = 4
+    (16420, 8, 2, 128, 128, 0.2),      # last block of 36 tokens: one 64-key tile
+    (5000, 4, 1, 64, 64, 0.3),         # ragged last block, block size 64
 ])
 def test_bf16_single_sequence_serial_equals_pipelined(S, Hq, Hkv, d, B, alpha):
     print(f"serial fill bf16 S={S} Hq={Hq} d={d} B={B} alpha={alpha}", flush=True)
