@@ -196,7 +196,8 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
             const int j0 = HT * hh + 32 * sub;
             const int nvalid = min(32, max(0, I - j0));
             const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-            sk[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[j0 >> 5] & valid);
+            // (a word past the bitmap can only occur with no valid block in it)
+            sk[sub] = __builtin_amdgcn_readfirstlane(~kept_bits[min(j0 >> 5, FP_MAX_BLOCKS / 32 - 1)] & valid);
             any |= sk[sub];
         }
         return any != 0;
