@@ -6,24 +6,25 @@
 //
 // One workgroup per (query block I, query head h): BLK/32 waves of 32 query
 // rows, at least two workgroups per CU.  The workgroup walks h's ascending
-// list of kept blocks as tiles of 64 keys (BLK/64 per block).  Per tile,
-// each wave computes
+// list of kept blocks as tiles of KT keys (64, or 32 at d = 128 with block
+// size 64; BLK/KT tiles per block).  Per tile, each wave computes
 //     S^T = K Q^T        v_mfma_f32_32x32x16_bf16, lane = query, 16 keys per
 //                        32-key subtile in registers
 //     online softmax     exp2 domain; row statistics are per-lane scalars
 //                        combined with the partner lane l ^ 32
 //     O^T += V^T P^T     P straight from registers; V^T operand read from the
 //                        row-major V rows with ds_read_b64_tr_b16
-// A tile buffer holds the tile's 64 K rows, then its 64 V rows, row-major
-// [64][D] bf16 with 16-byte chunks XOR-swizzled per row (32 KiB at d = 128).
-// Tiles arrive by global_load_lds_dwordx4 (DMA into LDS, no registers) into
-// two alternating buffers: the next tile's DMA is issued right after the one
-// barrier per tile and lands while the current tile is computed.  Rows past
-// a request's end re-read its last row (contiguous layout) or a zero chunk
-// (paged layout, also for out-of-range pages); the causal mask of the
-// diagonal block removes them, and a tile that lies wholly past the end (the
-// second half of a last block of at most 64 tokens) is not visited.  On the
-// diagonal block a wave whose rows all precede a tile's keys skips it.
+// A tile buffer holds the tile's KT K rows, then its KT V rows, row-major
+// [KT][D] bf16 with 16-byte chunks XOR-swizzled per row (32 KiB for 64 keys
+// at d = 128).  Tiles arrive by global_load_lds_dwordx4 (DMA into LDS, no
+// registers) into two alternating buffers: the next tile's DMA is issued
+// right after the one barrier per tile and lands while the current tile is
+// computed.  Rows past a request's end re-read its last row (contiguous
+// layout) or a zero chunk (paged layout, also for out-of-range pages); the
+// causal mask of the diagonal block removes them, and a tile that lies wholly
+// past the end (a tile of the last block after its last token) is not
+// visited.  On the diagonal block a wave whose rows all precede a tile's keys
+// skips it.
 //
 // With one head per workgroup no wave idles through a tile that only another
 // head keeps, and the resident workgroups of a CU hide each other's barrier
@@ -39,18 +40,20 @@
 namespace {
 using namespace fp_walk;
 
-// Two waves per SIMD; at d = 128 and block size 64 the LDS holds two
-// two-wave workgroups per CU, i.e. one wave per SIMD.
+// Keys per tile: 64, or 32 at d = 128 and block size 64, where 64-key
+// buffers would leave room for only two 2-wave workgroups per CU (one wave
+// per SIMD); with 32-key buffers four fit, two waves per SIMD.
 template <int D, int BLK>
-constexpr int kWavesPerSimd = (D == 128 && BLK == 64) ? 1 : 2;
+constexpr int kTileKeys = (D == 128 && BLK == 64) ? 32 : 64;
 
 template <int D, int BLK, bool PAGED>
-__global__ __launch_bounds__(2 * BLK, (kWavesPerSimd<D, BLK>)) void k_attn_bf16(AttnArgs a, SeqTable t) {
-    constexpr int KT = 64;                               // keys per tile
+__global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t) {
+    constexpr int KT = kTileKeys<D, BLK>;               // keys per tile
     constexpr int NH = BLK / KT;                         // tiles per KV block
     constexpr int NT = 2 * BLK;
     constexpr int NDS = D / 32;
     constexpr int VOFF = KT * D * 2;                     // bytes of a tile's K rows
+    constexpr int NSB = KT / 32;                         // 32-key subtiles per tile
     constexpr int BUF = 2 * KT * D * 2;
     static_assert(BUF >= BLK * D * 2, "a tile buffer also stages the output block");
     __shared__ __attribute__((aligned(16))) char buf0[BUF];
@@ -91,8 +94,8 @@ __global__ __launch_bounds__(2 * BLK, (kWavesPerSimd<D, BLK>)) void k_attn_bf16(
     f32x16 o[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) o[ds] = f32x16{};
-    f32x16 s[2];
-    uint32_t pk[2][8];
+    f32x16 s[NSB];
+    uint32_t pk[NSB][8];
     const float c = a.scale_log2;
 
     DmaPlan<D, KT, NT> plan;
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(2 * BLK, (kWavesPerSimd<D, BLK>)) void k_attn_bf16(
     const uint16_t* kfirst = static_cast<const uint16_t*>(a.k) + base;
     const uint16_t* vfirst = static_cast<const uint16_t*>(a.v) + base;
     const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
-    // Tile code = NH J + hh: keys KT code .. KT code + 63 of the request.
+    // Tile code = NH J + hh: keys KT code .. KT code + KT - 1 of the request.
     // Paged layout: pg holds the page ids of the next tile to issue, loaded a
     // step ahead so the issue does not wait on the block table.
     int pg[NLOAD];
@@ -159,22 +162,22 @@ __global__ __launch_bounds__(2 * BLK, (kWavesPerSimd<D, BLK>)) void k_attn_bf16(
         if (!kSerialFill) prefetch();
         const int J = code / NH, hh = code % NH;
         if (J != I || 32 * w + 31 >= KT * hh) {
-            qk<D, 0, 2>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+            qk<D, 0, NSB>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
             if (J == I) {
                 // Causal mask of the diagonal block (opaque limit: the lane
                 // masks are computed here, not hoisted and held).
                 int lim = qr - 4 * half - KT * hh;
                 asm volatile("" : "+v"(lim));
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NSB; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = 32 * j + (r & 3) + 8 * (r >> 2);
                         s[j][r] = key > lim ? -INFINITY : s[j][r];
                     }
             }
-            softmax_update<2, NDS>(s, c, 0.f, m, l, o, pk);
-            pv<D, 0, 2>(bcur + VOFF, pk, lane, o);
+            softmax_update<NSB, NDS>(s, c, 0.f, m, l, o, pk);
+            pv<D, 0, NSB>(bcur + VOFF, pk, lane, o);
         }
         if (kSerialFill) {
             lds_barrier();                               // every wave is done with the tile
