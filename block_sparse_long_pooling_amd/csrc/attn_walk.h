@@ -225,13 +225,19 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
         uint32_t sk[NS];
         skips(cur, sk);
         qk<D, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+        // Element r of a lane in half hf is block 32 sub + (r & 3) + 8 (r >> 2)
+        // + 4 hf.  The skip words are uniform, so each element's keep mask is
+        // built on the scalar unit as a 64-lane mask and applied with one
+        // select.
 #pragma unroll
-        for (int sub = 0; sub < NS; ++sub) {
-            const uint32_t bits = sk[sub] >> (4 * half);
+        for (int sub = 0; sub < NS; ++sub)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[sub][r] = ((bits >> ((r & 3) + 8 * (r >> 2))) & 1u) ? s[sub][r] : -INFINITY;
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int k0 = (r & 3) + 8 * (r >> 2);
+                const uint64_t keep = (((sk[sub] >> k0) & 1u) ? 0xffffffffull : 0ull) |
+                                      (((sk[sub] >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+                s[sub][r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[sub][r] : -INFINITY;
+            }
         softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
         pv<D, 0, NS>(bcur + HALF, pk, lane, o);
         if (kSerialFill) {
