@@ -73,6 +73,20 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
         // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
         // addressing form).
         const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * ROWS * rs);
+        if (nvalid >= ROWS) {
+            // Whole tile: load i's row offset is the thread's first row's plus
+            // a uniform step, so no multiply per load.  The base is opaque so
+            // the compiler keeps one register, not one offset per load.
+            int rbase = plan.row0 * (int)rs;
+            asm volatile("" : "+v"(rbase));
+#pragma unroll
+            for (int i = 0; i < P::NLOAD; ++i) {
+                const uint32_t off = (uint32_t)(rbase + i * P::ROWSTEP * (int)rs + plan.coff(i)) * 2u;
+                __builtin_amdgcn_global_load_lds(tile + off, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, 0,
+                                                 0);
+            }
+            return;
+        }
         // Rows past the end of the sequence re-read its last row: they occur
         // only on the diagonal block, where the causal mask removes them, and
         // finite values keep 0 * v at 0.  The row index is opaque so the
