@@ -173,13 +173,14 @@ __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int 
     }
 }
 
-// Mean-correction pass over the skipped past blocks J < I of row block I:
+// Mean-correction pass over the skipped past blocks J < I of row block I
+// (I > 0); J0 is list entry tid (any value when tid >= cnt):
 // BLK/2 pooled blocks per step, double-buffered DMA into buf0 / buf1 (each a
 // [BLK][D] bf16 tile buffer: BLK/2 K_bar rows, then BLK/2 V_bar rows, chunks
 // swizzled per row).
 template <int D, int BLK>
 __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable& t, int b, int I, int hk, int cnt,
-                                               const int32_t* list, const bf16x8* qf, char* buf0, char* buf1,
+                                               const int32_t* list, int J0, const bf16x8* qf, char* buf0, char* buf1,
                                                uint32_t* kept_bits, int tid, int col, int half, float c, float& m,
                                                float& l, f32x16* o) {
     constexpr int NT = 2 * BLK;                          // threads
@@ -187,14 +188,6 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
     constexpr int NS = HT / 32;                          // 32-key subtiles per step
     constexpr int HALF = HT * D * 2;                     // bytes of K_bar (or V_bar) rows per step
     const int lane = tid & 63;
-    const int nwords = (I + 31) >> 5;
-    for (int i = tid; i < nwords; i += NT) kept_bits[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < cnt; i += NT) {
-        const int J = list[i];
-        if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
-    }
-    __syncthreads();
     const uint16_t* kfirst = a.pk16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
     const uint16_t* vfirst = a.pv16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
     DmaPlan<D, HT, NT> plan;
@@ -202,6 +195,29 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * (tid >> 6) * 16);
     const float log2_blk = __log2f((float)BLK);          // every block J < I is full
     const int nht = (I + HT - 1) / HT;
+    auto issue = [&](int hh, char* dst) {
+        const int nvalid = I - HT * hh;
+        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
+        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
+    };
+    // The bitmap of kept past blocks is rebuilt from the list: J0, list
+    // entry tid, was loaded by the caller long before, so the marks wait on
+    // no memory.  Step 0's DMA goes out right after them (an LDS access
+    // while a DMA into LDS is in flight would wait for it), before the
+    // barrier that publishes the bitmap.  Step 0 (blocks 0 .. HT-1) is taken
+    // whether or not it holds a skipped block: a step with every block kept
+    // is fully masked and leaves m, l and O as they are.
+    const int nwords = (I + 31) >> 5;
+    for (int i = tid; i < nwords; i += NT) kept_bits[i] = 0u;
+    lds_barrier();
+    if (tid < cnt && J0 < I) atomicOr(&kept_bits[J0 >> 5], 1u << (J0 & 31));
+    for (int i = tid + NT; i < cnt; i += NT) {
+        const int J = list[i];
+        if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
+    }
+    if (!kSerialFill) issue(0, buf0);
+    lds_barrier();
+    if (kSerialFill) issue(0, buf0);
     // Skip bits of step hh: bit j of word sub <=> block HT hh + 32 sub + j is past and not kept.
     auto skips = [&](int hh, uint32_t* sk) {
         uint32_t any = 0;
@@ -222,15 +238,9 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
             if (skips(hh, sk)) return hh;
         return nht;
     };
-    auto issue = [&](int hh, char* dst) {
-        const int nvalid = I - HT * hh;
-        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
-        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
-    };
     f32x16 s[NS];
     uint32_t pk[NS][8];
-    int cur = next_step(-1);
-    if (cur < nht) issue(cur, buf0);
+    int cur = 0;
     auto step = [&](char* bcur, char* bnext) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
         lds_barrier();                                   // ... every thread's; the other buffer is free

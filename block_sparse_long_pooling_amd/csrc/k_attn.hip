@@ -80,6 +80,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     const int hk = h / a.g;
     const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, first);
     const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)];
+    const int J0 = list[min(tid, I)];                    // for the correction's bitmap (capacity I + 1)
     const int qr = 32 * w + col;
     // Rows outside lo .. nI-1 re-read the nearest valid row; they are never stored.
     bf16x8 qf[D / 16];
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     }
     lds_barrier();                                       // the last tile is read
     if (a.correction && I > 0)
-        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, qf, buf0, buf1, kept_bits, tid, col, half, c, m, l, o);
+        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qf, buf0, buf1, kept_bits, tid, col, half, c, m, l, o);
     store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, reinterpret_cast<uint4*>(buf0), tid);
 }
 

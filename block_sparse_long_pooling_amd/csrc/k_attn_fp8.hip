@@ -179,6 +179,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     const int hk = h / a.g;
     const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, first);
     const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)];
+    const int J0 = list[min(tid, I)];                    // for the correction's bitmap (capacity I + 1)
     const int qr = 32 * w + col;
     const uint8_t* q8 = static_cast<const uint8_t*>(a.q);
     const uint8_t* k8 = static_cast<const uint8_t*>(a.k);
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
                                         pack_bf16(f2.x * sq, f2.y * sq), pack_bf16(f3.x * sq, f3.y * sq));
             qb[kk] = __builtin_bit_cast(bf16x8, pk);
         }
-        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, qb, reinterpret_cast<char*>(lk),
+        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qb, reinterpret_cast<char*>(lk),
                                reinterpret_cast<char*>(lv), kept_bits, tid, col, half, a.scale_log2, m, l, o);
     }
     store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, lk, tid);
