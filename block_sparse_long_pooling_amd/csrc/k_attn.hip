@@ -80,8 +80,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     const int hk = h / a.g;
     const int32_t* list = a.kv_idx + list_row(t, b, h, I, nb, first);
     const int cnt = a.kv_cnt[count_index(t, a.Hq, b, h, I, nb, first)];
-    const int J0 = list[min(tid, I)];                    // for the correction's bitmap (capacity I + 1)
     const int qr = 32 * w + col;
+    // The list's first window (entries lane, within its capacity I + 1) and
+    // entry tid (for the correction's bitmap) load before Q: waiting for the
+    // window, which names the first tile, then does not wait for the Q rows
+    // as well (the vector-memory counter is in order).
+    int wJ = list[min(lane, I)];
+    const int J0 = list[min(tid, I)];
     // Rows outside lo .. nI-1 re-read the nearest valid row; they are never stored.
     bf16x8 qf[D / 16];
     {
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     };
     // The list is read 64 entries at a time, one per lane, bounded by its
     // capacity I + 1 (entries past the count are never used).
-    int wbase = 0, wJ = 0;
+    int wbase = 0;
     auto load_window = [&](int wb) {
         wbase = wb;
         wJ = list[min(wb + lane, I)];
@@ -140,7 +145,6 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
         }
         return NH * gJ + gh;
     };
-    load_window(0);
     int code = next_code();
     if (code >= 0) {
         load_pages(code);
