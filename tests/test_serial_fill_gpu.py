@@ -5,7 +5,8 @@ arithmetic in the same order, so every output -- lists, counts, pooled
 means, O, LSE, fp8 codes -- must be bit-identical; a fill that raced with a
 read in the pipelined kernels would show as a difference.  The cases span
 the bf16 kernel at block sizes 128 and 64 (thousands of workgroups, kept
-and correction tiles, a last block of at most 64 tokens), the paged and
+and correction tiles, a last block of at most 64 tokens, the 32-key tiles
+of d = 128 at block size 64), the paged and
 chunked walks, and the fp8 kept and correction pipelines."""
 import contextlib
 import ctypes
@@ -67,6 +68,7 @@ def _equal(a, b, what):
     (16384, 32, 8, 128, 128, 0.0),     # every block kept
     (16420, 8, 2, 128, 128, 0.2),      # last block of 36 tokens: one 64-key tile
     (5000, 4, 1, 64, 64, 0.3),         # ragged last block, block size 64
+    (3000, 8, 2, 128, 64, 0.2),        # d 128 at block size 64: 32-key tiles
 ])
 def test_bf16_single_sequence_serial_equals_pipelined(S, Hq, Hkv, d, B, alpha):
     print(f"serial fill bf16 S={S} Hq={Hq} d={d} B={B} alpha={alpha}", flush=True)
