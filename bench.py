@@ -57,6 +57,70 @@ def measured_traffic():
     return int(rec["traffic_bytes"])
 
 
+def _counter_rows(folder):
+    """(kernel name, counter, value) of every dispatch in the rocprofv3
+    counter-collection CSV files under folder."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+    return rows
+
+
+def traffic_record(fetch_dir, write_dir):
+    """Write the calibrated HBM-traffic record of the attention kernel from two
+    rocprofv3 --pmc runs of `bench.py --quick --layouts --steps 2 --warmup 0
+    --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  The 1 GiB
+    device copy of --copy-probe calibrates each counter: factor = bytes the copy
+    must move / bytes the counter reports for it.  Prints a per-kernel table."""
+    import hashlib
+    per = {}
+    for folder, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for name, cname, val, _ in _counter_rows(folder):
+            if cname != counter:
+                continue
+            per.setdefault(name, {}).setdefault(counter, []).append(val)
+    copy = [n for n in per if "copy" in n.lower() and max(per[n].get("WRITE_SIZE", [0])) > 1e6]
+    if not copy:
+        raise SystemExit("no 1 GiB copy dispatch found (run with --copy-probe)")
+    cname = max(copy, key=lambda n: max(per[n]["WRITE_SIZE"]))
+    gib_kib = float(1 << 20)
+    ff = gib_kib / max(per[cname]["FETCH_SIZE"])
+    wf = gib_kib / max(per[cname]["WRITE_SIZE"])
+    key = "k_attn_bf16<128, 128, false>"
+    attn = [n for n in per if key in n]
+    if not attn:
+        raise SystemExit(f"no {key} dispatch found")
+    fk = statistics.mean(per[attn[0]]["FETCH_SIZE"])
+    wk = statistics.mean(per[attn[0]]["WRITE_SIZE"])
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_sparse_long_pooling_amd", "csrc", f), "rb").read())
+    rec = {"kernel": key, "source_sha256": h.hexdigest(), "fetch_kib": fk, "write_kib": wk,
+           "fetch_factor": ff, "write_factor": wf, "traffic_bytes": (fk * ff + wk * wf) * 1024.0,
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
+               "python3 bench.py --quick --layouts --steps 2 --warmup 0 --copy-probe",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- "
+               "python3 bench.py --quick --layouts --steps 2 --warmup 0 --copy-probe"]}
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"copy calibration ({cname[:60]}): FETCH factor {ff:.4f}, WRITE factor {wf:.4f}")
+    print("| kernel | dispatches | FETCH_SIZE (KiB, mean) | WRITE_SIZE (KiB, mean) | read (GiB) | write (GiB) |")
+    print("|---|---|---|---|---|---|")
+    for n in sorted(per):
+        if not any(k in n for k in ("k_pool", "k_select", "k_quant", "k_attn")):
+            continue
+        f_ = statistics.mean(per[n].get("FETCH_SIZE", [0.0]))
+        w_ = statistics.mean(per[n].get("WRITE_SIZE", [0.0]))
+        print(f"| `{n[:70]}` | {len(per[n].get('FETCH_SIZE', []))} | {f_:.0f} | {w_:.0f} | "
+              f"{f_ * ff / gib_kib:.3f} | {w_ * wf / gib_kib:.3f} |")
+    print(f"record: {TRAFFIC_RECORD}: {rec['traffic_bytes']:.4g} bytes per attention launch")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -80,6 +144,9 @@ def parse():
     ap.add_argument("--no-parity", action="store_true", help="skip the parity summary")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: write the attention kernel's calibrated traffic record from two "
+                         "rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) and print a table")
     return ap.parse_args()
 
 
@@ -138,6 +205,9 @@ def time_steps(fn_sel, fn_attn, steps, stream):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the path is built and "
               "timed on a single MI355X; see the design notes for how it would shard.", file=sys.stderr)

@@ -175,18 +175,17 @@ __device__ __forceinline__ void pv(const char* vt, const uint32_t (*pk)[8], int 
 
 // Mean-correction pass over the skipped past blocks J < I of row block I
 // (I > 0); J0 is list entry tid (any value when tid >= cnt):
-// BLK/2 pooled blocks per step, double-buffered DMA into buf0 / buf1 (each a
-// [BLK][D] bf16 tile buffer: BLK/2 K_bar rows, then BLK/2 V_bar rows, chunks
-// swizzled per row).
+// BLK/2 pooled blocks per step, double-buffered DMA: step buffers (k0, v0)
+// and (k1, v1), each [BLK/2][D] bf16 (K_bar rows in k, V_bar rows in v,
+// chunks swizzled per row).
 template <int D, int BLK>
 __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable& t, int b, int I, int hk, int cnt,
-                                               const int32_t* list, int J0, const bf16x8* qf, char* buf0, char* buf1,
-                                               uint32_t* kept_bits, int tid, int col, int half, float c, float& m,
-                                               float& l, f32x16* o) {
+                                               const int32_t* list, int J0, const bf16x8* qf, char* k0, char* v0,
+                                               char* k1, char* v1, uint32_t* kept_bits, int tid, int col, int half,
+                                               float c, float& m, float& l, f32x16* o) {
     constexpr int NT = 2 * BLK;                          // threads
     constexpr int HT = BLK / 2;                          // pooled blocks per step
     constexpr int NS = HT / 32;                          // 32-key subtiles per step
-    constexpr int HALF = HT * D * 2;                     // bytes of K_bar (or V_bar) rows per step
     const int lane = tid & 63;
     const uint16_t* kfirst = a.pk16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
     const uint16_t* vfirst = a.pv16 + ((int64_t)hk * t.total_blocks + t.blk_off[b]) * D;
@@ -195,10 +194,10 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
     const int wave_base = __builtin_amdgcn_readfirstlane(64 * (tid >> 6) * 16);
     const float log2_blk = __log2f((float)BLK);          // every block J < I is full
     const int nht = (I + HT - 1) / HT;
-    auto issue = [&](int hh, char* dst) {
+    auto issue = [&](int hh, char* kd, char* vd) {
         const int nvalid = I - HT * hh;
-        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst, wave_base);
-        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, dst + HALF, wave_base);
+        issue_tile<D, HT, NT, false>(kfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, kd, wave_base);
+        issue_tile<D, HT, NT, false>(vfirst, nullptr, a.kv, D, hh, nvalid, plan, &kZeroChunk, vd, wave_base);
     };
     // The bitmap of kept past blocks is rebuilt from the list: J0, list
     // entry tid, was loaded by the caller long before, so the marks wait on
@@ -215,9 +214,9 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
         const int J = list[i];
         if (J < I) atomicOr(&kept_bits[J >> 5], 1u << (J & 31));
     }
-    if (!kSerialFill) issue(0, buf0);
+    if (!kSerialFill) issue(0, k0, v0);
     lds_barrier();
-    if (kSerialFill) issue(0, buf0);
+    if (kSerialFill) issue(0, k0, v0);
     // Skip bits of step hh: bit j of word sub <=> block HT hh + 32 sub + j is past and not kept.
     auto skips = [&](int hh, uint32_t* sk) {
         uint32_t any = 0;
@@ -241,14 +240,14 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
     f32x16 s[NS];
     uint32_t pk[NS][8];
     int cur = 0;
-    auto step = [&](char* bcur, char* bnext) {
+    auto step = [&](char* kc, char* vc, char* kn, char* vn) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of step cur is done
-        lds_barrier();                                   // ... every thread's; the other buffer is free
+        lds_barrier();                                   // ... every thread's; the other buffers are free
         const int nxt = next_step(cur);
-        if (!kSerialFill && nxt < nht) issue(nxt, bnext);
+        if (!kSerialFill && nxt < nht) issue(nxt, kn, vn);
         uint32_t sk[NS];
         skips(cur, sk);
-        qk<D, 0, NS>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+        qk<D, 0, NS>(reinterpret_cast<const uint4*>(kc), qf, col, half, s);
         // Element r of a lane in half hf is block 32 sub + (r & 3) + 8 (r >> 2)
         // + 4 hf.  The skip words are uniform, so each element's keep mask is
         // built on the scalar unit as a 64-lane mask and applied with one
@@ -263,17 +262,17 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
                 s[sub][r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[sub][r] : -INFINITY;
             }
         softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
-        pv<D, 0, NS>(bcur + HALF, pk, lane, o);
+        pv<D, 0, NS>(vc, pk, lane, o);
         if (kSerialFill) {
             lds_barrier();                               // every wave is done with step cur
-            if (nxt < nht) issue(nxt, bnext);
+            if (nxt < nht) issue(nxt, kn, vn);
         }
         cur = nxt;
     };
     while (cur < nht) {
-        step(buf0, buf1);
+        step(k0, v0, k1, v1);
         if (cur >= nht) break;
-        step(buf1, buf0);
+        step(k1, v1, k0, v0);
     }
     lds_barrier();                                       // buffers free for the output staging
 }

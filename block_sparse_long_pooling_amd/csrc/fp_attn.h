@@ -18,6 +18,20 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Row statistics of a query live in lanes l and l ^ 32.  v_permlane32_swap
+// exchanges the halves of two copies of v, which then hold the lower and the
+// upper half's value in every lane: a register move, where a lane shuffle
+// (ds_bpermute) would be an LDS round trip in the middle of the softmax.  Both
+// lanes of a pair get the same bits.
+__device__ __forceinline__ float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int BLK>
 struct Tile {
     static constexpr int NW = BLK / 32;     // waves per workgroup
@@ -46,7 +60,7 @@ __device__ __forceinline__ void softmax_update(f32x16* s, float c, float bias, f
     for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = pair_max(mt);
     const float mt2 = (mt == -INFINITY) ? -INFINITY : fmaf(mt, c, bias);
     const bool grow = mt2 > m + kLazy;
     if (__ballot(grow)) {
@@ -79,16 +93,19 @@ __device__ __forceinline__ void softmax_update(f32x16* s, float c, float bias, f
     l += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// Normalise O, stage the bf16 tile in LDS (reusing the K tile) and store full
-// rows; write the natural-log sum of exp when requested.
+// Normalise O, stage the bf16 tile in LDS (reusing tile buffers: rows
+// 0 .. BLK/2-1 in lo_rows, the rest in hi_rows, each [BLK/2][D] bf16) and
+// store full rows; write the natural-log sum of exp when requested.
 template <int D, int BLK>
 __device__ __forceinline__ void store_output(const AttnArgs& a, const SeqTable& t, int h, int q0, int lo, int nI,
-                                             int qr, int half, float m, float l, const f32x16* o, uint4* lk,
-                                             int tid) {
+                                             int qr, int half, float m, float l, const f32x16* o, uint4* lo_rows,
+                                             uint4* hi_rows, int tid) {
     using T = Tile<D, BLK>;
-    const float l_tot = l + __shfl_xor(l, 32);
+    constexpr int HR = BLK / 2;
+    const float l_tot = pair_sum(l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __syncthreads();
+    uint4* mine = qr < HR ? lo_rows + qr * T::KCH : hi_rows + (qr - HR) * T::KCH;   // uniform per wave
 #pragma unroll
     for (int ds = 0; ds < T::NDS; ++ds)
 #pragma unroll
@@ -96,13 +113,14 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, const SeqTable& 
             const int chunk = 4 * ds + g4;        // d0 = 32 ds + 8 g4 + 4 half
             uint2 v2 = make_uint2(pack_bf16(o[ds][4 * g4] * inv, o[ds][4 * g4 + 1] * inv),
                                   pack_bf16(o[ds][4 * g4 + 2] * inv, o[ds][4 * g4 + 3] * inv));
-            reinterpret_cast<uint2*>(&lk[qr * T::KCH + (chunk ^ (qr % T::KCH))])[half] = v2;
+            reinterpret_cast<uint2*>(&mine[chunk ^ (qr % T::KCH)])[half] = v2;
         }
     __syncthreads();
     for (int i = tid; i < (nI - lo) * T::KCH; i += T::NT) {
         const int row = lo + i / T::KCH, ch = i % T::KCH;
+        const uint4* src = row < HR ? lo_rows + row * T::KCH : hi_rows + (row - HR) * T::KCH;
         *reinterpret_cast<uint4*>(a.out + ((int64_t)(q0 + row) * a.Hq + h) * D + ch * 8) =
-            lk[row * T::KCH + (ch ^ (row % T::KCH))];
+            src[ch ^ (row % T::KCH)];
     }
     if (a.lse && half == 0 && qr >= lo && qr < nI)
         a.lse[(int64_t)h * t.total_tokens + q0 + qr] = (m + __log2f(l_tot)) * kLn2;

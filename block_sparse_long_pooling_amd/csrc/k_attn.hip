@@ -14,9 +14,9 @@
 //                        combined with the partner lane l ^ 32
 //     O^T += V^T P^T     P straight from registers; V^T operand read from the
 //                        row-major V rows with ds_read_b64_tr_b16
-// A tile buffer holds the tile's KT K rows, then its KT V rows, row-major
-// [KT][D] bf16 with 16-byte chunks XOR-swizzled per row (32 KiB for 64 keys
-// at d = 128).  Tiles arrive by global_load_lds_dwordx4 (DMA into LDS, no
+// A tile buffer holds the tile's KT K rows and its KT V rows in two arrays,
+// row-major [KT][D] bf16 with 16-byte chunks XOR-swizzled per row (16 KiB
+// each for 64 keys at d = 128).  Tiles arrive by global_load_lds_dwordx4 (DMA into LDS, no
 // registers) into two alternating buffers: the next tile's DMA is issued
 // right after the one barrier per tile and lands while the current tile is
 // computed.  Rows past a request's end re-read its last row (contiguous
@@ -52,12 +52,17 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     constexpr int NH = BLK / KT;                         // tiles per KV block
     constexpr int NT = 2 * BLK;
     constexpr int NDS = D / 32;
-    constexpr int VOFF = KT * D * 2;                     // bytes of a tile's K rows
     constexpr int NSB = KT / 32;                         // 32-key subtiles per tile
-    constexpr int BUF = 2 * KT * D * 2;
-    static_assert(BUF >= BLK * D * 2, "a tile buffer also stages the output block");
-    __shared__ __attribute__((aligned(16))) char buf0[BUF];
-    __shared__ __attribute__((aligned(16))) char buf1[BUF];
+    constexpr int TB = KT * D * 2;                       // bytes of a tile's K (or V) rows
+    static_assert(TB >= BLK * D, "a K or V tile buffer also holds BLK/2 pooled rows or output rows");
+    // Two tile buffers, each a K array and a V array.  Four separate arrays
+    // let the compiler see that the V rows a tile's PV product reads are not
+    // the ones the next tile's DMA writes; with K and V in one array it made
+    // the product wait for that DMA.
+    __shared__ __attribute__((aligned(16))) char kb0[TB];
+    __shared__ __attribute__((aligned(16))) char vb0[TB];
+    __shared__ __attribute__((aligned(16))) char kb1[TB];
+    __shared__ __attribute__((aligned(16))) char vb1[TB];
     __shared__ uint32_t kept_bits[FP_MAX_BLOCKS / 32];   // correction: kept past blocks
 
     const int tid = threadIdx.x;
@@ -120,10 +125,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     auto load_pages = [&](int code) {
         if (PAGED) load_tile_pages(pages, a.kv, code, len - code * KT, plan, pg);
     };
-    auto issue = [&](int code, char* dst) {
-        issue_tile<D, KT, NT, PAGED>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, dst, wave_base);
-        issue_tile<D, KT, NT, PAGED>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, dst + VOFF,
-                                     wave_base);
+    auto issue = [&](int code, char* kd, char* vd) {
+        issue_tile<D, KT, NT, PAGED>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, kd, wave_base);
+        issue_tile<D, KT, NT, PAGED>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, vd, wave_base);
     };
     // The list is read 64 entries at a time, one per lane, bounded by its
     // capacity I + 1 (entries past the count are never used).
@@ -148,26 +152,26 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     int code = next_code();
     if (code >= 0) {
         load_pages(code);
-        issue(code, buf0);
+        issue(code, kb0, vb0);
     }
     int coden = code >= 0 ? next_code() : -1;
     if (coden >= 0) load_pages(coden);
 
-    auto step = [&](char* bcur, char* bnext) {
+    auto step = [&](char* kc, char* vc, char* kn, char* vn) {
         __builtin_amdgcn_s_waitcnt(0);                   // this thread's DMA of the tile (and next page ids)
         lds_barrier();                                   // ... every thread's; the other buffer is free
         int codenn = -1;
         auto prefetch = [&]() {
             if (coden >= 0) {
                 codenn = next_code();
-                issue(coden, bnext);
+                issue(coden, kn, vn);
                 if (codenn >= 0) load_pages(codenn);
             }
         };
         if (!kSerialFill) prefetch();
         const int J = code / NH, hh = code % NH;
         if (J != I || 32 * w + 31 >= KT * hh) {
-            qk<D, 0, NSB>(reinterpret_cast<const uint4*>(bcur), qf, col, half, s);
+            qk<D, 0, NSB>(reinterpret_cast<const uint4*>(kc), qf, col, half, s);
             if (J == I) {
                 // Causal mask of the diagonal block (opaque limit: the lane
                 // masks are computed here, not hoisted and held).
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
                     }
             }
             softmax_update<NSB, NDS>(s, c, 0.f, m, l, o, pk);
-            pv<D, 0, NSB>(bcur + VOFF, pk, lane, o);
+            pv<D, 0, NSB>(vc, pk, lane, o);
         }
         if (kSerialFill) {
             lds_barrier();                               // every wave is done with the tile
@@ -192,14 +196,16 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
         coden = codenn;
     };
     while (code >= 0) {
-        step(buf0, buf1);
+        step(kb0, vb0, kb1, vb1);
         if (code < 0) break;
-        step(buf1, buf0);
+        step(kb1, vb1, kb0, vb0);
     }
     lds_barrier();                                       // the last tile is read
     if (a.correction && I > 0)
-        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qf, buf0, buf1, kept_bits, tid, col, half, c, m, l, o);
-    store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, reinterpret_cast<uint4*>(buf0), tid);
+        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qf, kb0, vb0, kb1, vb1, kept_bits, tid, col, half, c,
+                               m, l, o);
+    store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, reinterpret_cast<uint4*>(kb0),
+                         reinterpret_cast<uint4*>(vb0), tid);
 }
 
 template <int D, int BLK>

@@ -120,7 +120,7 @@ __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, fl
     for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sub][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = pair_max(mt);
     const float mt2 = (mt == -INFINITY) ? -INFINITY : mt * c;
     const float m_new = fmaxf(m, mt2);
     const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
@@ -365,10 +365,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
                                         pack_bf16(f2.x * sq, f2.y * sq), pack_bf16(f3.x * sq, f3.y * sq));
             qb[kk] = __builtin_bit_cast(bf16x8, pk);
         }
-        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qb, reinterpret_cast<char*>(lk),
-                               reinterpret_cast<char*>(lv), kept_bits, tid, col, half, a.scale_log2, m, l, o);
+        constexpr int HALF = (BLK / 2) * D * 2;          // bytes of BLK/2 pooled bf16 rows
+        char* b0 = reinterpret_cast<char*>(lk);
+        char* b1 = reinterpret_cast<char*>(lv);
+        correction_dma<D, BLK>(a, t, b, I, hk, cnt, list, J0, qb, b0, b0 + HALF, b1, b1 + HALF, kept_bits, tid,
+                               col, half, a.scale_log2, m, l, o);
     }
-    store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, lk, tid);
+    store_output<D, BLK>(a, t, h, q0, lo, nI, qr, half, m, l, o, lk, lk + (BLK / 2) * T::KCH, tid);
 }
 
 template <int D, int BLK>
