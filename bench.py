@@ -65,8 +65,9 @@ def _counter_rows(folder):
     rows = []
     for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
         with open(f, newline="") as fh:
-            for r in csv.DictReader(fh):
-                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+            for i, r in enumerate(csv.DictReader(fh)):
+                did = r.get("Dispatch_Id") or r.get("Correlation_Id") or f"{f}:{i}"
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), did))
     return rows
 
 
@@ -79,9 +80,11 @@ def traffic_record(fetch_dir, write_dir):
     import hashlib
     per = {}
     for folder, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
-        for name, cname, val, _ in _counter_rows(folder):
-            if cname != counter:
-                continue
+        disp = {}
+        for name, cname, val, did in _counter_rows(folder):
+            if cname == counter:
+                disp[(name, did)] = disp.get((name, did), 0.0) + val   # summed over the rows of a dispatch
+        for (name, _), val in disp.items():
             per.setdefault(name, {}).setdefault(counter, []).append(val)
     copy = [n for n in per if "copy" in n.lower() and max(per[n].get("WRITE_SIZE", [0])) > 1e6]
     if not copy:
@@ -121,6 +124,68 @@ def traffic_record(fetch_dir, write_dir):
     print(f"record: {TRAFFIC_RECORD}: {rec['traffic_bytes']:.4g} bytes per attention launch")
 
 
+def trace_summary(folder, timed):
+    """Markdown table of this library's kernels from a rocprofv3 --kernel-trace
+    --stats run: per kernel the launch count, the average over all launches
+    (what --stats reports) and over the last `timed` launches (the timed
+    steps), their min and max, and the attention kernel's durations in launch
+    order."""
+    import csv
+    import glob
+    runs = {}
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if not any(k in name for k in ("k_pool", "k_select", "k_quant", "k_attn")):
+                    continue
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                runs.setdefault(name.split("(")[0], []).append((int(r["Start_Timestamp"]), us))
+    print(f"| kernel | launches | average, all (us) | average, last {timed} (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(runs):
+        d = [u for _, u in sorted(runs[name])]
+        last = d[-timed:]
+        print(f"| `{name}` | {len(d)} | {statistics.mean(d):.1f} | {statistics.mean(last):.1f} | "
+              f"{min(last):.1f} | {max(last):.1f} |")
+    for name in sorted(runs):
+        if "k_attn_bf16<128, 128, false>" in name:
+            print("\nattention launches in order (us): " +
+                  ", ".join(f"{u:.0f}" for _, u in sorted(runs[name])))
+
+
+def counter_summary(folder):
+    """Markdown table of this library's kernels from one rocprofv3 --pmc run:
+    per kernel the mean of every counter per dispatch, and, when the counters
+    are there, MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE
+    / 8 XCDs / 1024 SIMDs), vector instructions per MFMA, the LDS bank-conflict
+    share and the share of wave cycles spent waiting."""
+    per = {}
+    for name, cname, val, disp in _counter_rows(folder):
+        if not any(k in name for k in ("k_pool", "k_select", "k_quant", "k_attn")):
+            continue
+        per.setdefault(name.split("(")[0], {}).setdefault(cname, {}).setdefault(disp, 0.0)
+        per[name.split("(")[0]][cname][disp] += val      # a counter may come per XCD / SE row
+    counters = sorted({c for k in per.values() for c in k})
+    derived = ["MFMA busy per SIMD", "VALU per MFMA", "LDS conflict share", "waiting share"]
+    print("| kernel | dispatches | " + " | ".join(counters) + " | " + " | ".join(derived) + " |")
+    print("|---|---|" + "---|" * (len(counters) + len(derived)))
+    for name in sorted(per):
+        mean = {c: statistics.mean(per[name][c].values()) for c in per[name]}
+        nd = max(len(per[name][c]) for c in per[name])
+        g = lambda c: mean.get(c)
+        d = []
+        d.append(f"{100 * g('SQ_VALU_MFMA_BUSY_CYCLES') / (g('GRBM_GUI_ACTIVE') / 8) / 1024:.1f}%"
+                 if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None and g("GRBM_GUI_ACTIVE") else "-")
+        d.append(f"{g('SQ_INSTS_VALU') / g('SQ_INSTS_MFMA'):.2f}" if g("SQ_INSTS_MFMA") else "-")
+        d.append(f"{100 * g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):.1f}%"
+                 if g("SQ_LDS_IDX_ACTIVE") and g("SQ_LDS_BANK_CONFLICT") is not None else "-")
+        d.append(f"{100 * g('SQ_WAIT_INST_ANY') / g('SQ_WAVE_CYCLES'):.0f}%"
+                 if g("SQ_WAVE_CYCLES") and g("SQ_WAIT_INST_ANY") is not None else "-")
+        print(f"| `{name}` | {nd} | " + " | ".join(f"{mean[c]:.4e}" if c in mean else "-" for c in counters)
+              + " | " + " | ".join(d) + " |")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -147,6 +212,11 @@ def parse():
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: write the attention kernel's calibrated traffic record from two "
                          "rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) and print a table")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="no GPU work: print a table of this library's kernels from a rocprofv3 --kernel-trace "
+                         "run (averages over all launches and over the last --steps launches)")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR",
+                    help="no GPU work: print a table of this library's kernels from one rocprofv3 --pmc run")
     return ap.parse_args()
 
 
@@ -207,6 +277,12 @@ def main():
     args = parse()
     if args.traffic_record:
         traffic_record(*args.traffic_record)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the path is built and "

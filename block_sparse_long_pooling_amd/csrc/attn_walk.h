@@ -46,6 +46,13 @@ struct DmaPlan {
     __device__ __forceinline__ int coff(int i) const { return (chunk0 ^ swz<D>(row(i))) * 8; }
 };
 
+// Raw buffer resource over the 4 GiB from base (stride 0, every offset in
+// range; dword 3 selects the 32-bit data format that untyped buffer loads
+// need on gfx9-family chips).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+
 // Page ids of this thread's DMA rows of tile J (paged layout), all loaded
 // before any of the tile's DMAs is issued: the vector-memory counter is in
 // order, so a page id loaded between DMAs could only be waited for together
@@ -70,9 +77,13 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
     using P = DmaPlan<D, ROWS, NT>;
     static_assert((ROWS * P::NCH) % NT == 0, "tile chunks must split evenly");
     if (!PAGED) {
-        // Uniform tile base plus a 32-bit per-lane offset (the scalar-base
-        // addressing form).
+        // Buffer loads into LDS from a resource whose base is the tile's first
+        // row, with a 32-bit per-lane offset.  (A global_load_lds is a FLAT
+        // instruction that the compiler counts as an LDS access too, so while
+        // one is in flight it waits for every outstanding LDS read instead of
+        // the one an MFMA needs.)
         const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * ROWS * rs);
+        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(tile);
         if (nvalid >= ROWS) {
             // Whole tile: load i's row offset is the thread's first row's plus
             // a uniform step, so no multiply per load.  The base is opaque so
@@ -82,8 +93,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
 #pragma unroll
             for (int i = 0; i < P::NLOAD; ++i) {
                 const uint32_t off = (uint32_t)(rbase + i * P::ROWSTEP * (int)rs + plan.coff(i)) * 2u;
-                __builtin_amdgcn_global_load_lds(tile + off, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, 0,
-                                                 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off,
+                                                         0, 0, 0);
             }
             return;
         }
@@ -97,7 +108,8 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
             int r = plan.row(i);
             asm volatile("" : "+v"(r));
             const uint32_t off = (uint32_t)(min(r, nvalid - 1) * (int)rs + plan.coff(i)) * 2u;
-            __builtin_amdgcn_global_load_lds(tile + off, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off, 0,
+                                                     0, 0);
         }
     } else {
 #pragma unroll
