@@ -64,7 +64,7 @@ __device__ __forceinline__ void load_tile_pages(const int32_t* pages, const KVLa
                                                 const DmaPlan<D, ROWS, NT>& plan, int* pg) {
 #pragma unroll
     for (int i = 0; i < DmaPlan<D, ROWS, NT>::NLOAD; ++i)
-        pg[i] = pages[(J * ROWS + min(plan.row(i), nvalid - 1)) / L.page_size];
+        pg[i] = pages[L.page_of(J * ROWS + min(plan.row(i), nvalid - 1))];
 }
 
 // DMA one tile: rows J*ROWS .. J*ROWS+ROWS-1 of the request whose first row
@@ -121,7 +121,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
             // pointer per chunk across the loop (it would spill).
             int co = plan.coff(i);
             asm volatile("" : "+v"(co));
-            const uint16_t* p = first + ((int64_t)page * L.page_size + tr % L.page_size) * rs + co;
+            const uint16_t* p = first + (((int64_t)page << L.page_shift) + L.slot_of(tr)) * rs + co;
             const void* src =
                 (row < nvalid && (unsigned)page < (unsigned)L.num_pages) ? (const void*)p : (const void*)zero;
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, 0, 0);

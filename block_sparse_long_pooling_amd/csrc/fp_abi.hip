@@ -299,7 +299,7 @@ FP_EXPORT int fp_select_blocks(const fp_params* params, const void* q, const voi
     if (pooled_kv_bf16 && (!aligned(pooled_kv_bf16, 16) || !aligned(v, 16)))
         return fail(FP_INVALID_ARGUMENT, "pooled_kv_bf16 needs a non-NULL, 16-byte aligned v (and itself aligned)");
     const int32_t cu[2] = {0, seqlen};
-    KVLayout kv = {nullptr, 1, 0, 0};
+    KVLayout kv = {nullptr, 1, 0, 0, 0};
     (void)hipGetLastError();
     rc = run_select(*params, cu, nullptr, 1, q, k, v, kv, false, pooled_q, pooled_k, pooled_v,
                     static_cast<uint16_t*>(pooled_kv_bf16), nullptr, 0, kv_idx, kv_cnt,
@@ -351,7 +351,7 @@ FP_EXPORT int fp_select_blocks_fp8(const fp_params* params, const void* q, const
     qa.H[0] = p.num_q_heads;
     qa.H[1] = qa.H[2] = p.num_kv_heads;
     qa.groups[0] = qa.groups[1] = qa.groups[2] = 0;
-    qa.kv = KVLayout{nullptr, 1, 0, 0};
+    qa.kv = KVLayout{nullptr, 1, 0, 0, 0};
     qa.D = p.head_dim;
     qa.B = p.block_size;
     qa.nB = t.total_blocks;
@@ -400,7 +400,7 @@ FP_EXPORT int fp_sparse_prefill_fwd(const fp_params* params, const void* q, cons
     a.pv16 = a.pk16 ? a.pk16 + (int64_t)p.num_kv_heads * t.total_blocks * p.head_dim : nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
-    a.kv = KVLayout{nullptr, 1, 0, 0};
+    a.kv = KVLayout{nullptr, 1, 0, 0, 0};
     a.Hq = p.num_q_heads;
     a.Hkv = p.num_kv_heads;
     a.g = p.num_q_heads / p.num_kv_heads;
@@ -428,6 +428,14 @@ struct Fp8Pages {
 // the pooled cache pcache (may be NULL) and its reuse flag.  f8 non-NULL:
 // fp8 attention over the e4m3 pages, whose query blocks' codes and scales
 // are written first (chunked prefill; params in fp8).
+// log2 of a power of two (a page size divides the block size, 64 or 128, so
+// it is one); the kernels address pages with shifts and masks.
+static int log2_exact(int v) {
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+
 int paged_prefill(const fp_params* params, const void* q, const void* k_cache, const void* v_cache, int32_t page_size,
                   int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_q,
                   const int32_t* kv_lens, int32_t batch, float* pcache, int32_t reuse, const Fp8Pages* f8,
@@ -471,7 +479,7 @@ int paged_prefill(const fp_params* params, const void* q, const void* k_cache, c
     float* pq = reinterpret_cast<float*>(wsb + ws.q);
     float* pk = reinterpret_cast<float*>(wsb + ws.k);
     uint16_t* pkv16 = p.mean_correction ? reinterpret_cast<uint16_t*>(wsb + ws.kv16) : nullptr;
-    KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
+    KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq, log2_exact(page_size)};
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (!f8) {
@@ -657,7 +665,7 @@ FP_EXPORT int fp_sparse_prefill_varlen_paged_fp8(const fp_params* params, const 
     uint16_t* pkv16 = p.mean_correction ? reinterpret_cast<uint16_t*>(wsb + ws.kv16) : nullptr;
     uint8_t* q8 = reinterpret_cast<uint8_t*>(wsb + ws.q8);
     float* qs = reinterpret_cast<float*>(wsb + ws.qs);
-    const KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq};
+    const KVLayout kv = {block_table, page_size, num_pages, max_pages_per_seq, log2_exact(page_size)};
     // One pass over the bf16 data: Q codes and scales into the workspace, K
     // and V codes into the e4m3 pages with their scales, the block means.
     QuantArgs qa;

@@ -127,6 +127,11 @@ struct KVLayout {
     int32_t page_size;
     int32_t num_pages;
     int32_t max_pages;
+    int32_t page_shift;          // log2(page_size): a page size divides the block size (64 or 128)
+    // Page index and slot of a request's token tr >= 0 (a shift and a mask,
+    // where a division by a run-time page size costs a few dozen instructions).
+    __device__ __forceinline__ int page_of(int tr) const { return tr >> page_shift; }
+    __device__ __forceinline__ int slot_of(int tr) const { return tr & (page_size - 1); }
 };
 
 // Row of token tr (0-based inside request b whose packed rows start at tok0);
@@ -134,9 +139,9 @@ struct KVLayout {
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_row(const KVLayout& L, int b, int tok0, int tr) {
     if (!PAGED) return (int64_t)tok0 + tr;
-    int page = L.block_table[(int64_t)b * L.max_pages + tr / L.page_size];
+    int page = L.block_table[(int64_t)b * L.max_pages + L.page_of(tr)];
     if ((unsigned)page >= (unsigned)L.num_pages) return -1;
-    return (int64_t)page * L.page_size + tr % L.page_size;
+    return ((int64_t)page << L.page_shift) + L.slot_of(tr);
 }
 
 // Head permutation that puts the query heads of one KV head on one XCD when

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
         wJ = list[i];
         if (PAGED) {
             // Paged scales: [num_pages, Hkv], the entry of the block's first page.
-            const int page = pages[wJ * BLK / a.kv.page_size];
+            const int page = pages[a.kv.page_of(wJ * BLK)];
             const bool ok = (unsigned)page < (unsigned)a.kv.num_pages;
             // A page id outside the pool reads as zero codes (the DMA's zero
             // chunk) with scale 1, i.e. as a page of zeros.

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a, SeqTable t) {
     // Pooled cache entry of this block: the page holding its first token.
     float* cache = nullptr;
     if (PAGED && a.pcache) {
-        const int page = a.kv.block_table[(int64_t)b * a.kv.max_pages + t0 / a.kv.page_size];
+        const int page = a.kv.block_table[(int64_t)b * a.kv.max_pages + a.kv.page_of(t0)];
         if ((unsigned)page < (unsigned)a.kv.num_pages)
             cache = a.pcache + (((int64_t)(isv ? a.kv.num_pages : 0) + page) * a.Hkv + h) * a.D + dd;
     }
