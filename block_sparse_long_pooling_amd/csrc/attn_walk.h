@@ -14,8 +14,10 @@ typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Source of DMA chunks for rows that hold no data (out-of-range pages).
+// Source of DMA chunks for rows that hold no data (out-of-range pages): one
+// zero chunk, and one zero row of the widest tile row (d = 128 bf16).
 static __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+static __device__ const uint4 kZeroRow[16] = {};
 
 // XOR swizzle of 16-byte chunks within a row: conflict-free for the MFMA K
 // reads (16 consecutive rows, one chunk) and for the transposing V reads
@@ -67,6 +69,46 @@ __device__ __forceinline__ void load_tile_pages(const int32_t* pages, const KVLa
         pg[i] = pages[L.page_of(J * ROWS + min(plan.row(i), nvalid - 1))];
 }
 
+// DMA ROWS rows starting at `tile` (row stride rs elements; nvalid >= 1 rows
+// hold data) by buffer loads into LDS from a resource whose base is the
+// tile's first row, with a 32-bit per-lane offset.  (A global_load_lds is a
+// FLAT instruction that the compiler counts as an LDS access too, so while one
+// is in flight it waits for every outstanding LDS read instead of the one an
+// MFMA needs.)
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void issue_rows(const char* tile, int rs, int nvalid, const DmaPlan<D, ROWS, NT>& plan,
+                                           char* lds, int wave_base) {
+    using P = DmaPlan<D, ROWS, NT>;
+    static_assert((ROWS * P::NCH) % NT == 0, "tile chunks must split evenly");
+    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(tile);
+    if (nvalid >= ROWS) {
+        // Whole tile: load i's row offset is the thread's first row's plus
+        // a uniform step, so no multiply per load.  The base is opaque so
+        // the compiler keeps one register, not one offset per load.
+        int rbase = plan.row0 * rs;
+        asm volatile("" : "+v"(rbase));
+#pragma unroll
+        for (int i = 0; i < P::NLOAD; ++i) {
+            const uint32_t off = (uint32_t)(rbase + i * P::ROWSTEP * rs + plan.coff(i)) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off, 0,
+                                                     0, 0);
+        }
+        return;
+    }
+    // Rows past the end of the sequence re-read its last row: they occur only
+    // on the diagonal block, where the causal mask removes them, and finite
+    // values keep 0 * v at 0.  The row index is opaque so the compiler does
+    // not keep a precomputed offset per chunk and row stride (it would spill).
+#pragma unroll
+    for (int i = 0; i < P::NLOAD; ++i) {
+        int r = plan.row(i);
+        asm volatile("" : "+v"(r));
+        const uint32_t off = (uint32_t)(min(r, nvalid - 1) * rs + plan.coff(i)) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off, 0, 0,
+                                                 0);
+    }
+}
+
 // DMA one tile: rows J*ROWS .. J*ROWS+ROWS-1 of the request whose first row
 // is `first` (contiguous), or of its pages pg from load_tile_pages (paged).
 // nvalid >= 1 rows of the tile hold data.
@@ -75,42 +117,9 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
                                            int64_t rs, int J, int nvalid, const DmaPlan<D, ROWS, NT>& plan,
                                            const uint4* zero, char* lds, int wave_base) {
     using P = DmaPlan<D, ROWS, NT>;
-    static_assert((ROWS * P::NCH) % NT == 0, "tile chunks must split evenly");
     if (!PAGED) {
-        // Buffer loads into LDS from a resource whose base is the tile's first
-        // row, with a 32-bit per-lane offset.  (A global_load_lds is a FLAT
-        // instruction that the compiler counts as an LDS access too, so while
-        // one is in flight it waits for every outstanding LDS read instead of
-        // the one an MFMA needs.)
-        const char* tile = reinterpret_cast<const char*>(first + (int64_t)J * ROWS * rs);
-        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(tile);
-        if (nvalid >= ROWS) {
-            // Whole tile: load i's row offset is the thread's first row's plus
-            // a uniform step, so no multiply per load.  The base is opaque so
-            // the compiler keeps one register, not one offset per load.
-            int rbase = plan.row0 * (int)rs;
-            asm volatile("" : "+v"(rbase));
-#pragma unroll
-            for (int i = 0; i < P::NLOAD; ++i) {
-                const uint32_t off = (uint32_t)(rbase + i * P::ROWSTEP * (int)rs + plan.coff(i)) * 2u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off,
-                                                         0, 0, 0);
-            }
-            return;
-        }
-        // Rows past the end of the sequence re-read its last row: they occur
-        // only on the diagonal block, where the causal mask removes them, and
-        // finite values keep 0 * v at 0.  The row index is opaque so the
-        // compiler does not keep a precomputed offset per chunk and row stride
-        // (it would spill).
-#pragma unroll
-        for (int i = 0; i < P::NLOAD; ++i) {
-            int r = plan.row(i);
-            asm volatile("" : "+v"(r));
-            const uint32_t off = (uint32_t)(min(r, nvalid - 1) * (int)rs + plan.coff(i)) * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, off, 0,
-                                                     0, 0);
-        }
+        issue_rows<D, ROWS, NT>(reinterpret_cast<const char*>(first + (int64_t)J * ROWS * rs), (int)rs, nvalid, plan,
+                                lds, wave_base);
     } else {
 #pragma unroll
         for (int i = 0; i < P::NLOAD; ++i) {
@@ -127,6 +136,22 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (i * NT) * 16 + wave_base), 16, 0, 0);
         }
     }
+}
+
+// Paged tile that lies in one page (page_size >= ROWS; both are powers of two
+// and tiles start at multiples of ROWS): the tile is ROWS consecutive rows of
+// page `page` (uniform) from slot (J*ROWS mod page_size), so it takes the
+// contiguous form with a uniform base.  Rows past the request's end re-read
+// its last row, which lies in the same page.  A page id outside the pool reads
+// as zeros: every row then reads one zero row (stride 0).
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void issue_page_tile(const uint16_t* first, int page, const KVLayout& L, int rs, int J,
+                                                int nvalid, const DmaPlan<D, ROWS, NT>& plan, const uint4* zero_row,
+                                                char* lds, int wave_base) {
+    const bool ok = (unsigned)page < (unsigned)L.num_pages;
+    const uint16_t* base = first + (((int64_t)page << L.page_shift) + L.slot_of(J * ROWS)) * rs;
+    issue_rows<D, ROWS, NT>(ok ? reinterpret_cast<const char*>(base) : reinterpret_cast<const char*>(zero_row),
+                            ok ? rs : 0, nvalid, plan, lds, wave_base);
 }
 
 // S^T for subtiles SUB0 .. SUB0+NS-1 (keys 32 SUB0 ..) of this wave's 32

@@ -46,8 +46,13 @@ using namespace fp_walk;
 template <int D, int BLK>
 constexpr int kTileKeys = (D == 128 && BLK == 64) ? 32 : 64;
 
-template <int D, int BLK, bool PAGED>
+// K/V layout: contiguous rows, pages of any size (page ids per tile row), or
+// pages of at least a tile (one page id per tile, contiguous DMA form).
+enum { kContig = 0, kPagedRows = 1, kPagedTiles = 2 };
+
+template <int D, int BLK, int PG>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t) {
+    constexpr bool PAGED = PG != kContig;
     constexpr int KT = kTileKeys<D, BLK>;               // keys per tile
     constexpr int NH = BLK / KT;                         // tiles per KV block
     constexpr int NT = 2 * BLK;
@@ -121,13 +126,26 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     // Tile code = NH J + hh: keys KT code .. KT code + KT - 1 of the request.
     // Paged layout: pg holds the page ids of the next tile to issue, loaded a
     // step ahead so the issue does not wait on the block table.
-    int pg[NLOAD];
+    // With pages of at least a tile, the tile's one page id (the same in
+    // every lane) is read instead.
+    int pg[PG == kPagedRows ? NLOAD : 1];
     auto load_pages = [&](int code) {
-        if (PAGED) load_tile_pages(pages, a.kv, code, len - code * KT, plan, pg);
+        if (PG == kPagedRows) load_tile_pages(pages, a.kv, code, len - code * KT, plan, pg);
+        if (PG == kPagedTiles) pg[0] = pages[a.kv.page_of(code * KT)];
     };
     auto issue = [&](int code, char* kd, char* vd) {
-        issue_tile<D, KT, NT, PAGED>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, kd, wave_base);
-        issue_tile<D, KT, NT, PAGED>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, vd, wave_base);
+        if (PG == kPagedTiles) {
+            const int page = __builtin_amdgcn_readfirstlane(pg[0]);
+            issue_page_tile<D, KT, NT>(kfirst, page, a.kv, (int)rs, code, len - code * KT, plan, kZeroRow, kd,
+                                       wave_base);
+            issue_page_tile<D, KT, NT>(vfirst, page, a.kv, (int)rs, code, len - code * KT, plan, kZeroRow, vd,
+                                       wave_base);
+        } else {
+            issue_tile<D, KT, NT, PAGED>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, kd,
+                                         wave_base);
+            issue_tile<D, KT, NT, PAGED>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, vd,
+                                         wave_base);
+        }
     };
     // The list is read 64 entries at a time, one per lane, bounded by its
     // capacity I + 1 (entries past the count are never used).
@@ -211,10 +229,12 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
 template <int D, int BLK>
 hipError_t launch_db(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     const dim3 grid((unsigned)(t.total_items * a.Hq));
-    if (paged)
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, true>), grid, dim3(2 * BLK), 0, s, a, t);
+    if (paged && a.kv.page_size >= kTileKeys<D, BLK>)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, kPagedTiles>), grid, dim3(2 * BLK), 0, s, a, t);
+    else if (paged)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, kPagedRows>), grid, dim3(2 * BLK), 0, s, a, t);
     else
-        hipLaunchKernelGGL((k_attn_bf16<D, BLK, false>), grid, dim3(2 * BLK), 0, s, a, t);
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, kContig>), grid, dim3(2 * BLK), 0, s, a, t);
     return hipGetLastError();
 }
 
