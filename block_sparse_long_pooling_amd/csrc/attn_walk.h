@@ -138,12 +138,59 @@ __device__ __forceinline__ void issue_tile(const uint16_t* first, const int* pg,
     }
 }
 
+// K/V layout of a kernel's kept tiles: contiguous rows; pages of any size (a
+// page id per tile row); pages that hold each DMA load's rows (a page id per
+// load, contiguous form); pages that hold whole tiles (one page id per tile,
+// contiguous form).
+enum { kContig = 0, kPagedRows = 1, kPagedSpans = 2, kPagedTiles = 3 };
+
+// Paged tiles whose loads each fall in one page: load i of every thread of
+// the workgroup reads rows i*ROWSTEP .. i*ROWSTEP + ROWSTEP-1 of the tile, and
+// with page_size >= ROWSTEP (both powers of two, tiles aligned) those rows are
+// consecutive rows of one page.  Each load then takes the contiguous form: a
+// uniform base (its page's row) and 32-bit lane offsets, by buffer loads.
+// Lane i of pgv holds the page id of load i (load_span_pages, a step ahead).
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void load_span_pages(const int32_t* pages, const KVLayout& L, int J, int nvalid, int lane,
+                                                int& pgv) {
+    using P = DmaPlan<D, ROWS, NT>;
+    const int i = min(lane, P::NLOAD - 1);
+    // (clamped to the request's last row, so the block-table read stays
+    // inside the pages that cover the request)
+    pgv = pages[L.page_of(J * ROWS + min(i * P::ROWSTEP, nvalid - 1))];
+}
+
+// Rows past the request's end (nvalid >= 1 rows of the tile hold data)
+// re-read its last row, which lies in the same load's page when the load
+// still holds a valid row; a load wholly past the end, or whose page id is
+// outside the pool, reads one zero row (stride 0).
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void issue_span_tile(const uint16_t* first, int pgv, const KVLayout& L, int rs, int J,
+                                                int nvalid, const DmaPlan<D, ROWS, NT>& plan, const uint4* zero_row,
+                                                char* lds, int wave_base) {
+    using P = DmaPlan<D, ROWS, NT>;
+#pragma unroll
+    for (int i = 0; i < P::NLOAD; ++i) {
+        const int r0 = i * P::ROWSTEP;                   // the load's first tile row
+        const int page = __builtin_amdgcn_readlane(pgv, i);
+        const bool ok = r0 < nvalid && (unsigned)page < (unsigned)L.num_pages;
+        const uint16_t* base = first + (((int64_t)page << L.page_shift) + L.slot_of(J * ROWS + r0)) * rs;
+        const char* src = ok ? reinterpret_cast<const char*>(base) : reinterpret_cast<const char*>(zero_row);
+        const int stride = ok ? rs : 0;
+        int r = min(plan.row0, nvalid - 1 - r0);         // row within the load's rows
+        asm volatile("" : "+v"(r));
+        const uint32_t off = (uint32_t)(r * stride + plan.coff(i)) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(src), (lds_void*)(lds + (i * NT) * 16 + wave_base), 16,
+                                                 off, 0, 0, 0);
+    }
+}
+
 // Paged tile that lies in one page (page_size >= ROWS; both are powers of two
 // and tiles start at multiples of ROWS): the tile is ROWS consecutive rows of
 // page `page` (uniform) from slot (J*ROWS mod page_size), so it takes the
-// contiguous form with a uniform base.  Rows past the request's end re-read
-// its last row, which lies in the same page.  A page id outside the pool reads
-// as zeros: every row then reads one zero row (stride 0).
+// contiguous form with one uniform base.  Rows past the request's end re-read
+// its last row, which lies in the same page.  A page id outside the pool
+// reads as zeros: every row then reads one zero row (stride 0).
 template <int D, int ROWS, int NT>
 __device__ __forceinline__ void issue_page_tile(const uint16_t* first, int page, const KVLayout& L, int rs, int J,
                                                 int nvalid, const DmaPlan<D, ROWS, NT>& plan, const uint4* zero_row,
@@ -152,6 +199,36 @@ __device__ __forceinline__ void issue_page_tile(const uint16_t* first, int page,
     const uint16_t* base = first + (((int64_t)page << L.page_shift) + L.slot_of(J * ROWS)) * rs;
     issue_rows<D, ROWS, NT>(ok ? reinterpret_cast<const char*>(base) : reinterpret_cast<const char*>(zero_row),
                             ok ? rs : 0, nvalid, plan, lds, wave_base);
+}
+
+// Page ids and DMA of one tile in any of the paged forms: pg holds NLOAD page
+// ids (kPagedRows) or one value (lane i: load i's page for kPagedSpans; the
+// tile's page for kPagedTiles), loaded a step ahead by load_pages_any.
+template <int PG, int D, int ROWS, int NT>
+__device__ __forceinline__ void load_pages_any(const int32_t* pages, const KVLayout& L, int J, int nvalid, int lane,
+                                               const DmaPlan<D, ROWS, NT>& plan, int* pg) {
+    if (PG == kPagedRows) load_tile_pages(pages, L, J, nvalid, plan, pg);
+    if (PG == kPagedSpans) load_span_pages<D, ROWS, NT>(pages, L, J, nvalid, lane, pg[0]);
+    if (PG == kPagedTiles) pg[0] = pages[L.page_of(J * ROWS)];
+}
+
+template <int PG, int D, int ROWS, int NT>
+__device__ __forceinline__ void issue_tile_any(const uint16_t* first, const int* pg, const KVLayout& L, int64_t rs,
+                                               int J, int nvalid, const DmaPlan<D, ROWS, NT>& plan, char* lds,
+                                               int wave_base) {
+    if (PG == kPagedSpans)
+        issue_span_tile<D, ROWS, NT>(first, pg[0], L, (int)rs, J, nvalid, plan, kZeroRow, lds, wave_base);
+    else if (PG == kPagedTiles)
+        issue_page_tile<D, ROWS, NT>(first, __builtin_amdgcn_readfirstlane(pg[0]), L, (int)rs, J, nvalid, plan,
+                                     kZeroRow, lds, wave_base);
+    else
+        issue_tile<D, ROWS, NT, PG != kContig>(first, pg, L, rs, J, nvalid, plan, &kZeroChunk, lds, wave_base);
+}
+
+// The paged form a kernel takes for tiles of ROWS rows DMA'd by plan P.
+template <int ROWS, int ROWSTEP>
+inline int paged_form(int page_size) {
+    return page_size >= ROWS ? kPagedTiles : page_size >= ROWSTEP ? kPagedSpans : kPagedRows;
 }
 
 // S^T for subtiles SUB0 .. SUB0+NS-1 (keys 32 SUB0 ..) of this wave's 32

@@ -46,10 +46,6 @@ using namespace fp_walk;
 template <int D, int BLK>
 constexpr int kTileKeys = (D == 128 && BLK == 64) ? 32 : 64;
 
-// K/V layout: contiguous rows, pages of any size (page ids per tile row), or
-// pages of at least a tile (one page id per tile, contiguous DMA form).
-enum { kContig = 0, kPagedRows = 1, kPagedTiles = 2 };
-
 template <int D, int BLK, int PG>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t) {
     constexpr bool PAGED = PG != kContig;
@@ -124,28 +120,16 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
     const uint16_t* vfirst = static_cast<const uint16_t*>(a.v) + base;
     const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
     // Tile code = NH J + hh: keys KT code .. KT code + KT - 1 of the request.
-    // Paged layout: pg holds the page ids of the next tile to issue, loaded a
+    // Paged layout: pg holds the page ids of the next tile to issue (one per
+    // DMA row, one per load, or one per tile, by the paged form), loaded a
     // step ahead so the issue does not wait on the block table.
-    // With pages of at least a tile, the tile's one page id (the same in
-    // every lane) is read instead.
     int pg[PG == kPagedRows ? NLOAD : 1];
     auto load_pages = [&](int code) {
-        if (PG == kPagedRows) load_tile_pages(pages, a.kv, code, len - code * KT, plan, pg);
-        if (PG == kPagedTiles) pg[0] = pages[a.kv.page_of(code * KT)];
+        if (PAGED) load_pages_any<PG, D, KT, NT>(pages, a.kv, code, len - code * KT, lane, plan, pg);
     };
     auto issue = [&](int code, char* kd, char* vd) {
-        if (PG == kPagedTiles) {
-            const int page = __builtin_amdgcn_readfirstlane(pg[0]);
-            issue_page_tile<D, KT, NT>(kfirst, page, a.kv, (int)rs, code, len - code * KT, plan, kZeroRow, kd,
-                                       wave_base);
-            issue_page_tile<D, KT, NT>(vfirst, page, a.kv, (int)rs, code, len - code * KT, plan, kZeroRow, vd,
-                                       wave_base);
-        } else {
-            issue_tile<D, KT, NT, PAGED>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, kd,
-                                         wave_base);
-            issue_tile<D, KT, NT, PAGED>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, &kZeroChunk, vd,
-                                         wave_base);
-        }
+        issue_tile_any<PG, D, KT, NT>(kfirst, pg, a.kv, rs, code, len - code * KT, plan, kd, wave_base);
+        issue_tile_any<PG, D, KT, NT>(vfirst, pg, a.kv, rs, code, len - code * KT, plan, vd, wave_base);
     };
     // The list is read 64 entries at a time, one per lane, bounded by its
     // capacity I + 1 (entries past the count are never used).
@@ -229,9 +213,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_bf16(AttnArgs a, SeqTable t
 template <int D, int BLK>
 hipError_t launch_db(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     const dim3 grid((unsigned)(t.total_items * a.Hq));
-    if (paged && a.kv.page_size >= kTileKeys<D, BLK>)
+    constexpr int KT = kTileKeys<D, BLK>;
+    const int form = paged ? paged_form<KT, DmaPlan<D, KT, 2 * BLK>::ROWSTEP>(a.kv.page_size) : kContig;
+    if (form == kPagedTiles)
         hipLaunchKernelGGL((k_attn_bf16<D, BLK, kPagedTiles>), grid, dim3(2 * BLK), 0, s, a, t);
-    else if (paged)
+    else if (form == kPagedSpans)
+        hipLaunchKernelGGL((k_attn_bf16<D, BLK, kPagedSpans>), grid, dim3(2 * BLK), 0, s, a, t);
+    else if (form == kPagedRows)
         hipLaunchKernelGGL((k_attn_bf16<D, BLK, kPagedRows>), grid, dim3(2 * BLK), 0, s, a, t);
     else
         hipLaunchKernelGGL((k_attn_bf16<D, BLK, kContig>), grid, dim3(2 * BLK), 0, s, a, t);

@@ -152,8 +152,9 @@ __device__ __forceinline__ void softmax8_update(f32x16* s, float c, float vr, fl
     }
 }
 
-template <int D, int BLK, bool PAGED>
+template <int D, int BLK, int PG>
 __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t) {
+    constexpr bool PAGED = PG != kContig;
     using T = Tile<D, BLK>;          // bf16 geometry: LDS sized for the correction tiles
     __shared__ uint4 lk[BLK * T::KCH];
     __shared__ uint4 lv[D * T::VCH];
@@ -223,16 +224,19 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     const uint16_t* kfirst = reinterpret_cast<const uint16_t*>(k8 + kvbase);
     const uint16_t* vfirst = reinterpret_cast<const uint16_t*>(v8 + kvbase);
     const int32_t* pages = PAGED ? a.kv.block_table + (int64_t)b * a.kv.max_pages : nullptr;
-    constexpr int NLOAD = DmaPlan<D / 2, BLK, NTH>::NLOAD;
+    // Page ids of a tile: one per DMA row, one per load or one per tile, by
+    // the paged form.
+    constexpr int NPG = PG == kPagedRows ? DmaPlan<D / 2, BLK, NTH>::NLOAD : 1;
+    auto load_pages8 = [&](int J, int* pg) {
+        if (PAGED) load_pages_any<PG, D / 2, BLK, NTH>(pages, a.kv, J, len - J * BLK, lane, plan, pg);
+    };
     auto issue8_pg = [&](int J, char* dst, const int* pg) {
-        issue_tile<D / 2, BLK, NTH, PAGED>(kfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk, dst,
-                                           wave_base);
-        issue_tile<D / 2, BLK, NTH, PAGED>(vfirst, pg, a.kv, rs2, J, len - J * BLK, plan, &kZeroChunk,
-                                           dst + VOFF, wave_base);
+        issue_tile_any<PG, D / 2, BLK, NTH>(kfirst, pg, a.kv, rs2, J, len - J * BLK, plan, dst, wave_base);
+        issue_tile_any<PG, D / 2, BLK, NTH>(vfirst, pg, a.kv, rs2, J, len - J * BLK, plan, dst + VOFF, wave_base);
     };
     auto issue8 = [&](int J, char* dst) {
-        int pg[NLOAD];
-        if (PAGED) load_tile_pages(pages, a.kv, J, len - J * BLK, plan, pg);
+        int pg[NPG];
+        load_pages8(J, pg);
         issue8_pg(J, dst, pg);
     };
     char* buf0 = reinterpret_cast<char*>(lk);
@@ -276,14 +280,14 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
     // first waiting on the block table.
     int Ja = 0;
     float ska = 1.f, sva = 1.f;
-    int pga[NLOAD];
+    int pga[NPG];
     if (cnt > 0) {
         load_window(0);
         from_window(0, J, sk, sv);
         issue8(J, buf0);
         if (PAGED && cnt > 1) {
             from_window(1, Ja, ska, sva);
-            load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+            load_pages8(Ja, pga);
         }
     }
     auto step = [&](int it, char* bcur, char* bnext) {
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
                 if (it + 1 < cnt) issue8_pg(Jn, bnext, pga);
                 if (it + 2 < cnt) {
                     from_window(it + 2, Ja, ska, sva);
-                    load_tile_pages(pages, a.kv, Ja, len - Ja * BLK, plan, pga);
+                    load_pages8(Ja, pga);
                 }
             } else if (it + 1 < cnt) {
                 if (it + 1 - wbase == 64) load_window(it + 1);
@@ -377,10 +381,15 @@ __global__ __launch_bounds__(2 * BLK, 2) void k_attn_fp8(AttnArgs a, SeqTable t)
 template <int D, int BLK>
 hipError_t launch_fp8_t(const AttnArgs& a, const SeqTable& t, bool paged, hipStream_t s) {
     dim3 grid((unsigned)t.total_items * a.Hq);
-    if (paged)
-        hipLaunchKernelGGL((k_attn_fp8<D, BLK, true>), grid, dim3(2 * BLK), 0, s, a, t);
+    const int form = paged ? paged_form<BLK, DmaPlan<D / 2, BLK, 2 * BLK>::ROWSTEP>(a.kv.page_size) : kContig;
+    if (form == kPagedTiles)
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, kPagedTiles>), grid, dim3(2 * BLK), 0, s, a, t);
+    else if (form == kPagedSpans)
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, kPagedSpans>), grid, dim3(2 * BLK), 0, s, a, t);
+    else if (paged)
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, kPagedRows>), grid, dim3(2 * BLK), 0, s, a, t);
     else
-        hipLaunchKernelGGL((k_attn_fp8<D, BLK, false>), grid, dim3(2 * BLK), 0, s, a, t);
+        hipLaunchKernelGGL((k_attn_fp8<D, BLK, kContig>), grid, dim3(2 * BLK), 0, s, a, t);
     return hipGetLastError();
 }
 
