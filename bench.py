@@ -57,6 +57,14 @@ def measured_traffic():
     return int(rec["traffic_bytes"])
 
 
+def _short_name(name):
+    """Kernel name without 'void', the anonymous namespace and the argument list."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
 def _counter_rows(folder):
     """(kernel name, counter, value) of every dispatch in the rocprofv3
     counter-collection CSV files under folder."""
@@ -86,13 +94,15 @@ def traffic_record(fetch_dir, write_dir):
                 disp[(name, did)] = disp.get((name, did), 0.0) + val   # summed over the rows of a dispatch
         for (name, _), val in disp.items():
             per.setdefault(name, {}).setdefault(counter, []).append(val)
-    copy = [n for n in per if "copy" in n.lower() and max(per[n].get("WRITE_SIZE", [0])) > 1e6]
+    # the probe's copy: a copy kernel with a dispatch that writes 1 GiB (within 1%)
+    gib_kib = float(1 << 20)
+    copy = [(n, i) for n in per if "copy" in n.lower() and "Cat" not in n
+            for i, w in enumerate(per[n].get("WRITE_SIZE", [])) if abs(w / gib_kib - 1.0) < 0.01]
     if not copy:
         raise SystemExit("no 1 GiB copy dispatch found (run with --copy-probe)")
-    cname = max(copy, key=lambda n: max(per[n]["WRITE_SIZE"]))
-    gib_kib = float(1 << 20)
-    ff = gib_kib / max(per[cname]["FETCH_SIZE"])
-    wf = gib_kib / max(per[cname]["WRITE_SIZE"])
+    cname, ci = copy[0]
+    ff = gib_kib / per[cname]["FETCH_SIZE"][ci]
+    wf = gib_kib / per[cname]["WRITE_SIZE"][ci]
     key = "k_attn_bf16<128, 128, false>"
     attn = [n for n in per if key in n]
     if not attn:
@@ -119,7 +129,7 @@ def traffic_record(fetch_dir, write_dir):
             continue
         f_ = statistics.mean(per[n].get("FETCH_SIZE", [0.0]))
         w_ = statistics.mean(per[n].get("WRITE_SIZE", [0.0]))
-        print(f"| `{n[:70]}` | {len(per[n].get('FETCH_SIZE', []))} | {f_:.0f} | {w_:.0f} | "
+        print(f"| `{_short_name(n)}` | {len(per[n].get('FETCH_SIZE', []))} | {f_:.0f} | {w_:.0f} | "
               f"{f_ * ff / gib_kib:.3f} | {w_ * wf / gib_kib:.3f} |")
     print(f"record: {TRAFFIC_RECORD}: {rec['traffic_bytes']:.4g} bytes per attention launch")
 
@@ -128,8 +138,9 @@ def trace_summary(folder, timed):
     """Markdown table of this library's kernels from a rocprofv3 --kernel-trace
     --stats run: per kernel the launch count, the average over all launches
     (what --stats reports) and over the last `timed` launches (the timed
-    steps), their min and max, and the attention kernel's durations in launch
-    order."""
+    steps), their min and max, then every kernel's durations in launch order
+    (a kernel that several calls use lists their launches one call after the
+    other)."""
     import csv
     import glob
     runs = {}
@@ -140,7 +151,7 @@ def trace_summary(folder, timed):
                 if not any(k in name for k in ("k_pool", "k_select", "k_quant", "k_attn")):
                     continue
                 us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                runs.setdefault(name.split("(")[0], []).append((int(r["Start_Timestamp"]), us))
+                runs.setdefault(_short_name(name), []).append((int(r["Start_Timestamp"]), us))
     print(f"| kernel | launches | average, all (us) | average, last {timed} (us) | min (us) | max (us) |")
     print("|---|---|---|---|---|---|")
     for name in sorted(runs):
@@ -148,10 +159,9 @@ def trace_summary(folder, timed):
         last = d[-timed:]
         print(f"| `{name}` | {len(d)} | {statistics.mean(d):.1f} | {statistics.mean(last):.1f} | "
               f"{min(last):.1f} | {max(last):.1f} |")
+    print("\nLaunch durations in launch order (us):\n")
     for name in sorted(runs):
-        if "k_attn_bf16<128, 128, false>" in name:
-            print("\nattention launches in order (us): " +
-                  ", ".join(f"{u:.0f}" for _, u in sorted(runs[name])))
+        print(f"- `{name}`: " + ", ".join(f"{u:.0f}" for _, u in sorted(runs[name])))
 
 
 def counter_summary(folder):
@@ -164,8 +174,8 @@ def counter_summary(folder):
     for name, cname, val, disp in _counter_rows(folder):
         if not any(k in name for k in ("k_pool", "k_select", "k_quant", "k_attn")):
             continue
-        per.setdefault(name.split("(")[0], {}).setdefault(cname, {}).setdefault(disp, 0.0)
-        per[name.split("(")[0]][cname][disp] += val      # a counter may come per XCD / SE row
+        per.setdefault(_short_name(name), {}).setdefault(cname, {}).setdefault(disp, 0.0)
+        per[_short_name(name)][cname][disp] += val       # a counter may come per XCD / SE row
     counters = sorted({c for k in per.values() for c in k})
     derived = ["MFMA busy per SIMD", "VALU per MFMA", "LDS conflict share", "waiting share"]
     print("| kernel | dispatches | " + " | ".join(counters) + " | " + " | ".join(derived) + " |")
