@@ -103,7 +103,7 @@ def traffic_record(fetch_dir, write_dir):
     cname, ci = copy[0]
     ff = gib_kib / per[cname]["FETCH_SIZE"][ci]
     wf = gib_kib / per[cname]["WRITE_SIZE"][ci]
-    key = "k_attn_bf16<128, 128, false>"
+    key = "k_attn_bf16<128, 128, 0>"          # the contiguous form
     attn = [n for n in per if key in n]
     if not attn:
         raise SystemExit(f"no {key} dispatch found")
