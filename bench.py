@@ -44,17 +44,29 @@ ATTN_SOURCES = ("k_attn.hip", "attn_walk.h", "fp_attn.h", "fp_device.h", "fp_lau
 def measured_traffic():
     """Calibrated HBM bytes per attention launch from the committed rocprofv3
     counter record, or None when the kernel sources changed since it was taken."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
     except (OSError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in ATTN_SOURCES:
-        h.update(open(os.path.join(ROOT, "block_sparse_long_pooling_amd", "csrc", f), "rb").read())
-    if h.hexdigest() != rec.get("source_sha256"):
+    if attn_source_hash() != rec.get("source_sha256"):
         return None
     return int(rec["traffic_bytes"])
+
+
+def attn_source_hash():
+    """sha256 of the attention kernel's sources with comments and blank lines
+    left out, so that the traffic record stays valid across comment edits and
+    reads null once the code changes."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        text = open(os.path.join(ROOT, "block_sparse_long_pooling_amd", "csrc", f)).read()
+        for line in text.splitlines():
+            code = re.sub(r"//.*$", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def _short_name(name):
@@ -85,7 +97,6 @@ def traffic_record(fetch_dir, write_dir):
     --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  The 1 GiB
     device copy of --copy-probe calibrates each counter: factor = bytes the copy
     must move / bytes the counter reports for it.  Prints a per-kernel table."""
-    import hashlib
     per = {}
     for folder, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         disp = {}
@@ -109,10 +120,7 @@ def traffic_record(fetch_dir, write_dir):
         raise SystemExit(f"no {key} dispatch found")
     fk = statistics.mean(per[attn[0]]["FETCH_SIZE"])
     wk = statistics.mean(per[attn[0]]["WRITE_SIZE"])
-    h = hashlib.sha256()
-    for f in ATTN_SOURCES:
-        h.update(open(os.path.join(ROOT, "block_sparse_long_pooling_amd", "csrc", f), "rb").read())
-    rec = {"kernel": key, "source_sha256": h.hexdigest(), "fetch_kib": fk, "write_kib": wk,
+    rec = {"kernel": key, "source_sha256": attn_source_hash(), "fetch_kib": fk, "write_kib": wk,
            "fetch_factor": ff, "write_factor": wf, "traffic_bytes": (fk * ff + wk * wf) * 1024.0,
            "commands": [
                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "

@@ -16,14 +16,15 @@
 //                        row-major V rows with ds_read_b64_tr_b16
 // A tile buffer holds the tile's KT K rows and its KT V rows in two arrays,
 // row-major [KT][D] bf16 with 16-byte chunks XOR-swizzled per row (16 KiB
-// each for 64 keys at d = 128).  Tiles arrive by global_load_lds_dwordx4 (DMA into LDS, no
-// registers) into two alternating buffers: the next tile's DMA is issued
-// right after the one barrier per tile and lands while the current tile is
-// computed.  Rows past a request's end re-read its last row (contiguous
-// layout) or a zero chunk (paged layout, also for out-of-range pages); the
-// causal mask of the diagonal block removes them, and a tile that lies wholly
-// past the end (a tile of the last block after its last token) is not
-// visited.  On the diagonal block a wave whose rows all precede a tile's keys
+// each for 64 keys at d = 128).  Tiles arrive by buffer loads into LDS (DMA,
+// no registers; per-row page addresses by global_load_lds only for pages
+// smaller than a load's rows) into two alternating buffers: the next tile's
+// DMA is issued right after the one barrier per tile and lands while the
+// current tile is computed.  Rows past a request's end re-read its last row
+// (a zero chunk with per-row page addresses; a page id outside the pool reads
+// as zeros); the causal mask of the diagonal block removes them, and a tile
+// that lies wholly past the end (a tile of the last block after its last
+// token) is not visited.  On the diagonal block a wave whose rows all precede a tile's keys
 // skips it.
 //
 // With one head per workgroup no wave idles through a tile that only another
