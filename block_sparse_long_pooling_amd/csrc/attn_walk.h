@@ -365,16 +365,22 @@ __device__ __forceinline__ void correction_dma(const AttnArgs& a, const SeqTable
         // Element r of a lane in half hf is block 32 sub + (r & 3) + 8 (r >> 2)
         // + 4 hf.  The skip words are uniform, so each element's keep mask is
         // built on the scalar unit as a 64-lane mask and applied with one
-        // select.
+        // select.  A step whose blocks are all skipped past blocks (most of
+        // them at low density) needs no mask at all.
+        uint32_t all = 0xffffffffu;
 #pragma unroll
-        for (int sub = 0; sub < NS; ++sub)
+        for (int sub = 0; sub < NS; ++sub) all &= sk[sub];
+        if (all != 0xffffffffu) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int k0 = (r & 3) + 8 * (r >> 2);
-                const uint64_t keep = (((sk[sub] >> k0) & 1u) ? 0xffffffffull : 0ull) |
-                                      (((sk[sub] >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-                s[sub][r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[sub][r] : -INFINITY;
-            }
+            for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int k0 = (r & 3) + 8 * (r >> 2);
+                    const uint64_t keep = (((sk[sub] >> k0) & 1u) ? 0xffffffffull : 0ull) |
+                                          (((sk[sub] >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+                    s[sub][r] = __builtin_amdgcn_inverse_ballot_w64(keep) ? s[sub][r] : -INFINITY;
+                }
+        }
         softmax_update<NS, D / 32>(s, c, log2_blk, m, l, o, pk);
         pv<D, 0, NS>(vc, pk, lane, o);
         if (kSerialFill) {
